@@ -1,0 +1,243 @@
+/*
+ * smoe.h -- C ABI of the MI355X (gfx950) routed-expert MoE library.
+ *
+ * The library computes one routed Mixture-of-Experts FFN layer of an S-MoE
+ * style engine, as the S-MoE documentation pages describe it:
+ *   - the exact router: RMSNorm of the residual, an E x d_model bf16 gate
+ *     matvec on that true hidden state, top-k selection and norm_topk_prob
+ *     mixing weights as Qwen3 defines them ("Optimizations", section
+ *     "Routing Is Exact"; "System Overview", per-token step table);
+ *   - the fused SMOE-Q4 expert FFN: per-chunk affine dequant, gate and up in
+ *     one pass, SwiGLU, down projection, and the gate-weighted sum of the
+ *     experts' outputs into the residual ("Optimizations", section "Coalesced
+ *     GPU Kernels"; "System Overview", step table, Metal-kernel row);
+ *   - layer-major prefill of chunks of up to 64 tokens whose routed experts are
+ *     deduplicated into a union read once per chunk ("Optimizations", section
+ *     "Prefill Reads Each Expert Once");
+ *   - an LRU ring of expert slots in HBM, refilled from a vault in host memory
+ *     ("Optimizations", section "The Ring Is an LRU Cache"; "System Overview",
+ *     memory-budget paragraph on the [64, 4096] slot clamp).
+ *
+ * Conventions (all entry points):
+ *   - Every call returns an smoe_status.  Arguments are checked before any
+ *     work is enqueued: a call that fails validation has no side effects and
+ *     smoe_last_error() describes the problem.  A failed HIP launch returns
+ *     SMOE_EHIP; faults inside a kernel surface at the caller's next
+ *     synchronisation, as with any asynchronous HIP work.
+ *   - "device" pointers are HIP device memory (or memory the GPU can read
+ *     directly); "host" pointers are ordinary host memory.  The caller owns
+ *     every buffer; the library never allocates or frees device memory and
+ *     keeps no pointer after the call returns (the ring keeps the pointers
+ *     given in its descriptor until smoe_ring_destroy).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  The layer calls only
+ *     enqueue kernels on it; they never synchronise and never allocate, so they
+ *     can be captured into a HIP graph (no memset nodes are recorded).
+ *   - Scalars are passed by value in kernel arguments.
+ *   - bf16 tensors are arrays of uint16_t bit patterns.
+ *   - Calls on one stream are ordered; concurrent calls that share a workspace
+ *     race.  A ring handle is single-threaded.
+ *
+ * SMOE-Q4 expert blob (the pages fix only "4-bit codes, per-chunk affine
+ * dequant, 16 KB-aligned blobs"; this byte layout is the library's):
+ *   matrices G (gate) [d_ff][d_model], U (up) [d_ff][d_model],
+ *            D (down) [d_model][d_ff];
+ *   W[n][k] = scale[n][k / chunk] * q[n][k] + min[n][k / chunk], q in 0..15;
+ *   sections, in order: G codes, U codes, D codes (row-major, two codes per
+ *   byte, the even element in the low nibble), then G params, U params,
+ *   D params (per row and chunk: bf16 scale, then bf16 min);
+ *   blob bytes = 1.5*d_model*d_ff + 12*d_model*d_ff/chunk; blobs sit at a
+ *   stride rounded up to 16384 bytes; a blob must be 16-byte aligned.
+ */
+#ifndef SMOE_H
+#define SMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMOE_OK = 0,
+  SMOE_EINVAL = -1,  /* bad argument; nothing was enqueued                    */
+  SMOE_EHIP = -2,    /* a HIP runtime call or launch failed                   */
+  SMOE_ENOSLOT = -3, /* ring: every slot is held by the current layer         */
+  SMOE_EBUSY = -4,   /* ring: destroy while slots are held or fills pending   */
+  SMOE_ENOMEM = -5   /* ring: host metadata allocation failed                 */
+} smoe_status;
+
+/* Geometry of one MoE layer. */
+typedef struct {
+  int32_t d_model;        /* hidden size; multiple of 256, <= 8192          */
+  int32_t d_ff;           /* expert FFN size; multiple of 64, <= 8192        */
+  int32_t n_experts;      /* E, 1..256                                       */
+  int32_t top_k;          /* k, 1..min(E, 16)                                */
+  int32_t chunk;          /* Q4 affine chunk along the reduction dim: 32, 64 */
+  int32_t norm_topk_prob; /* 1: divide the k weights by their sum (Qwen3)    */
+  float rms_eps;          /* RMSNorm epsilon (1e-6 for the Qwen3 shapes)     */
+} smoe_dims;
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* smoe_last_error(void);
+
+/* Library ABI version (this header: 1). */
+int32_t smoe_version(void);
+
+/* Exact byte size of one expert blob and its 16 KiB-aligned stride. */
+size_t smoe_q4_blob_bytes(const smoe_dims* dims);
+size_t smoe_q4_blob_stride(const smoe_dims* dims);
+
+/* Workspace bytes needed by smoe_route / smoe_moe_decode /
+ * smoe_decode_layers / smoe_moe_prefill_chunk for up to `max_tokens` tokens
+ * per call (1 for decode, up to 64 for prefill).  Writes *bytes. */
+int smoe_workspace_bytes(const smoe_dims* dims, int32_t max_tokens, size_t* bytes);
+
+/* Exact router for n_tok tokens ("Routing Is Exact"; step table, heavy-pass
+ * row).
+ *   residual  device fp32 [n_tok][d_model]            (read)
+ *   x_out     device bf16 [n_tok][d_model]            (written) the RMSNorm
+ *             output x = bf16(r / sqrt(mean(r^2) + eps)), round to nearest
+ *             even; gain 1
+ *   w_router  device bf16 [E][d_model]                 (read)
+ *   bias      device fp32 [E] or NULL                   added to every logit
+ *             before selection and softmax
+ *   topk_idx  device int32 [n_tok][k]                   (written) rank order:
+ *             logits descending, equal logits -> lower expert index first
+ *   topk_w    device fp32 [n_tok][k]                    (written) softmax over
+ *             all E logits at the selected experts, renormalised over the k
+ *             when dims->norm_topk_prob
+ * Logits are accumulated in float64 (each bf16*bf16 product is exact).
+ * 0 <= n_tok <= 64; n_tok == 0 does nothing.  Pointers 16-byte aligned. */
+int smoe_route(const smoe_dims* dims, int32_t n_tok, const float* residual, uint16_t* x_out,
+               const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Decode MoE FFN for one token ("Coalesced GPU Kernels"; step table,
+ * Metal-kernel row): for r = 0..k-1, expert e = topk_idx[r]:
+ *   h_r = silu(G_e x) * (U_e x),   y = sum_r topk_w[r] * (D_e h_r)  (rank order)
+ *   residual += y
+ *   x             device bf16 [d_model]   (from smoe_route)
+ *   topk_idx      device int32 [k], topk_w device fp32 [k]
+ *   expert_table  device array [E] of device blob pointers (this layer)
+ *   residual      device fp32 [d_model], updated in place
+ * Deterministic: no atomics, fixed reduction order. */
+int smoe_moe_decode(const smoe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
+                    const float* topk_w, const void* const* expert_table, float* residual,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* As smoe_moe_decode, but the k blob pointers come from the host, in rank
+ * order, and travel as kernel arguments (the pages pass dispatch parameters by
+ * value, "Zero Allocations, Zero Locks in the Token Loop").  Used with the
+ * ring, which returns slot pointers on the host.
+ *   blobs_host  host array [k] of device blob pointers */
+int smoe_moe_decode_slots(const smoe_dims* dims, const uint16_t* x, const float* topk_w,
+                          const void* const* blobs_host, float* residual, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* n_layers chained decode layers for one token, all experts resident
+ * ("What Happens at Each Generated Token Step"): for L = 0..n_layers-1,
+ * smoe_route then smoe_moe_decode with layer L's weights, the residual carried
+ * from layer to layer.  Three kernels per layer, no host synchronisation.
+ *   residual       device fp32 [d_model], updated in place
+ *   w_router       device bf16 [n_layers][E][d_model]
+ *   bias           device fp32 [n_layers][E] or NULL
+ *   expert_tables  device array [n_layers][E] of device blob pointers
+ *   x_rec          device bf16 [n_layers][d_model] or NULL: x used per layer
+ *   idx_rec        device int32 [n_layers][k] or NULL: routing per layer
+ *   w_rec          device fp32 [n_layers][k] or NULL: weights per layer
+ *   events         host array [n_layers][2] of hipEvent_t, or NULL: when
+ *                  given, the gate/up kernel of layer L is launched with
+ *                  hipExtLaunchKernel recording events[2L] at its start and
+ *                  events[2L+1] at its end (per-kernel timing, in the spirit
+ *                  of the pages' --instrument panel) */
+int smoe_decode_layers(const smoe_dims* dims, int32_t n_layers, float* residual,
+                       const uint16_t* w_router, const float* bias,
+                       const void* const* expert_tables, uint16_t* x_rec, int32_t* idx_rec,
+                       float* w_rec, void* const* events, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Layer-major prefill of one chunk through one layer ("Prefill Reads Each
+ * Expert Once, Not Once Per Token").  Inputs x/topk_idx/topk_w come from
+ * smoe_route over the chunk's n_tok tokens (1..64).
+ *   union_ids    device int32 [min(E, n_tok*k)] (written) experts the chunk
+ *                routes to, in first-touch order (t ascending, then rank)
+ *   union_count  device int32 [1] (written) |union|
+ *   offsets      device int32 [min(E, n_tok*k) + 1] (written) exclusive scan of
+ *                the per-expert token counts, in union order
+ *   perm         device int32 [n_tok*k] (written) for union member u, entries
+ *                offsets[u]..offsets[u+1]-1 list t*k + r of its tokens, t ascending
+ *   residual     device fp32 [n_tok][d_model], += the MoE output per token
+ * Each union expert's blob is streamed once per chunk; the grouped FFN runs on
+ * MFMA with weights dequantised to fp16 (exact for min = -8*scale).  The
+ * per-token mix is summed in rank order; no atomics. */
+int smoe_moe_prefill_chunk(const smoe_dims* dims, int32_t n_tok, const uint16_t* x,
+                           const int32_t* topk_idx, const float* topk_w,
+                           const void* const* expert_table, float* residual, int32_t* union_ids,
+                           int32_t* union_count, int32_t* offsets, int32_t* perm, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Expert ring ("The Ring Is an LRU Cache"): HBM slots caching (layer, expert)
+ * blobs from a vault in pinned host memory.  Released slots keep their data
+ * and identity; a re-request is a hit that moves zero bytes; eviction is lazy
+ * least-recently-used and never touches a slot held by the current layer.
+ * Every request (hit or load) stamps the slot with a fresh tick.  Empty slots
+ * are used first, lowest index first.  Misses are copied with hipMemcpyAsync
+ * on copy_stream; the compute stream waits on their completion events.
+ * ------------------------------------------------------------------------- */
+typedef struct smoe_ring smoe_ring;
+
+typedef struct {
+  int32_t n_slots;        /* 64..4096 (the pages' clamp), >= k              */
+  int32_t n_layers;       /* >= 1                                          */
+  int32_t n_experts;      /* E                                             */
+  int32_t top_k;          /* k                                             */
+  size_t slot_bytes;      /* bytes copied per fill (the blob size)         */
+  size_t slot_stride;     /* distance between slots in slab_dev (>= bytes) */
+  const void* vault_host; /* host: blob (L, e) at vault_host + (L*E+e)*vault_stride;
+                             pinned (hipHostMalloc) for asynchronous copies */
+  size_t vault_stride;
+  void* slab_dev;         /* device: n_slots * slot_stride bytes            */
+  void* copy_stream;      /* hipStream_t used for fills                     */
+  size_t log_capacity;    /* events kept for smoe_ring_log (0 = none)       */
+} smoe_ring_desc;
+
+/* One ring decision. */
+typedef struct {
+  int32_t layer, rank, expert;
+  int32_t kind;           /* 0 = hit, 1 = miss                              */
+  int32_t slot;
+  int32_t evicted_layer;  /* -1 if no eviction                              */
+  int32_t evicted_expert;
+  int32_t pad;
+} smoe_ring_event;
+
+int smoe_ring_create(const smoe_ring_desc* desc, smoe_ring** out);
+
+/* Acquire the k experts of `layer` (host array, rank order).  Drops the
+ * previous acquisition's holds first (an implicit release), so the caller must
+ * have synchronised with every kernel that read the previously acquired slots
+ * -- the per-layer routing round trip does this.  On return slot_ptrs_host[r]
+ * is the device blob pointer for rank r, and compute_stream will not run
+ * later work until the fills are complete. */
+int smoe_ring_acquire(smoe_ring* ring, int32_t layer, const int32_t* experts_host, int32_t k,
+                      const void** slot_ptrs_host, void* compute_stream);
+
+/* Drop the current holds (the slots stay resident for later hits). */
+int smoe_ring_release(smoe_ring* ring);
+
+int smoe_ring_stats(const smoe_ring* ring, uint64_t* hits, uint64_t* misses, uint64_t* evictions,
+                    uint64_t* h2d_bytes);
+
+/* Copy up to `cap` logged events (oldest first) to events_host; *n_out = count. */
+int smoe_ring_log(const smoe_ring* ring, smoe_ring_event* events_host, size_t cap, size_t* n_out);
+
+/* Returns SMOE_EBUSY (and keeps the ring) if slots are still held. */
+int smoe_ring_destroy(smoe_ring* ring);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOE_H */

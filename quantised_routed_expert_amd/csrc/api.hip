@@ -1,0 +1,242 @@
+// C ABI entry points: argument validation, workspace carving, kernel launches.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+
+
+namespace smoe {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+static int hip_fail(hipError_t e, const char* what) {
+  return fail(SMOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_dims(const smoe_dims* d) {
+  if (!d) return fail(SMOE_EINVAL, "dims is NULL");
+  if (d->d_model <= 0 || d->d_model > 8192 || d->d_model % 256)
+    return fail(SMOE_EINVAL, "d_model=%d must be a multiple of 256 in [256, 8192]", d->d_model);
+  if (d->d_ff <= 0 || d->d_ff > 8192 || d->d_ff % 64)
+    return fail(SMOE_EINVAL, "d_ff=%d must be a multiple of 64 in [64, 8192]", d->d_ff);
+  if (d->n_experts < 1 || d->n_experts > kMaxExperts)
+    return fail(SMOE_EINVAL, "n_experts=%d must be in [1, %d]", d->n_experts, kMaxExperts);
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > kMaxTopK)
+    return fail(SMOE_EINVAL, "top_k=%d must be in [1, min(n_experts, %d)]", d->top_k, kMaxTopK);
+  if (d->chunk != 32 && d->chunk != 64) return fail(SMOE_EINVAL, "chunk=%d must be 32 or 64", d->chunk);
+  if (!(d->rms_eps >= 0.0f) || d->rms_eps > 1.0f) return fail(SMOE_EINVAL, "rms_eps out of range");
+  if (!decode_shape_supported(d->d_model, d->d_ff, d->chunk))
+    return fail(SMOE_EINVAL, "unsupported row split for d_model=%d d_ff=%d", d->d_model, d->d_ff);
+  return SMOE_OK;
+}
+
+// Workspace carve-up (offsets from the workspace base, 256-byte aligned).
+struct Workspace {
+  size_t logits, idx, w, x, h, ph, py, pinv, end;
+};
+
+Workspace ws_layout(const smoe_dims* d, int max_tokens) {
+  Workspace w;
+  const size_t T = (size_t)(max_tokens < 1 ? 1 : max_tokens);
+  const size_t E = d->n_experts, k = d->top_k, D = d->d_model, F = d->d_ff;
+  size_t o = 0;
+  w.logits = o; o = align_up(o + T * E * 8, 256);
+  w.idx = o;    o = align_up(o + k * 4, 256);
+  w.w = o;      o = align_up(o + k * 4, 256);
+  w.x = o;      o = align_up(o + T * D * 2, 256);
+  w.h = o;      o = align_up(o + k * F * 2, 256);
+  if (max_tokens > 1) {
+    w.ph = o;   o = align_up(o + T * k * F * 2, 256);
+    w.py = o;   o = align_up(o + T * k * D * 4, 256);
+    w.pinv = o; o = align_up(o + T * k * 4, 256);
+  } else {
+    w.ph = w.py = w.pinv = o;
+  }
+  w.end = o;
+  return w;
+}
+
+static int check_ws(const smoe_dims* d, int tokens, const void* ws, size_t bytes, Workspace* out) {
+  *out = ws_layout(d, tokens);
+  if (!ws) return fail(SMOE_EINVAL, "workspace is NULL");
+  if (((uintptr_t)ws & 255u) != 0) return fail(SMOE_EINVAL, "workspace must be 256-byte aligned");
+  if (bytes < out->end)
+    return fail(SMOE_EINVAL, "workspace too small: %zu < %zu bytes", bytes, out->end);
+  return SMOE_OK;
+}
+
+static DecodeArgs decode_args(const smoe_dims* d, char* ws, const Workspace& L) {
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.d = d->d_model;
+  a.f = d->d_ff;
+  a.E = d->n_experts;
+  a.k = d->top_k;
+  a.chunk = d->chunk;
+  a.norm = d->norm_topk_prob ? 1 : 0;
+  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk);
+  a.h = reinterpret_cast<_Float16*>(ws + L.h);
+  return a;
+}
+
+}  // namespace smoe
+
+using namespace smoe;
+
+extern "C" {
+
+const char* smoe_last_error(void) { return g_err; }
+
+int32_t smoe_version(void) { return 1; }
+
+size_t smoe_q4_blob_bytes(const smoe_dims* d) {
+  if (check_dims(d) != SMOE_OK) return 0;
+  return blob_layout(d->d_model, d->d_ff, d->chunk).bytes;
+}
+
+size_t smoe_q4_blob_stride(const smoe_dims* d) {
+  const size_t b = smoe_q4_blob_bytes(d);
+  return (b + 16383) / 16384 * 16384;
+}
+
+int smoe_workspace_bytes(const smoe_dims* d, int32_t max_tokens, size_t* bytes) {
+  g_err[0] = 0;
+  if (int e = check_dims(d)) return e;
+  if (!bytes) return fail(SMOE_EINVAL, "bytes is NULL");
+  if (max_tokens < 0 || max_tokens > kMaxPrefillTokens)
+    return fail(SMOE_EINVAL, "max_tokens=%d must be in [0, %d]", max_tokens, kMaxPrefillTokens);
+  *bytes = ws_layout(d, max_tokens).end;
+  return SMOE_OK;
+}
+
+int smoe_route(const smoe_dims* d, int32_t n_tok, const float* residual, uint16_t* x_out,
+               const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w, void* ws,
+               size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int e = check_dims(d)) return e;
+  if (n_tok < 0 || n_tok > kMaxPrefillTokens)
+    return fail(SMOE_EINVAL, "n_tok=%d must be in [0, %d]", n_tok, kMaxPrefillTokens);
+  if (!residual || !x_out || !w_router || !topk_idx || !topk_w)
+    return fail(SMOE_EINVAL, "NULL tensor argument");
+  if (!aligned16(residual) || !aligned16(x_out) || !aligned16(w_router))
+    return fail(SMOE_EINVAL, "residual, x_out and w_router must be 16-byte aligned");
+  Workspace L;
+  if (int e = check_ws(d, n_tok, ws, ws_bytes, &L)) return e;
+  if (n_tok == 0) return SMOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  double* logits = reinterpret_cast<double*>((char*)ws + L.logits);
+  RouteArgs ra{residual, x_out, w_router, bias, logits, n_tok, d->d_model, d->n_experts, d->rms_eps};
+  hipError_t he = launch_route_logits(ra, s);
+  if (he != hipSuccess) return hip_fail(he, "route_logits launch");
+  he = launch_route_topk(logits, n_tok, d->n_experts, d->top_k, d->norm_topk_prob ? 1 : 0, topk_idx,
+                         topk_w, s);
+  if (he != hipSuccess) return hip_fail(he, "route_topk launch");
+  return SMOE_OK;
+}
+
+int smoe_moe_decode(const smoe_dims* d, const uint16_t* x, const int32_t* topk_idx, const float* topk_w,
+                    const void* const* expert_table, float* residual, void* ws, size_t ws_bytes,
+                    void* stream) {
+  g_err[0] = 0;
+  if (int e = check_dims(d)) return e;
+  if (!x || !topk_idx || !topk_w || !expert_table || !residual)
+    return fail(SMOE_EINVAL, "NULL tensor argument");
+  if (!aligned16(x) || !aligned16(residual)) return fail(SMOE_EINVAL, "x and residual must be 16-byte aligned");
+  Workspace L;
+  if (int e = check_ws(d, 1, ws, ws_bytes, &L)) return e;
+  DecodeArgs a = decode_args(d, (char*)ws, L);
+  a.x = x;
+  a.src.idx = topk_idx;
+  a.src.table = expert_table;
+  a.w = topk_w;
+  a.residual = residual;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t he = launch_decode_gate_up(a, s);
+  if (he != hipSuccess) return hip_fail(he, "decode gate/up launch");
+  he = launch_decode_down(a, s);
+  if (he != hipSuccess) return hip_fail(he, "decode down launch");
+  return SMOE_OK;
+}
+
+int smoe_moe_decode_slots(const smoe_dims* d, const uint16_t* x, const float* topk_w,
+                          const void* const* blobs_host, float* residual, void* ws, size_t ws_bytes,
+                          void* stream) {
+  g_err[0] = 0;
+  if (int e = check_dims(d)) return e;
+  if (!x || !topk_w || !blobs_host || !residual) return fail(SMOE_EINVAL, "NULL argument");
+  if (!aligned16(x) || !aligned16(residual)) return fail(SMOE_EINVAL, "x and residual must be 16-byte aligned");
+  for (int r = 0; r < d->top_k; ++r)
+    if (!blobs_host[r] || !aligned16(blobs_host[r]))
+      return fail(SMOE_EINVAL, "blob pointer %d is NULL or not 16-byte aligned", r);
+  Workspace L;
+  if (int e = check_ws(d, 1, ws, ws_bytes, &L)) return e;
+  DecodeArgs a = decode_args(d, (char*)ws, L);
+  a.x = x;
+  for (int r = 0; r < d->top_k; ++r) a.src.direct[r] = blobs_host[r];
+  a.w = topk_w;
+  a.residual = residual;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t he = launch_decode_gate_up(a, s);
+  if (he != hipSuccess) return hip_fail(he, "decode gate/up launch");
+  he = launch_decode_down(a, s);
+  if (he != hipSuccess) return hip_fail(he, "decode down launch");
+  return SMOE_OK;
+}
+
+int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, const uint16_t* w_router,
+                       const float* bias, const void* const* expert_tables, uint16_t* x_rec,
+                       int32_t* idx_rec, float* w_rec, void* const* events, void* ws, size_t ws_bytes,
+                       void* stream) {
+  g_err[0] = 0;
+  if (int e = check_dims(d)) return e;
+  if (n_layers < 0) return fail(SMOE_EINVAL, "n_layers=%d < 0", n_layers);
+  if (!residual || !w_router || !expert_tables) return fail(SMOE_EINVAL, "NULL tensor argument");
+  if (!aligned16(residual) || !aligned16(w_router) || (x_rec && !aligned16(x_rec)))
+    return fail(SMOE_EINVAL, "residual, w_router and x_rec must be 16-byte aligned");
+  Workspace L;
+  if (int e = check_ws(d, 1, ws, ws_bytes, &L)) return e;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  double* logits = reinterpret_cast<double*>(base + L.logits);
+  uint16_t* xbuf = reinterpret_cast<uint16_t*>(base + L.x);
+  const size_t D = d->d_model, E = d->n_experts, K = d->top_k;
+  for (int layer = 0; layer < n_layers; ++layer) {
+    uint16_t* xl = x_rec ? x_rec + (size_t)layer * D : xbuf;
+    RouteArgs ra{residual, xl, w_router + (size_t)layer * E * D, bias ? bias + (size_t)layer * E : nullptr,
+                 logits, 1, d->d_model, d->n_experts, d->rms_eps};
+    hipError_t he = launch_route_logits(ra, s);
+    if (he != hipSuccess) return hip_fail(he, "route_logits launch");
+    DecodeArgs a = decode_args(d, base, L);
+    a.x = xl;
+    a.logits = logits;
+    a.idx_ws = reinterpret_cast<int32_t*>(base + L.idx);
+    a.w_ws = reinterpret_cast<float*>(base + L.w);
+    a.idx_rec = idx_rec ? idx_rec + (size_t)layer * K : nullptr;
+    a.w_rec = w_rec ? w_rec + (size_t)layer * K : nullptr;
+    a.src.idx = a.idx_ws;
+    a.src.table = expert_tables + (size_t)layer * E;
+    a.w = a.w_ws;
+    a.residual = residual;
+    he = events ? launch_decode_gate_up(a, s, (hipEvent_t)events[2 * layer], (hipEvent_t)events[2 * layer + 1])
+                : launch_decode_gate_up(a, s);
+    if (he != hipSuccess) return hip_fail(he, "decode gate/up launch");
+    he = launch_decode_down(a, s);
+    if (he != hipSuccess) return hip_fail(he, "decode down launch");
+  }
+  return SMOE_OK;
+}
+
+}  // extern "C"

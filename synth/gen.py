@@ -121,9 +121,11 @@ def normal_box_muller(words: np.ndarray) -> np.ndarray:
 # Layer geometry and the SMOE-Q4 blob layout
 # --------------------------------------------------------------------------
 class Dims:
-    """Geometry of one routed-expert MoE layer."""
+    """Geometry of one routed-expert MoE layer.  ``rms_eps`` is a float32 value
+    (the library takes it as float), 1e-6 rounded to float32 by default."""
 
-    def __init__(self, d_model, d_ff, n_experts, top_k, chunk, norm_topk_prob=True, rms_eps=1e-6):
+    def __init__(self, d_model, d_ff, n_experts, top_k, chunk, norm_topk_prob=True,
+                 rms_eps=float(np.float32(1e-6))):
         self.d_model = int(d_model)
         self.d_ff = int(d_ff)
         self.n_experts = int(n_experts)
