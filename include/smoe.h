@@ -90,7 +90,8 @@ size_t smoe_q4_blob_stride(const smoe_dims* dims);
 
 /* Workspace bytes needed by smoe_route / smoe_moe_decode /
  * smoe_decode_layers / smoe_moe_prefill_chunk for up to `max_tokens` tokens
- * per call (1 for decode, up to 64 for prefill).  Writes *bytes. */
+ * per call (1 for decode, up to 64 for prefill).  Writes *bytes.  The
+ * workspace must be 256-byte aligned; its contents need no initialisation. */
 int smoe_workspace_bytes(const smoe_dims* dims, int32_t max_tokens, size_t* bytes);
 
 /* Exact router for n_tok tokens ("Routing Is Exact"; step table, heavy-pass

@@ -133,8 +133,8 @@ def workspace_bytes(dims, max_tokens: int) -> int:
 
 
 def workspace(dims, max_tokens: int, device="cuda") -> torch.Tensor:
-    """A device workspace of the size the library asks for (256-byte aligned)."""
-    return torch.empty(workspace_bytes(dims, max_tokens), dtype=torch.uint8, device=device)
+    """A zero-filled device workspace of the size the library asks for."""
+    return torch.zeros(workspace_bytes(dims, max_tokens), dtype=torch.uint8, device=device)
 
 
 def route(dims, residual, x_out, w_router, bias, topk_idx, topk_w, ws, stream=None):

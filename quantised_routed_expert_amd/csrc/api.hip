@@ -45,7 +45,7 @@ int check_dims(const smoe_dims* d) {
 
 // Workspace carve-up (offsets from the workspace base, 256-byte aligned).
 struct Workspace {
-  size_t logits, idx, w, x, h, ph, py, pinv, end;
+  size_t logits, idx, w, ptr, x, px, h, ph, py, pinv, end;
 };
 
 Workspace ws_layout(const smoe_dims* d, int max_tokens) {
@@ -56,7 +56,9 @@ Workspace ws_layout(const smoe_dims* d, int max_tokens) {
   w.logits = o; o = align_up(o + T * E * 8, 256);
   w.idx = o;    o = align_up(o + k * 4, 256);
   w.w = o;      o = align_up(o + k * 4, 256);
+  w.ptr = o;    o = align_up(o + k * 8, 256);
   w.x = o;      o = align_up(o + T * D * 2, 256);
+  w.px = o;     o = align_up(o + D * 2, 256);
   w.h = o;      o = align_up(o + k * F * 2, 256);
   if (max_tokens > 1) {
     w.ph = o;   o = align_up(o + T * k * F * 2, 256);
@@ -138,11 +140,18 @@ int smoe_route(const smoe_dims* d, int32_t n_tok, const float* residual, uint16_
   if (n_tok == 0) return SMOE_OK;
   hipStream_t s = (hipStream_t)stream;
   double* logits = reinterpret_cast<double*>((char*)ws + L.logits);
-  RouteArgs ra{residual, x_out, w_router, bias, logits, n_tok, d->d_model, d->n_experts, d->rms_eps};
+  RouteArgs ra{residual, x_out, nullptr, w_router, bias, logits, n_tok, d->d_model, d->n_experts, d->rms_eps};
   hipError_t he = launch_route_logits(ra, s);
   if (he != hipSuccess) return hip_fail(he, "route_logits launch");
-  he = launch_route_topk(logits, n_tok, d->n_experts, d->top_k, d->norm_topk_prob ? 1 : 0, topk_idx,
-                         topk_w, s);
+  TopkArgs ta;
+  memset(&ta, 0, sizeof(ta));
+  ta.logits = logits;
+  ta.idx = topk_idx;
+  ta.w = topk_w;
+  ta.E = d->n_experts;
+  ta.k = d->top_k;
+  ta.norm = d->norm_topk_prob ? 1 : 0;
+  he = launch_route_topk(ta, n_tok, s);
   if (he != hipSuccess) return hip_fail(he, "route_topk launch");
   return SMOE_OK;
 }
@@ -215,21 +224,32 @@ int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, co
   const size_t D = d->d_model, E = d->n_experts, K = d->top_k;
   for (int layer = 0; layer < n_layers; ++layer) {
     uint16_t* xl = x_rec ? x_rec + (size_t)layer * D : xbuf;
-    RouteArgs ra{residual, xl, w_router + (size_t)layer * E * D, bias ? bias + (size_t)layer * E : nullptr,
-                 logits, 1, d->d_model, d->n_experts, d->rms_eps};
+    _Float16* px = reinterpret_cast<_Float16*>(base + L.px);
+    const RouteArgs ra{residual, xl, px, w_router + (size_t)layer * E * D, bias ? bias + (size_t)layer * E : nullptr,
+                       logits, 1, d->d_model, d->n_experts, d->rms_eps};
     hipError_t he = launch_route_logits(ra, s);
     if (he != hipSuccess) return hip_fail(he, "route_logits launch");
+    TopkArgs ta;
+    memset(&ta, 0, sizeof(ta));
+    ta.logits = logits;
+    ta.idx = reinterpret_cast<int32_t*>(base + L.idx);
+    ta.w = reinterpret_cast<float*>(base + L.w);
+    ta.table = expert_tables + (size_t)layer * E;
+    ta.ptr_out = reinterpret_cast<const void**>(base + L.ptr);
+    ta.idx_rec = idx_rec ? idx_rec + (size_t)layer * K : nullptr;
+    ta.w_rec = w_rec ? w_rec + (size_t)layer * K : nullptr;
+    ta.E = d->n_experts;
+    ta.k = d->top_k;
+    ta.norm = d->norm_topk_prob ? 1 : 0;
+    he = launch_route_topk(ta, 1, s);
+    if (he != hipSuccess) return hip_fail(he, "route_topk launch");
     DecodeArgs a = decode_args(d, base, L);
     a.x = xl;
-    a.logits = logits;
-    a.idx_ws = reinterpret_cast<int32_t*>(base + L.idx);
-    a.w_ws = reinterpret_cast<float*>(base + L.w);
-    a.idx_rec = idx_rec ? idx_rec + (size_t)layer * K : nullptr;
-    a.w_rec = w_rec ? w_rec + (size_t)layer * K : nullptr;
-    a.src.idx = a.idx_ws;
-    a.src.table = expert_tables + (size_t)layer * E;
-    a.w = a.w_ws;
+    a.px = px;
+    a.ptrs = ta.ptr_out;
+    a.w = ta.w;
     a.residual = residual;
+    if (layer + 1 < n_layers) a.pf_base = reinterpret_cast<const uint8_t*>(w_router + (size_t)(layer + 1) * E * D);
     he = events ? launch_decode_gate_up(a, s, (hipEvent_t)events[2 * layer], (hipEvent_t)events[2 * layer + 1])
                 : launch_decode_gate_up(a, s);
     if (he != hipSuccess) return hip_fail(he, "decode gate/up launch");

@@ -5,10 +5,10 @@
 // computes gate and up in one pass, then the down projection; the System
 // Overview step table adds the gate-weighted sum into the residual.  The pages'
 // Metal design (one 32-lane simdgroup per output row, input staged per 8-row
-// threadgroup) is prior art; on gfx950 the row is split over LR lanes of a
-// wave64 (LR = 64 for the 235B/30B gate-up rows), each lane streaming 16-byte
-// segments of packed nibbles with global_load_dwordx4, the input held in
-// registers as f16 pairs for v_dot2_f32_f16, and rows reduced with butterflies.
+// threadgroup) is prior art; on gfx950 a row is split over LR lanes of a
+// wave64, each lane streaming one contiguous run of NSEG 16-byte segments of
+// packed nibbles (global_load_dwordx4), the input held in registers as f16
+// pairs for v_dot2_f32_f16, and rows reduced with DPP.
 //
 // Affine folding: a 16-byte segment (32 codes) lies inside one chunk, so its
 // contribution is scale * sum(q x) + min * sum(x); sum(x) over the segment is
@@ -17,204 +17,276 @@
 
 #include "kernels.h"
 
+#ifndef SMOE_GU_ROWS_MAX
+#define SMOE_GU_ROWS_MAX 4     // rows per wave of the gate/up kernel (upper bound)
+#endif
+#ifndef SMOE_GU_MIN_WAVES
+#define SMOE_GU_MIN_WAVES 2048 // keep at least this many waves per gate/up launch
+#endif
+#ifndef SMOE_DN_PASSES_MAX
+#define SMOE_DN_PASSES_MAX 4   // row passes per wave of the down kernel (upper bound)
+#endif
+#ifndef SMOE_DN_MIN_WG
+#define SMOE_DN_MIN_WG 256     // keep at least this many down workgroups
+#endif
+
 namespace smoe {
 
-// Blob of rank r, or null when the routed index is outside [0, E) (such a
-// rank contributes nothing; it cannot come from the router itself).
-__device__ __forceinline__ const uint8_t* expert_blob(const DecodeArgs& a, const int* s_idx, int r) {
-  if (a.src.direct[0]) return reinterpret_cast<const uint8_t*>(a.src.direct[r]);
-  const int e = s_idx[r];
-  if (e < 0 || e >= a.E) return nullptr;
-  return reinterpret_cast<const uint8_t*>(a.src.table[e]);
+// Per-lane layout of one row: lane li owns bytes [li*CW, li*CW + CW) of the
+// row's codes (NSEG segments) and the (scale, min) records of the chunks they
+// fall in.
+template <int NSEG, int CHUNK>
+struct LaneRun {
+  static constexpr int CW = NSEG * 16;              // code bytes per lane
+  static constexpr int CB = CHUNK / 2;              // code bytes per chunk
+  static constexpr bool ONE = CW <= CB;             // the run sits in one chunk
+  static constexpr bool ALIGNED = CW % CB == 0;     // the run is whole chunks
+  static constexpr int NPL = ONE ? 1 : (ALIGNED ? CW / CB : NSEG);  // param dwords
+  __device__ static int param_of_seg(int s) { return ONE ? 0 : (ALIGNED ? (16 * s) / CB : s); }
+  // chunk index (within the row) of param dword j of lane li
+  __device__ static int chunk_of(int li, int j) {
+    return ONE ? (li * CW) / CB : (ALIGNED ? (li * CW) / CB + j : (li * CW + 16 * j) / CB);
+  }
+};
+
+// Pair-ordered f16 input of one lane run (NSEG segments of 32 values) and the
+// per-segment sums, from bf16 (x) or pair-ordered f16 (h) storage.  The raw
+// loads are separate from the conversion so that the weight loads can be
+// issued in between.
+template <int NSEG>
+__device__ __forceinline__ void load_raw(const void* base, uint4 (*raw)[4]) {
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) raw[s][q] = gload16(reinterpret_cast<const uint8_t*>(base) + s * 64 + q * 16);
 }
 
-// ---------------------------------------------------------------------------
-// Gate + up + SwiGLU.  One wave owns rows_per_wave consecutive rows of the
-// flattened (rank, row) space, all inside one expert; LR lanes share a row.
-// grid = ceil(k * d_ff / (4 * rows_per_wave)), 256 threads.
-// ---------------------------------------------------------------------------
-template <int LR, int NLD>
-__global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a, int rows_per_wave) {
-  __shared__ int s_idx[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  if (a.logits) {
-    // fused routing: every workgroup selects the experts itself
-    if (wave == 0) topk_wave(a.logits, a.E, a.k, a.norm, s_idx, s_w);
-    __syncthreads();
-    if (blockIdx.x == 0 && tid < a.k) {
-      a.idx_ws[tid] = s_idx[tid];
-      a.w_ws[tid] = s_w[tid];
-      if (a.idx_rec) a.idx_rec[tid] = s_idx[tid];
-      if (a.w_rec) a.w_rec[tid] = s_w[tid];
-    }
-  } else if (!a.src.direct[0]) {
-    if (tid < a.k) s_idx[tid] = a.src.idx[tid];
-    __syncthreads();
-  }
-
-  constexpr int P = kWave / LR;  // rows per pass
-  const int li = lane % LR, grp = lane / LR;
-  const int gw = blockIdx.x * 4 + wave;
-  const int total = a.k * a.f;
-  const int row0 = gw * rows_per_wave;
-  if (row0 >= total) return;
-  const int r = row0 / a.f;
-  const uint8_t* blob = expert_blob(a, s_idx, r);
-  const int n_begin = row0 - r * a.f;
-  if (!blob) {
-    for (int it = lane; it < rows_per_wave; it += kWave) {
-      const int n = n_begin + it;
-      a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)0.0f;
-    }
-    return;
-  }
-
-  // the wave's input columns, as f16 pairs, and their per-segment sums
-  uint32_t xp[NLD][16];
-  float cseg[NLD], xseg[NLD];
+template <int NSEG>
+__device__ __forceinline__ void pack_bf16_run(const uint4 (*raw)[4], uint32_t (*xp)[16], float* xseg) {
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int seg = li + LR * i;
-    const uint4* xv = reinterpret_cast<const uint4*>(a.x + seg * 32);
+  for (int s = 0; s < NSEG; ++s) {
     float v[32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 u = xv[q];
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+      const uint32_t w4[4] = {raw[s][q].x, raw[s][q].y, raw[s][q].z, raw[s][q].w};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         v[8 * q + 2 * p] = bf16_to_f32(w4[p] & 0xFFFF);
         v[8 * q + 2 * p + 1] = bf16_to_f32(w4[p] >> 16);
       }
     }
-    pack_segment(v, xp[i], cseg[i], xseg[i]);
+    pack_segment(v, xp[s]);
+    xseg[s] = seg_sum(xp[s]);
+  }
+}
+
+// Pair-ordered f16 storage (the router's prepared x, or h) is used as is.
+template <int NSEG>
+__device__ __forceinline__ void pack_f16_run(const uint4 (*raw)[4], uint32_t (*hp)[16], float* xseg) {
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hp[s][4 * q + 0] = raw[s][q].x; hp[s][4 * q + 1] = raw[s][q].y;
+      hp[s][4 * q + 2] = raw[s][q].z; hp[s][4 * q + 3] = raw[s][q].w;
+    }
+    xseg[s] = seg_sum(hp[s]);
+  }
+}
+
+// Blob of rank r: passed by value, published by the router, or looked up in the
+// layer's table; null when the index is outside [0, E) (the rank then
+// contributes nothing -- the router itself never produces such an index).
+__device__ __forceinline__ const void* expert_pointer(const DecodeArgs& a, int r) {
+  if (a.src.direct[0]) return a.src.direct[r];
+  if (a.ptrs) return a.ptrs[r];
+  const int e = a.src.idx[r];
+  return (e >= 0 && e < a.E) ? a.src.table[e] : nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// Gate + up + SwiGLU.  One wave owns NP * (64 / LR) consecutive rows of the
+// flattened (rank, row) space, all inside one expert; LR lanes share a row.
+// Every load of the wave's rows is issued before
+// any is consumed.  grid = ceil(k * d_ff / (4 * rows per wave)), 256 threads.
+// ---------------------------------------------------------------------------
+template <int LR, int NSEG, int NP, int CHUNK>
+__global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a) {
+  using Run = LaneRun<NSEG, CHUNK>;
+  constexpr int P = kWave / LR;  // rows per pass
+  constexpr int RPW = NP * P;    // rows per wave
+  __shared__ const void* s_ptr[kMaxTopK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane % LR, grp = lane / LR;
+
+  if (tid < a.k) s_ptr[tid] = expert_pointer(a, tid);
+  uint4 xraw[NSEG][4];
+  if (a.px) load_raw<NSEG>(a.px + li * (NSEG * 32), xraw);
+  else load_raw<NSEG>(a.x + li * (NSEG * 32), xraw);
+  __syncthreads();
+
+  const int gw = blockIdx.x * 4 + wave;
+  const int row0 = gw * RPW;
+  if (row0 >= a.k * a.f) return;
+  const int r = row0 / a.f;
+  const int n_begin = row0 - r * a.f;
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
+  if (!blob) {  // an index outside [0, E): the rank contributes nothing
+    for (int it = lane; it < RPW; it += kWave) {
+      const int n = n_begin + it;
+      a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)0.0f;
+    }
+    return;
   }
 
   const size_t row_bytes = (size_t)a.d / 2;
-  const size_t prow_bytes = (size_t)(a.d / a.chunk) * 4;
-  const uint8_t* gcodes = blob;
-  const uint8_t* ucodes = blob + a.lay.up_codes;
-  const uint8_t* gpar = blob + a.lay.gate_params;
-  const uint8_t* upar = blob + a.lay.up_params;
-  int poff[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) poff[i] = ((li + LR * i) * 32 / a.chunk) * 4;
+  const size_t prow_bytes = (size_t)(a.d / CHUNK) * 4;
+  const size_t first = (size_t)(n_begin + grp);
+  const uint8_t* gcodes = blob + first * row_bytes + li * Run::CW;
+  const uint8_t* ucodes = blob + a.lay.up_codes + first * row_bytes + li * Run::CW;
+  const uint8_t* gpar = blob + a.lay.gate_params + first * prow_bytes;
+  const uint8_t* upar = blob + a.lay.up_params + first * prow_bytes;
 
-  for (int it = 0; it < rows_per_wave; it += P) {
-    const int n = n_begin + it + grp;
-    uint4 cg[NLD], cu[NLD];
-    uint32_t pg[NLD], pu[NLD];
+  uint4 cg[NP][NSEG], cu[NP][NSEG];
+  uint32_t pg[NP][Run::NPL], pu[NP][Run::NPL];
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const size_t co = (size_t)n * row_bytes + (size_t)(li + LR * i) * 16;
-      cg[i] = *reinterpret_cast<const uint4*>(gcodes + co);
-      cu[i] = *reinterpret_cast<const uint4*>(ucodes + co);
-      const size_t po = (size_t)n * prow_bytes + poff[i];
-      pg[i] = *reinterpret_cast<const uint32_t*>(gpar + po);
-      pu[i] = *reinterpret_cast<const uint32_t*>(upar + po);
+  for (int p = 0; p < NP; ++p) {
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      cg[p][s] = gload16(gcodes + (size_t)p * P * row_bytes + s * 16);
+      cu[p][s] = gload16(ucodes + (size_t)p * P * row_bytes + s * 16);
     }
+#pragma unroll
+    for (int j = 0; j < Run::NPL; ++j) {
+      const size_t po = (size_t)p * P * prow_bytes + Run::chunk_of(li, j) * 4;
+      pg[p][j] = gload4(gpar + po);
+      pu[p][j] = gload4(upar + po);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
+
+  // this lane's input columns as f16 pairs, converted while the weights stream
+  uint32_t xp[NSEG][16];
+  float xseg[NSEG];
+  if (a.px) pack_f16_run<NSEG>(xraw, xp, xseg);
+  else pack_bf16_run<NSEG>(xraw, xp, xseg);
+
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
     float g = 0.f, u = 0.f;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      g += seg_contrib(cg[i], xp[i], cseg[i], xseg[i], pg[i]);
-      u += seg_contrib(cu[i], xp[i], cseg[i], xseg[i], pu[i]);
+    for (int s = 0; s < NSEG; ++s) {
+      g += seg_contrib(cg[p][s], xp[s], xseg[s], pg[p][Run::param_of_seg(s)]);
+      u += seg_contrib(cu[p][s], xp[s], xseg[s], pu[p][Run::param_of_seg(s)]);
     }
     g = group_sum<LR>(g);
     u = group_sum<LR>(u);
     if (li == 0) {
-      const float h = silu_f32(g) * u;
-      a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)h;
+      const int n = n_begin + p * P + grp;
+      a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)(silu_f32(g) * u);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Down projection + weighted combine into the residual.  A workgroup owns
-// rows_per_wg output rows; its wave w handles ranks w, w + nw, ... so that each
-// wave keeps one expert's h in registers; per-row partial results meet in LDS
-// and are mixed in rank order (no atomics).  grid = ceil(d / rows_per_wg),
-// block = 64 * min(k, 8).
+// NPASS * (64 / LR) output rows; its wave w handles ranks w, w + nw, ... so
+// that each wave keeps one expert's h in registers; per-row partial results
+// meet in LDS and are mixed in rank order (no atomics).  Each wave issues all
+// weight loads of its rows before it computes.
+// grid = ceil(d / rows per workgroup), block = 64 * min(k, 8).
 // ---------------------------------------------------------------------------
-constexpr int kDownMaxRows = 64;
-
-template <int LR, int NLD>
-__global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a, int rows_per_wg) {
-  __shared__ float ylds[kMaxTopK][kDownMaxRows];
-  __shared__ int s_idx[kMaxTopK];
+template <int LR, int NSEG, int NPASS, int CHUNK>
+__global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
+  using Run = LaneRun<NSEG, CHUNK>;
+  constexpr int P = kWave / LR;
+  constexpr int ROWS = NPASS * P;
+  __shared__ float ylds[kMaxTopK][ROWS];
+  __shared__ const void* s_ptr[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
-  if (!a.src.direct[0] && tid < a.k) s_idx[tid] = a.src.idx[tid];
-  __syncthreads();
-
-  constexpr int P = kWave / LR;
-  const int li = lane % LR, grp = lane / LR;
-  const int n0 = blockIdx.x * rows_per_wg;
-  const size_t row_bytes = (size_t)a.f / 2;
-  const size_t prow_bytes = (size_t)(a.f / a.chunk) * 4;
-  int poff[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) poff[i] = ((li + LR * i) * 32 / a.chunk) * 4;
-
-  for (int r = wave; r < a.k; r += nw) {
-    const uint8_t* blob = expert_blob(a, s_idx, r);
-    if (!blob) {
-      for (int row = lane; row < rows_per_wg; row += kWave) ylds[r][row] = 0.f;
-      continue;
-    }
-    const uint8_t* codes = blob + a.lay.down_codes;
-    const uint8_t* par = blob + a.lay.down_params;
-    // h_r for this lane's columns (already pair-ordered) and its segment sums
-    uint32_t hp[NLD][16];
-    float cseg[NLD], xseg[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const uint4* hv = reinterpret_cast<const uint4*>(a.h + (size_t)r * a.f + (li + LR * i) * 32);
-      float se = 0.f, so = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 u = hv[q];
-        hp[i][4 * q + 0] = u.x; hp[i][4 * q + 1] = u.y; hp[i][4 * q + 2] = u.z; hp[i][4 * q + 3] = u.w;
-        const half2_t h0 = __builtin_bit_cast(half2_t, u.x), h1 = __builtin_bit_cast(half2_t, u.y);
-        const half2_t h2 = __builtin_bit_cast(half2_t, u.z), h3 = __builtin_bit_cast(half2_t, u.w);
-        // dwords 0 and 2 hold the even elements, 1 and 3 the odd ones
-        se += ((float)h0.x + (float)h0.y) + ((float)h2.x + (float)h2.y);
-        so += ((float)h1.x + (float)h1.y) + ((float)h3.x + (float)h3.y);
+  if (tid < a.k) {
+    s_w[tid] = a.w[tid];
+    s_ptr[tid] = expert_pointer(a, tid);
+  }
+  // Pull the next layer's router rows into cache while this kernel streams:
+  // the router workgroup w (rows [16w, 16w + 16)) runs on XCD w % 8, so the
+  // down workgroups of that XCD each fetch one slice of those rows.
+  uint2 pf = make_uint2(0, 0);
+  if (a.pf_base) {
+    const size_t row_bytes = (size_t)a.d * 2, blk = (size_t)kRouteRowsPerWG * row_bytes;
+    const size_t total = (size_t)a.E * row_bytes;
+    const int x = blockIdx.x % kXcds, q = blockIdx.x / kXcds, Q = (gridDim.x + kXcds - 1) / kXcds;
+    const int rw = (a.E + kRouteRowsPerWG - 1) / kRouteRowsPerWG;
+    const int cx = x < rw ? (rw - x + kXcds - 1) / kXcds : 0;
+    const size_t bx = (size_t)cx * blk, share = (bx + Q - 1) / Q;
+    const size_t lo = (size_t)q * share, hi = lo + share < bx ? lo + share : bx;
+    for (size_t o = lo + (size_t)tid * 8; o < hi; o += (size_t)blockDim.x * 8) {
+      const size_t addr = (size_t)(x + kXcds * (int)(o / blk)) * blk + o % blk;
+      if (addr + 8 <= total) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.pf_base + addr);
+        pf.x ^= v.x;
+        pf.y ^= v.y;
       }
-      cseg[i] = fmaf(1024.f, se, 64.f * so);
-      xseg[i] = se + so;
-    }
-    for (int pass = 0; pass < rows_per_wg; pass += P) {
-      const int n = n0 + pass + grp;
-      const bool ok = n < a.d;
-      uint4 c[NLD];
-      uint32_t pr[NLD];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        if (ok) {
-          c[i] = *reinterpret_cast<const uint4*>(codes + (size_t)n * row_bytes + (size_t)(li + LR * i) * 16);
-          pr[i] = *reinterpret_cast<const uint32_t*>(par + (size_t)n * prow_bytes + poff[i]);
-        } else {
-          c[i] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-          pr[i] = 0;
-        }
-      }
-      float y = 0.f;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) y += seg_contrib(c[i], hp[i], cseg[i], xseg[i], pr[i]);
-      y = group_sum<LR>(y);
-      if (li == 0) ylds[r][pass + grp] = y;
     }
   }
   __syncthreads();
-  for (int row = tid; row < rows_per_wg; row += blockDim.x) {
+
+  const int li = lane % LR, grp = lane / LR;
+  const int n0 = blockIdx.x * ROWS;
+  const size_t row_bytes = (size_t)a.f / 2;
+  const size_t prow_bytes = (size_t)(a.f / CHUNK) * 4;
+
+  for (int r = wave; r < a.k; r += nw) {
+    const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
+    if (!blob) {
+      for (int row = lane; row < ROWS; row += kWave) ylds[r][row] = 0.f;
+      continue;
+    }
+    const uint8_t* codes = blob + a.lay.down_codes + li * Run::CW;
+    const uint8_t* par = blob + a.lay.down_params;
+    uint4 hraw[NSEG][4];
+    load_raw<NSEG>(a.h + (size_t)r * a.f + li * (NSEG * 32), hraw);
+    uint4 c[NPASS][NSEG];
+    uint32_t pr[NPASS][Run::NPL];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int n = n0 + p * P + grp;
+      const bool ok = n < a.d;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+        c[p][s] = ok ? gload16(codes + (size_t)n * row_bytes + s * 16)
+                     : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+#pragma unroll
+      for (int j = 0; j < Run::NPL; ++j)
+        pr[p][j] = ok ? gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, j) * 4)
+                      : 0u;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
+    // h_r for this lane's columns (already pair-ordered) and its segment sums
+    uint32_t hp[NSEG][16];
+    float xseg[NSEG];
+    pack_f16_run<NSEG>(hraw, hp, xseg);
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      float y = 0.f;
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+        y += seg_contrib(c[p][s], hp[s], xseg[s], pr[p][Run::param_of_seg(s)]);
+      y = group_sum<LR>(y);
+      if (li == 0) ylds[r][p * P + grp] = y;
+    }
+  }
+  __syncthreads();
+  for (int row = tid; row < ROWS; row += blockDim.x) {
     const int n = n0 + row;
     if (n >= a.d) break;
     float acc = 0.f;
-    for (int r = 0; r < a.k; ++r) acc = fmaf(a.w[r], ylds[r][row], acc);
+    for (int r = 0; r < a.k; ++r) acc = fmaf(s_w[r], ylds[r][row], acc);
     a.residual[n] += acc;
   }
+  asm volatile("" ::"v"(pf.x), "v"(pf.y));  // keeps the prefetch loads alive
 }
 
 // ---------------------------------------------------------------------------
@@ -223,9 +295,10 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a, int rows
 static int pow2_part(int v) { return v & (-v); }
 
 struct RowSplit {
-  int lr, nld;
+  int lr, nseg;
 };
 
+// LR = the largest power of two <= 64 dividing the row's segment count.
 static RowSplit split_row(int cols) {
   const int segs = cols / 32;  // 16-byte segments per row
   int lr = pow2_part(segs);
@@ -237,57 +310,63 @@ bool decode_shape_supported(int d, int f, int chunk) {
   if (chunk != 32 && chunk != 64) return false;
   if (d % 256 || f % 64) return false;
   const RowSplit g = split_row(d), dn = split_row(f);
-  return g.lr >= 8 && g.nld <= 4 && dn.lr >= 2 && dn.nld <= 4;
+  return g.lr >= 8 && g.nseg <= 4 && dn.lr >= 2 && dn.nseg <= 4;
 }
 
-#define SMOE_NLD_SWITCH(NLD_VAL, ...)          \
-  switch (NLD_VAL) {                           \
-    case 1: { constexpr int NLD = 1; __VA_ARGS__; } break; \
-    case 2: { constexpr int NLD = 2; __VA_ARGS__; } break; \
-    case 3: { constexpr int NLD = 3; __VA_ARGS__; } break; \
-    case 4: { constexpr int NLD = 4; __VA_ARGS__; } break; \
-    default: return hipErrorInvalidValue;      \
-  }
+#define SMOE_CASE(N, NAME, ...) case N: { constexpr int NAME = N; __VA_ARGS__; } break;
+#define SMOE_NSEG_SWITCH(V, ...)                                                            \
+  switch (V) { SMOE_CASE(1, NSEG, __VA_ARGS__) SMOE_CASE(2, NSEG, __VA_ARGS__)             \
+               SMOE_CASE(3, NSEG, __VA_ARGS__) SMOE_CASE(4, NSEG, __VA_ARGS__)             \
+               default: return hipErrorInvalidValue; }
+#define SMOE_LR_SWITCH(V, ...)                                                              \
+  switch (V) { SMOE_CASE(2, LR, __VA_ARGS__) SMOE_CASE(4, LR, __VA_ARGS__)                 \
+               SMOE_CASE(8, LR, __VA_ARGS__) SMOE_CASE(16, LR, __VA_ARGS__)                \
+               SMOE_CASE(32, LR, __VA_ARGS__) SMOE_CASE(64, LR, __VA_ARGS__)               \
+               default: return hipErrorInvalidValue; }
+#define SMOE_NP_SWITCH(V, NAME, ...)                                                        \
+  switch (V) { SMOE_CASE(1, NAME, __VA_ARGS__) SMOE_CASE(2, NAME, __VA_ARGS__)             \
+               SMOE_CASE(4, NAME, __VA_ARGS__)                                             \
+               default: return hipErrorInvalidValue; }
+#define SMOE_CHUNK_SWITCH(V, ...)                                                           \
+  switch (V) { SMOE_CASE(32, CHUNK, __VA_ARGS__) SMOE_CASE(64, CHUNK, __VA_ARGS__)         \
+               default: return hipErrorInvalidValue; }
 
-#define SMOE_LR_SWITCH(LR_VAL, ...)            \
-  switch (LR_VAL) {                            \
-    case 2: { constexpr int LR = 2; __VA_ARGS__; } break;  \
-    case 4: { constexpr int LR = 4; __VA_ARGS__; } break;  \
-    case 8: { constexpr int LR = 8; __VA_ARGS__; } break;  \
-    case 16: { constexpr int LR = 16; __VA_ARGS__; } break; \
-    case 32: { constexpr int LR = 32; __VA_ARGS__; } break; \
-    case 64: { constexpr int LR = 64; __VA_ARGS__; } break; \
-    default: return hipErrorInvalidValue;      \
-  }
+// Rows per wave of the gate/up kernel: NP passes of 64/LR rows, the largest
+// NP <= SMOE_GU_ROWS_MAX that divides d_ff and leaves >= SMOE_GU_MIN_WAVES waves.
+static int gate_up_np(int lr, int total, int f) {
+  const int P = 64 / lr;
+  int np = 1;
+  while (np * 2 <= SMOE_GU_ROWS_MAX && f % (P * np * 2) == 0 && total / (P * np * 2) >= SMOE_GU_MIN_WAVES)
+    np *= 2;
+  return np;
+}
 
 hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const RowSplit sp = split_row(a.d);
-  const int P = 64 / sp.lr;
   const int total = a.k * a.f;
-  // about 2048 waves per launch; rows per wave a power of two dividing d_ff
-  int rpw = P;
-  while (rpw * 2 <= 64 && a.f % (rpw * 2) == 0 && total / (rpw * 2) >= 2048) rpw *= 2;
-  const int waves = total / rpw;
+  const int np = gate_up_np(sp.lr, total, a.f);
+  const int waves = total / (np * (64 / sp.lr));
   const dim3 grid((waves + 3) / 4);
-  if (start || stop) {
-    SMOE_LR_SWITCH(sp.lr, SMOE_NLD_SWITCH(sp.nld,
-        hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NLD>), grid, dim3(256), 0, s, start, stop, 0, a, rpw)));
-  } else {
-    SMOE_LR_SWITCH(sp.lr, SMOE_NLD_SWITCH(sp.nld,
-        hipLaunchKernelGGL((decode_gate_up_kernel<LR, NLD>), grid, dim3(256), 0, s, a, rpw)));
-  }
+  SMOE_CHUNK_SWITCH(a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
+      if (start || stop) {
+        hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(256), 0, s, start, stop,
+                              0, a);
+      } else {
+        hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(256), 0, s, a);
+      }))));
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   const RowSplit sp = split_row(a.f);
   const int P = 64 / sp.lr;
-  int rows = P;
-  while (rows * 2 <= kDownMaxRows && a.d / (rows * 2) >= 256) rows *= 2;
+  int np = 1;
+  while (np * 2 <= SMOE_DN_PASSES_MAX && a.d / (P * np * 2) >= SMOE_DN_MIN_WG) np *= 2;
+  const int rows = np * P;
   const int nw = a.k < 8 ? a.k : 8;
   const dim3 grid((a.d + rows - 1) / rows);
-  SMOE_LR_SWITCH(sp.lr, SMOE_NLD_SWITCH(sp.nld,
-      hipLaunchKernelGGL((decode_down_kernel<LR, NLD>), grid, dim3(64 * nw), 0, s, a, rows)));
+  SMOE_CHUNK_SWITCH(a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NPASS,
+      hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK>), grid, dim3(64 * nw), 0, s, a)))));
   return hipGetLastError();
 }
 

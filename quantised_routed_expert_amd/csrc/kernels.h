@@ -1,4 +1,4 @@
-// Kernel argument blocks and launchers (internal to the library).
+// Kernel argument blocks, the block-wide top-k, and launchers (internal).
 #pragma once
 
 #include "smoe_internal.h"
@@ -6,62 +6,76 @@
 namespace smoe {
 
 // ---------------------------------------------------------------------------
-// top-k of one token's E float64 logits by one wave: k rounds of a wave-wide
-// argmax on (logit, -index).  Results in rank order.  Weights in float64.
+// Exact top-k of E <= 256 float64 logits by one workgroup of NT threads
+// (NT a multiple of 128 when E <= 128, of 256 otherwise).
+// Order: logit descending, equal logits -> lower expert index first.  The rank
+// of expert i is the number of experts that beat it; thread t counts the
+// beaters of expert t % EP over one slice of the others (broadcast LDS reads,
+// no cross-lane shuffles), the slices are summed, and the experts of rank < k
+// land in rank order.  Weights: softmax over all E at the selected logits,
+// renormalised over the k when `norm` (Qwen3's norm_topk_prob), in float64.
+// `s.log` must hold the E logits before the call; every thread must call it.
 // ---------------------------------------------------------------------------
-__device__ inline void topk_wave(const double* logits, int E, int k, int norm, int* idx_out, float* w_out) {
-  const int lane = threadIdx.x & 63;
-  double v[4];
-  int id[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    id[i] = lane + 64 * i;
-    v[i] = id[i] < E ? logits[id[i]] : -INFINITY;
-  }
-  bool taken[4] = {id[0] >= E, id[1] >= E, id[2] >= E, id[3] >= E};
-  double sel_v[kMaxTopK];
-  int sel_i[kMaxTopK];
-  for (int r = 0; r < k; ++r) {
-    double bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!taken[i] && (v[i] > bv || (v[i] == bv && id[i] < bi))) { bv = v[i]; bi = id[i]; }
+constexpr int kTopkMaxSlices = 8;
+
+struct TopkShared {
+  double log[kMaxExperts];
+  int part[kTopkMaxSlices][kMaxExperts];
+  int idx[kMaxTopK];
+  double val[kMaxTopK];
+  double ex[kMaxExperts];
+  float w[kMaxTopK];
+};
+
+__device__ inline void topk_block(TopkShared& s, int E, int k, int norm) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int ep = E <= 128 ? 128 : 256;  // experts per slice row
+  int slices = nt / ep;
+  if (slices > kTopkMaxSlices) slices = kTopkMaxSlices;
+  const int i = t % ep, h = t / ep;
+  if (h < slices && i < E) {
+    const int span = (E + slices - 1) / slices;
+    const int j0 = h * span, j1 = min(E, j0 + span);
+    const double li = s.log[i];
+    int cnt = 0;
+#pragma unroll 4
+    for (int j = j0; j < j1; ++j) {
+      const double lj = s.log[j];
+      cnt += (lj > li) | ((lj == li) & (j < i));
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const double ov = __shfl_xor(bv, m, 64);
-      const int oi = __shfl_xor(bi, m, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) if (id[i] == bi) taken[i] = true;
-    sel_v[r] = bv;
-    sel_i[r] = bi;
+    s.part[h][i] = cnt;
   }
-  // softmax over all E at the selected logits; renormalise over the k if asked
-  const double lmax = sel_v[0];
-  double den;
+  __syncthreads();
+  if (t < E) {
+    int rank = 0;
+    for (int q = 0; q < slices; ++q) rank += s.part[q][t];
+    if (rank < k) {
+      s.idx[rank] = t;
+      s.val[rank] = s.log[t];
+    }
+  }
+  __syncthreads();
+  const double lmax = s.val[0];
   if (norm) {
-    den = 0.0;
-    for (int r = 0; r < k; ++r) den += exp(sel_v[r] - lmax);
+    if (t < k) s.ex[t] = exp(s.val[t] - lmax);
   } else {
-    double s = 0.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) if (id[i] < E) s += exp(v[i] - lmax);
-    den = group_sum_f64<64>(s);
+    if (t < E) s.ex[t] = exp(s.log[t] - lmax);
   }
-  if (lane == 0) {
-    for (int r = 0; r < k; ++r) {
-      idx_out[r] = sel_i[r];
-      w_out[r] = (float)(exp(sel_v[r] - lmax) / den);
-    }
+  __syncthreads();
+  if (t < k) {
+    const int n = norm ? k : E;
+    double den = 0.0;
+    for (int j = 0; j < n; ++j) den += s.ex[j];
+    const double num = norm ? s.ex[t] : exp(s.val[t] - lmax);
+    s.w[t] = (float)(num / den);
   }
+  __syncthreads();
 }
 
 struct RouteArgs {
   const float* residual;    // [n_tok][d]
   uint16_t* x_out;          // [n_tok][d] bf16, or null
+  _Float16* px_out;         // [d] the same values as f16 in pair order (one token), or null
   const uint16_t* w_router; // [E][d] bf16
   const float* bias;        // [E] or null
   double* logits;           // [n_tok][E]
@@ -70,8 +84,18 @@ struct RouteArgs {
 };
 
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s);
-hipError_t launch_route_topk(const double* logits, int n_tok, int E, int k, int norm, int32_t* idx,
-                             float* w, hipStream_t s);
+
+struct TopkArgs {
+  const double* logits;      // [n_tok][E]
+  int32_t* idx;              // [n_tok][k]
+  float* w;                  // [n_tok][k]
+  const void* const* table;  // [E] blob pointers of the layer (with ptr_out)
+  const void** ptr_out;      // [n_tok][k] selected blob pointers, or null
+  int32_t* idx_rec;          // optional copies
+  float* w_rec;
+  int E, k, norm;
+};
+hipError_t launch_route_topk(const TopkArgs& a, int n_tok, hipStream_t s);
 
 // Where the k experts of a decode step come from.
 struct ExpertSource {
@@ -80,18 +104,20 @@ struct ExpertSource {
   const void* direct[kMaxTopK];     // blob pointers passed by value (ring slots)
 };
 
+// Router rows per workgroup of the logits kernel (one per wave); the down
+// kernel uses it to prefetch the next layer's router rows per XCD.
+constexpr int kRouteRowsPerWG = 4;
+constexpr int kXcds = 8;  // MI355X: workgroup i is dispatched to XCD i % 8
+
 struct DecodeArgs {
   const uint16_t* x;        // [d] bf16
+  const _Float16* px;       // [d] x as f16 in pair order, or null (then x is converted)
   ExpertSource src;
   const float* w;           // [k] mixing weights (device), read by the down kernel
-  // fused routing (gate/up kernel computes top-k from logits when non-null)
-  const double* logits;     // [E]
-  int32_t* idx_ws;          // [k] written by block 0 when routing is fused
-  float* w_ws;              // [k]
-  int32_t* idx_rec;         // optional copies of the routing
-  float* w_rec;
+  const void* const* ptrs;   // [k] device blob pointers from the router, or null
   _Float16* h;              // [k][d_ff], pair-ordered within groups of 8
   float* residual;          // [d]
+  const uint8_t* pf_base;   // next layer's router [E][d] bf16 to pull into cache, or null
   int d, f, E, k, chunk, norm;
   BlobLayout lay;
 };

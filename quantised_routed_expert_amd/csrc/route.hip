@@ -15,9 +15,13 @@ namespace smoe {
 // RMSNorm + logits.  grid = (ceil(E / 4), ceil(n_tok / TB)); 256 threads.
 // Each workgroup normalises its TB tokens into LDS (redundantly across the
 // expert blocks: the residual is tiny and L2-resident), then each wave computes
-// one expert row's dot products for all TB tokens.  Every bf16*bf16 product is
-// exact in fp32; partial sums are float64.
+// one expert row's dot products for all TB tokens.  The router row is loaded
+// first, in full, so its HBM latency overlaps the norm.  Every bf16*bf16
+// product is exact in fp32; partial sums are float64.
 // ---------------------------------------------------------------------------
+constexpr int kRouteMaxW = 16;  // uint4 of router row per lane: d <= 8192
+constexpr int kRouteMaxR = 8;   // float4 of residual per thread: d <= 8192
+
 template <int TB>
 __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a) {
   extern __shared__ uint16_t xs[];  // [TB][d]
@@ -27,15 +31,32 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a) {
   const int t0 = blockIdx.y * TB;
   const int nt = min(TB, a.n_tok - t0);
   const int d = a.d;
+  const int e = blockIdx.x * 4 + wave;
+  const bool has_e = e < a.E;
+
+  // --- this wave's router row, all of it in flight at once
+  uint4 wv[kRouteMaxW];
+  const uint16_t* wrow = a.w_router + (size_t)(has_e ? e : 0) * d;
+#pragma unroll
+  for (int s = 0; s < kRouteMaxW; ++s) {
+    const int j = lane * 8 + 512 * s;
+    wv[s] = (has_e && j < d) ? *reinterpret_cast<const uint4*>(wrow + j) : make_uint4(0, 0, 0, 0);
+  }
 
   // --- RMSNorm: sum of squares in float64, fixed reduction tree
+  float4 rv[kRouteMaxR];
   for (int t = 0; t < nt; ++t) {
     const float* r = a.residual + (size_t)(t0 + t) * d;
-    double s = 0.0;
-    for (int j = tid * 4; j < d; j += 256 * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(r + j);
-      s += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+#pragma unroll
+    for (int q = 0; q < kRouteMaxR; ++q) {
+      const int j = tid * 4 + 1024 * q;
+      rv[q] = j < d ? *reinterpret_cast<const float4*>(r + j) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < kRouteMaxR; ++q)
+      s += ((double)rv[q].x * rv[q].x + (double)rv[q].y * rv[q].y) +
+           ((double)rv[q].z * rv[q].z + (double)rv[q].w * rv[q].w);
     s = group_sum_f64<64>(s);
     if (lane == 0) red[t][wave] = s;
   }
@@ -48,44 +69,55 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a) {
   for (int t = 0; t < nt; ++t) {
     const float* r = a.residual + (size_t)(t0 + t) * d;
     const double den = rms_den[t];
-    for (int j = tid * 4; j < d; j += 256 * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(r + j);
-      const uint32_t b0 = f64_to_bf16_rne((double)v.x / den), b1 = f64_to_bf16_rne((double)v.y / den);
-      const uint32_t b2 = f64_to_bf16_rne((double)v.z / den), b3 = f64_to_bf16_rne((double)v.w / den);
-      const uint2 packed = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-      *reinterpret_cast<uint2*>(xs + (size_t)t * d + j) = packed;
-      if (blockIdx.x == 0 && a.x_out) *reinterpret_cast<uint2*>(a.x_out + (size_t)(t0 + t) * d + j) = packed;
+    const float inv = (float)(1.0 / den);
+#pragma unroll
+    for (int q = 0; q < kRouteMaxR; ++q) {
+      const int j = tid * 4 + 1024 * q;
+      if (j < d) {
+        // a single token keeps its residual in registers; more tokens reload (L2)
+        const float4 v = TB == 1 ? rv[q] : *reinterpret_cast<const float4*>(r + j);
+        const uint32_t b0 = bf16_of_quotient(v.x, den, inv), b1 = bf16_of_quotient(v.y, den, inv);
+        const uint32_t b2 = bf16_of_quotient(v.z, den, inv), b3 = bf16_of_quotient(v.w, den, inv);
+        const uint2 packed = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        *reinterpret_cast<uint2*>(xs + (size_t)t * d + j) = packed;
+        if (blockIdx.x == 0 && a.x_out) *reinterpret_cast<uint2*>(a.x_out + (size_t)(t0 + t) * d + j) = packed;
+        if (TB == 1 && blockIdx.x == 0 && a.px_out) {
+          // the same values as f16, in pair order within each group of 8
+          const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            a.px_out[(j & ~7) + pair_slot((j & 7) + i)] = (_Float16)bf16_to_f32(bb[i]);
+        }
+      }
     }
   }
   __syncthreads();
+  if (!has_e) return;
 
-  // --- logits: one expert row per wave, 8 bf16 per lane per step
-  const int e = blockIdx.x * 4 + wave;
-  if (e >= a.E) return;
-  const uint16_t* w = a.w_router + (size_t)e * d;
-  double acc[TB];
+  // --- logits: four independent float64 chains per token
+  double acc[TB][4];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) acc[t] = 0.0;
-  for (int j = lane * 8; j < d; j += 64 * 8) {
-    const uint4 wv = *reinterpret_cast<const uint4*>(w + j);
-    float wf[8];
-    wf[0] = bf16_to_f32(wv.x & 0xFFFF); wf[1] = bf16_to_f32(wv.x >> 16);
-    wf[2] = bf16_to_f32(wv.y & 0xFFFF); wf[3] = bf16_to_f32(wv.y >> 16);
-    wf[4] = bf16_to_f32(wv.z & 0xFFFF); wf[5] = bf16_to_f32(wv.z >> 16);
-    wf[6] = bf16_to_f32(wv.w & 0xFFFF); wf[7] = bf16_to_f32(wv.w >> 16);
+  for (int t = 0; t < TB; ++t)
 #pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      if (t < nt) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)t * d + j);
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-        double s = 0.0;
+    for (int c = 0; c < 4; ++c) acc[t][c] = 0.0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // products of two bf16 values are exact in fp32
-          s += (double)(wf[2 * i] * bf16_to_f32(xw[i] & 0xFFFF));
-          s += (double)(wf[2 * i + 1] * bf16_to_f32(xw[i] >> 16));
+  for (int s = 0; s < kRouteMaxW; ++s) {
+    const int j = lane * 8 + 512 * s;
+    if (j < d) {
+      const uint32_t ww[4] = {wv[s].x, wv[s].y, wv[s].z, wv[s].w};
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        if (t < nt) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)t * d + j);
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // products of two bf16 values are exact in fp32
+            const float p0 = bf16_to_f32(ww[i] & 0xFFFF) * bf16_to_f32(xw[i] & 0xFFFF);
+            const float p1 = bf16_to_f32(ww[i] >> 16) * bf16_to_f32(xw[i] >> 16);
+            acc[t][i] += (double)p0 + (double)p1;
+          }
         }
-        acc[t] += s;
       }
     }
   }
@@ -93,18 +125,30 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a) {
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     if (t < nt) {
-      const double v = group_sum_f64<64>(acc[t]);
+      const double v = group_sum_f64<64>((acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]));
       if (lane == 0) a.logits[(size_t)(t0 + t) * a.E + e] = v + b;
     }
   }
 }
 
-// One wave per token.  grid = ceil(n_tok / 4), 256 threads.
-__global__ __launch_bounds__(256) void route_topk_kernel(const double* logits, int n_tok, int E, int k,
-                                                         int norm, int32_t* idx, float* w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= n_tok) return;
-  topk_wave(logits + (size_t)t * E, E, k, norm, idx + (size_t)t * k, w + (size_t)t * k);
+// Top-k for each token: one workgroup of 1024 threads per token (the rank
+// count is spread over 8 slices of the experts).  Optionally also publishes the
+// selected blob pointers from the layer's table and copies of the routing.
+__global__ __launch_bounds__(1024) void route_topk_kernel(TopkArgs a) {
+  __shared__ TopkShared tk;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < a.E) tk.log[tid] = a.logits[(size_t)t * a.E + tid];
+  __syncthreads();
+  topk_block(tk, a.E, a.k, a.norm);
+  if (tid < a.k) {
+    const size_t o = (size_t)t * a.k + tid;
+    const int e = tk.idx[tid];
+    a.idx[o] = e;
+    a.w[o] = tk.w[tid];
+    if (a.ptr_out) a.ptr_out[o] = a.table[e];
+    if (a.idx_rec) a.idx_rec[o] = e;
+    if (a.w_rec) a.w_rec[o] = tk.w[tid];
+  }
 }
 
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
@@ -122,10 +166,8 @@ hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_route_topk(const double* logits, int n_tok, int E, int k, int norm, int32_t* idx,
-                             float* w, hipStream_t s) {
-  hipLaunchKernelGGL(route_topk_kernel, dim3((n_tok + 3) / 4), dim3(256), 0, s, logits, n_tok, E, k,
-                     norm, idx, w);
+hipError_t launch_route_topk(const TopkArgs& a, int n_tok, hipStream_t s) {
+  hipLaunchKernelGGL(route_topk_kernel, dim3(n_tok), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

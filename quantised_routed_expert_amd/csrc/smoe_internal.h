@@ -59,6 +59,20 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
   return (uint16_t)((__float_as_uint(f) >> 16) | (uint32_t)(sign >> 48));
 }
 
+// bf16 bits of fl64(r / den) for a float r.  Fast path: q = r * inv32 in
+// fp32 (inv32 = fp32(1 / den)) is within about one fp32 ulp of the exact
+// quotient; unless it lies within 4 fp32 ulps of a bf16 tie point (or is
+// zero / below the fp32 normal range), its round-to-nearest-even bf16 equals
+// that of the correctly rounded double quotient.  Otherwise divide in fp64.
+__device__ __forceinline__ uint32_t bf16_of_quotient(float r, double den, float inv32) {
+  const float q = r * inv32;
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t rem = b & 0xFFFFu;
+  const uint32_t dist = rem > 0x8000u ? rem - 0x8000u : 0x8000u - rem;
+  if (dist <= 4u || (b & 0x7F800000u) == 0u) return f64_to_bf16_rne((double)r / den);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ uint32_t f16_bits(float v) {
   _Float16 h = (_Float16)v;
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
@@ -70,35 +84,75 @@ __device__ __forceinline__ uint32_t f16_bits(float v) {
 __device__ __forceinline__ int pair_slot(int j) { return j < 4 ? 2 * j : 2 * (j - 4) + 1; }
 
 // ---------------------------------------------------------------------------
-// Wave reductions (butterfly; every lane of the group ends with the result;
-// the summation tree is fixed, so results are bitwise reproducible)
+// Wave reductions.  Within a row of 16 lanes the partial sums move with DPP
+// (quad_perm xor 1 / xor 2, half-row mirror, row mirror), across rows with
+// ds_bpermute.  Every lane of a W-lane group ends with a sum of the group;
+// the order is fixed, so results are bitwise reproducible.
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, kWave);
+  if (W >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (W >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (W >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if (W >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if (W >= 32) v += __shfl_xor(v, 16, kWave);
+  if (W >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum over each W-lane group, valid in the LAST lane of the group (lane
+// W-1 of it): DPP inside rows of 16, then row_bcast:15 / row_bcast:31 to
+// carry row sums upward (no LDS traffic).
+template <int W>
+__device__ __forceinline__ float group_sum_last(float v) {
+  if (W >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (W >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (W >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if (W >= 16) v += dpp_f32<0x140>(v); // row_mirror: every lane of a row holds its row sum
+  if (W >= 32)                          // rows 1, 3 += rows 0, 2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  if (W >= 64)                          // rows 2, 3 += row 1 (= rows 0 + 1)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
   return v;
 }
 
 template <int W>
 __device__ __forceinline__ double group_sum_f64(double v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, kWave);
+  if (W >= 2) v += dpp_f64<0xB1>(v);
+  if (W >= 4) v += dpp_f64<0x4E>(v);
+  if (W >= 8) v += dpp_f64<0x141>(v);
+  if (W >= 16) v += dpp_f64<0x140>(v);
+  if (W >= 32) v += __shfl_xor(v, 16, kWave);
+  if (W >= 64) v += __shfl_xor(v, 32, kWave);
   return v;
 }
 
 // ---------------------------------------------------------------------------
 // Nibble-pair dot products.
-// A dword w of codes holds elements e0..e7 (e_j in bits 4j..4j+3).  OR-ing the
-// f16 pattern of 1024.0 onto a 4-bit field placed at mantissa bits 0..3 gives
-// 1024 + q exactly; at bits 4..7 it gives 1024 + 16 q exactly.  So
-//   (w & 0x000F000F) | 0x64006400 = (1024 + e0, 1024 + e4)
-//   (w & 0x00F000F0) | 0x64006400 = (1024 + 16 e1, 1024 + 16 e5)
-// and the same on w >> 8 for (e2, e6), (e3, e7).  With the input stored in
-// pair order, v_dot2_f32_f16 accumulates
-//   acc_lo += sum (1024 + q) x   over the even elements
-//   acc_hi += sum (1024 + 16 q) x over the odd elements
-// and  sum q x = acc_lo + acc_hi / 16 - (1024 X_even + 64 X_odd).
+// A dword w of codes holds elements e0..e7 (e_j in bits 4j..4j+3).  Masking a
+// 4-bit field into the low mantissa bits of an fp16 half gives the fp16
+// subnormal q * 2^-24 exactly; at bits 4..7 it gives 16 q * 2^-24.  So
+//   w & 0x000F000F        = (e0, e4) * 2^-24
+//   w & 0x00F000F0        = (e1, e5) * 16 * 2^-24
+//   (w >> 8) & 0x000F000F = (e2, e6) * 2^-24
+//   (w >> 8) & 0x00F000F0 = (e3, e7) * 16 * 2^-24
+// and, with the input stored in pair order (dword p of a group of 8 holds
+// (x_p, x_{p+4})), v_dot2_f32_f16 -- which keeps fp16 subnormal inputs on
+// gfx950 -- accumulates exact products into lo (even elements) and hi (odd):
+//   sum q x = 2^24 * (lo + hi / 16).
 // ---------------------------------------------------------------------------
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -109,46 +163,60 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 // One dword of codes against four dwords of pair-ordered f16 inputs.
 __device__ __forceinline__ void nib8_dot(uint32_t w, const uint32_t* xp, float& lo, float& hi) {
-  const uint32_t magic = 0x64006400u;
   const uint32_t w8 = w >> 8;
-  lo = dot2((w & 0x000F000Fu) | magic, xp[0], lo);
-  hi = dot2((w & 0x00F000F0u) | magic, xp[1], hi);
-  lo = dot2((w8 & 0x000F000Fu) | magic, xp[2], lo);
-  hi = dot2((w8 & 0x00F000F0u) | magic, xp[3], hi);
+  lo = dot2(w & 0x000F000Fu, xp[0], lo);
+  hi = dot2(w & 0x00F000F0u, xp[1], hi);
+  lo = dot2(w8 & 0x000F000Fu, xp[2], lo);
+  hi = dot2(w8 & 0x00F000F0u, xp[3], hi);
 }
 
 // Contribution of one 16-byte segment (32 codes, inside one chunk) of a row:
-// scale * sum(q x) + min * sum(x).  xp: 16 pair-ordered input dwords;
-// cseg = 1024 X_even + 64 X_odd and xseg = X_even + X_odd for the segment;
-// params: bf16 scale (low half) and bf16 min (high half).
-__device__ __forceinline__ float seg_contrib(const uint4& c, const uint32_t* xp, float cseg, float xseg,
-                                             uint32_t params) {
+// scale * sum(q x) + min * sum(x).  xp: 16 pair-ordered input dwords; xseg =
+// sum of the segment's inputs; params: bf16 scale (low half), bf16 min (high).
+__device__ __forceinline__ float seg_contrib(const uint4& c, const uint32_t* xp, float xseg, uint32_t params) {
   float lo = 0.f, hi = 0.f;
   nib8_dot(c.x, xp + 0, lo, hi);
   nib8_dot(c.y, xp + 4, lo, hi);
   nib8_dot(c.z, xp + 8, lo, hi);
   nib8_dot(c.w, xp + 12, lo, hi);
-  const float sq = fmaf(hi, 0.0625f, lo) - cseg;
+  const float sq = fmaf(hi, 0.0625f, lo) * 16777216.0f;  // sum q x
   const float s = __uint_as_float(params << 16);
   const float m = __uint_as_float(params & 0xFFFF0000u);
   return fmaf(s, sq, m * xseg);
 }
 
-// Builds the pair-ordered f16 dwords and the two sums of a 32-value segment
-// from 32 float values v[0..31] (exact in f16 for the magnitudes used here).
-__device__ __forceinline__ void pack_segment(const float* v, uint32_t* xp, float& cseg, float& xseg) {
-  float se = 0.f, so = 0.f;
+// Sum of the 32 values of one pair-ordered f16 segment (dot2 against ones).
+__device__ __forceinline__ float seg_sum(const uint32_t* xp) {
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    a = dot2(xp[i], 0x3C003C00u, a);
+    b = dot2(xp[i + 1], 0x3C003C00u, b);
+  }
+  return a + b;
+}
+
+// Pair-ordered f16 dwords of a 32-value segment from 32 float values v[0..31]
+// (exact in f16 for the magnitudes used here).
+__device__ __forceinline__ void pack_segment(const float* v, uint32_t* xp) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const float* e = v + 8 * g;
 #pragma unroll
     for (int p = 0; p < 4; ++p) xp[4 * g + p] = f16_bits(e[p]) | (f16_bits(e[p + 4]) << 16);
-    se += (e[0] + e[2]) + (e[4] + e[6]);
-    so += (e[1] + e[3]) + (e[5] + e[7]);
   }
-  cseg = fmaf(1024.f, se, 64.f * so);
-  xseg = se + so;
 }
+
+// Loads through the global address space (pointers read from LDS or kernel
+// arguments are otherwise generic, and would become flat loads).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t g_u32x4;
+typedef __attribute__((address_space(1))) const uint32_t g_uint32;
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  const u32x4_t v = *(g_u32x4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t gload4(const void* p) { return *(g_uint32*)(p); }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
