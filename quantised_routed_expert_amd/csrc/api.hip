@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include "kernels.h"
+#include "prefill.h"
 
 
 namespace smoe {
@@ -38,6 +39,8 @@ int check_dims(const smoe_dims* d) {
     return fail(SMOE_EINVAL, "top_k=%d must be in [1, min(n_experts, %d)]", d->top_k, kMaxTopK);
   if (d->chunk != 32 && d->chunk != 64) return fail(SMOE_EINVAL, "chunk=%d must be 32 or 64", d->chunk);
   if (!(d->rms_eps >= 0.0f) || d->rms_eps > 1.0f) return fail(SMOE_EINVAL, "rms_eps out of range");
+  if (d->d_model % 128 || d->d_ff % 128)
+    return fail(SMOE_EINVAL, "d_model=%d and d_ff=%d must be multiples of 128", d->d_model, d->d_ff);
   if (!decode_shape_supported(d->d_model, d->d_ff, d->chunk))
     return fail(SMOE_EINVAL, "unsupported row split for d_model=%d d_ff=%d", d->d_model, d->d_ff);
   return SMOE_OK;
@@ -60,13 +63,9 @@ Workspace ws_layout(const smoe_dims* d, int max_tokens) {
   w.x = o;      o = align_up(o + T * D * 2, 256);
   w.px = o;     o = align_up(o + D * 2, 256);
   w.h = o;      o = align_up(o + k * F * 2, 256);
-  if (max_tokens > 1) {
-    w.ph = o;   o = align_up(o + T * k * F * 2, 256);
-    w.py = o;   o = align_up(o + T * k * D * 4, 256);
-    w.pinv = o; o = align_up(o + T * k * 4, 256);
-  } else {
-    w.ph = w.py = w.pinv = o;
-  }
+  w.ph = o;     o = align_up(o + T * k * F * 2, 256);
+  w.py = o;     o = align_up(o + T * k * D * 4, 256);
+  w.pinv = o;   o = align_up(o + T * k * 4, 256);
   w.end = o;
   return w;
 }
@@ -256,6 +255,46 @@ int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, co
     he = launch_decode_down(a, s);
     if (he != hipSuccess) return hip_fail(he, "decode down launch");
   }
+  return SMOE_OK;
+}
+
+int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x, const int32_t* topk_idx,
+                           const float* topk_w, const void* const* expert_table, float* residual,
+                           int32_t* union_ids, int32_t* union_count, int32_t* offsets, int32_t* perm, void* ws,
+                           size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int e = check_dims(d)) return e;
+  if (n_tok < 1 || n_tok > kMaxPrefillTokens)
+    return fail(SMOE_EINVAL, "n_tok=%d must be in [1, %d]", n_tok, kMaxPrefillTokens);
+  if (!x || !topk_idx || !topk_w || !expert_table || !residual || !union_ids || !union_count || !offsets || !perm)
+    return fail(SMOE_EINVAL, "NULL argument");
+  if (!aligned16(x) || !aligned16(residual)) return fail(SMOE_EINVAL, "x and residual must be 16-byte aligned");
+  Workspace L;
+  if (int e = check_ws(d, n_tok, ws, ws_bytes, &L)) return e;
+  char* base = (char*)ws;
+  PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.idx = topk_idx;
+  a.w = topk_w;
+  a.table = expert_table;
+  a.residual = residual;
+  a.union_ids = union_ids;
+  a.union_count = union_count;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.invperm = reinterpret_cast<int32_t*>(base + L.pinv);
+  a.H = reinterpret_cast<_Float16*>(base + L.ph);
+  a.Y = reinterpret_cast<float*>(base + L.py);
+  a.T = n_tok;
+  a.d = d->d_model;
+  a.f = d->d_ff;
+  a.E = d->n_experts;
+  a.k = d->top_k;
+  a.chunk = d->chunk;
+  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk);
+  hipError_t he = launch_prefill(a, (hipStream_t)stream);
+  if (he != hipSuccess) return hip_fail(he, "prefill launch");
   return SMOE_OK;
 }
 

@@ -1,0 +1,27 @@
+// Prefill (layer-major, one chunk of up to 64 tokens) argument block (internal).
+#pragma once
+
+#include "kernels.h"
+
+namespace smoe {
+
+struct PrefillArgs {
+  const uint16_t* x;          // [T][d] bf16 (the router's RMSNorm output)
+  const int32_t* idx;         // [T][k]
+  const float* w;             // [T][k]
+  const void* const* table;   // [E] blob pointers of the layer
+  float* residual;            // [T][d]
+  int32_t* union_ids;         // [min(E, T*k)]
+  int32_t* union_count;       // [1]
+  int32_t* offsets;           // [min(E, T*k) + 1]
+  int32_t* perm;              // [T*k]
+  int32_t* invperm;           // [T*k] position of entry t*k+r in perm (workspace)
+  _Float16* H;                // [T*k][f] SwiGLU activations, fp16 pair order
+  float* Y;                   // [T*k][d] per-entry expert outputs
+  int T, d, f, E, k, chunk;
+  BlobLayout lay;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace smoe

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = {
     "tiny": synth.Dims(256, 128, 16, 4, 32),
-    "ragged": synth.Dims(768, 192, 24, 3, 64),
+    "ragged": synth.Dims(768, 384, 24, 3, 64),
     "q30b": synth.Dims(2048, 768, 128, 8, 64),
     "q235b": synth.Dims(4096, 1536, 128, 8, 64),
 }
