@@ -83,8 +83,6 @@ def lib():
             "smoe_ring_destroy": (I, [VP]),
         }
         for name, (res, args) in sig.items():
-            if not hasattr(L, name):
-                continue          # calling it raises AttributeError
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args

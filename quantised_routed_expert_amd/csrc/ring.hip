@@ -1,0 +1,208 @@
+// Expert ring: an LRU cache of (layer, expert) blobs in HBM slots, filled from
+// a vault in host memory ("The Ring Is an LRU Cache", Optimizations page;
+// slot clamp [64, 4096] from the System Overview memory budget).
+//
+// Policy (host side, single-threaded per handle):
+//   - a request for a resident (layer, expert) is a hit: no bytes move;
+//   - a miss takes the lowest-index empty slot, else evicts the unpinned slot
+//     with the oldest tick (lazy LRU; slots held by the current acquisition are
+//     pinned and never evicted);
+//   - every request, hit or load, stamps the slot with a fresh tick;
+//   - slots keep their data and identity when released; nothing is ever wiped.
+// Data movement: misses are copied with hipMemcpyAsync on the copy stream.
+// Before the copies of an acquisition, the copy stream waits for all work
+// already enqueued on the compute stream (so no slot is overwritten while an
+// earlier kernel may still read it); after them, the compute stream waits on
+// the completion event of every slot it is handed.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+
+namespace smoe {
+int fail(int code, const char* fmt, ...);
+}
+using smoe::fail;
+
+struct smoe_ring {
+  smoe_ring_desc desc;
+  std::vector<long long> key;      // per slot: layer * E + expert, or -1 when empty
+  std::vector<unsigned long long> tick;
+  std::vector<unsigned char> pinned;
+  std::vector<unsigned char> fill_recorded;
+  std::vector<hipEvent_t> fill_done;  // per slot, recorded after its latest fill
+  std::vector<int> where;          // (layer * E + expert) -> slot, or -1
+  std::vector<int> held;           // slots of the current acquisition
+  hipEvent_t compute_mark;
+  unsigned long long now = 0;
+  int n_filled = 0;                // empty slots are exactly [n_filled, n_slots)
+  unsigned long long hits = 0, misses = 0, evictions = 0, h2d_bytes = 0;
+  std::vector<smoe_ring_event> log;
+};
+
+static int hip_err(hipError_t e, const char* what) {
+  return fail(SMOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+extern "C" {
+
+int smoe_ring_create(const smoe_ring_desc* d, smoe_ring** out) {
+  if (!d || !out) return fail(SMOE_EINVAL, "NULL argument");
+  *out = nullptr;
+  if (d->n_slots < 64 || d->n_slots > 4096)
+    return fail(SMOE_EINVAL, "n_slots=%d must be in [64, 4096]", d->n_slots);
+  if (d->n_layers < 1 || d->n_experts < 1 || d->n_experts > smoe::kMaxExperts)
+    return fail(SMOE_EINVAL, "n_layers=%d / n_experts=%d out of range", d->n_layers, d->n_experts);
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > smoe::kMaxTopK || d->n_slots < d->top_k)
+    return fail(SMOE_EINVAL, "top_k=%d out of range for %d experts / %d slots", d->top_k, d->n_experts,
+                d->n_slots);
+  if (d->slot_bytes == 0 || d->slot_stride < d->slot_bytes || d->slot_stride % 16)
+    return fail(SMOE_EINVAL, "slot_bytes/slot_stride invalid (stride must be >= bytes, multiple of 16)");
+  if (!d->vault_host || d->vault_stride < d->slot_bytes || !d->slab_dev)
+    return fail(SMOE_EINVAL, "vault_host / vault_stride / slab_dev invalid");
+  if (((uintptr_t)d->slab_dev & 15u) != 0) return fail(SMOE_EINVAL, "slab_dev must be 16-byte aligned");
+  smoe_ring* r = new (std::nothrow) smoe_ring();
+  if (!r) return fail(SMOE_ENOMEM, "host allocation failed");
+  r->desc = *d;
+  const size_t n = (size_t)d->n_slots;
+  r->key.assign(n, -1);
+  r->tick.assign(n, 0);
+  r->pinned.assign(n, 0);
+  r->fill_recorded.assign(n, 0);
+  r->fill_done.assign(n, nullptr);
+  r->where.assign((size_t)d->n_layers * d->n_experts, -1);
+  r->log.reserve(d->log_capacity);
+  hipError_t e = hipEventCreateWithFlags(&r->compute_mark, hipEventDisableTiming);
+  for (size_t i = 0; e == hipSuccess && i < n; ++i) e = hipEventCreateWithFlags(&r->fill_done[i], hipEventDisableTiming);
+  if (e != hipSuccess) {
+    for (hipEvent_t ev : r->fill_done)
+      if (ev) (void)hipEventDestroy(ev);
+    if (r->compute_mark) (void)hipEventDestroy(r->compute_mark);
+    delete r;
+    return hip_err(e, "hipEventCreate");
+  }
+  *out = r;
+  return SMOE_OK;
+}
+
+int smoe_ring_release(smoe_ring* r) {
+  if (!r) return fail(SMOE_EINVAL, "NULL ring");
+  for (int s : r->held) r->pinned[s] = 0;
+  r->held.clear();
+  return SMOE_OK;
+}
+
+int smoe_ring_acquire(smoe_ring* r, int32_t layer, const int32_t* experts, int32_t k, const void** slot_ptrs,
+                      void* compute_stream) {
+  if (!r || !experts || !slot_ptrs) return fail(SMOE_EINVAL, "NULL argument");
+  const smoe_ring_desc& d = r->desc;
+  if (layer < 0 || layer >= d.n_layers) return fail(SMOE_EINVAL, "layer=%d out of range", layer);
+  if (k < 1 || k > d.top_k) return fail(SMOE_EINVAL, "k=%d must be in [1, %d]", k, d.top_k);
+  for (int i = 0; i < k; ++i) {
+    if (experts[i] < 0 || experts[i] >= d.n_experts) return fail(SMOE_EINVAL, "expert %d out of range", experts[i]);
+    for (int j = 0; j < i; ++j)
+      if (experts[j] == experts[i]) return fail(SMOE_EINVAL, "expert %d requested twice", experts[i]);
+  }
+  hipStream_t cs = (hipStream_t)compute_stream, ps = (hipStream_t)d.copy_stream;
+  smoe_ring_release(r);
+  // fills below must not overtake work already enqueued on the compute stream
+  hipError_t he = hipEventRecord(r->compute_mark, cs);
+  if (he == hipSuccess) he = hipStreamWaitEvent(ps, r->compute_mark, 0);
+  if (he != hipSuccess) return hip_err(he, "ordering the copy stream after the compute stream");
+
+  for (int rank = 0; rank < k; ++rank) {
+    const long long kk = (long long)layer * d.n_experts + experts[rank];
+    int s = r->where[kk];
+    smoe_ring_event ev;
+    ev.layer = layer;
+    ev.rank = rank;
+    ev.expert = experts[rank];
+    ev.evicted_layer = -1;
+    ev.evicted_expert = -1;
+    ev.pad = 0;
+    if (s >= 0) {
+      ev.kind = 0;
+      ++r->hits;
+    } else {
+      if (r->n_filled < d.n_slots) {
+        s = r->n_filled++;
+      } else {
+        unsigned long long best = ~0ull;
+        for (int i = 0; i < d.n_slots; ++i)
+          if (!r->pinned[i] && r->tick[i] < best) {
+            best = r->tick[i];
+            s = i;
+          }
+        if (s < 0) return fail(SMOE_ENOSLOT, "every slot is held by the current layer");
+        const long long old = r->key[s];
+        r->where[old] = -1;
+        ev.evicted_layer = (int)(old / d.n_experts);
+        ev.evicted_expert = (int)(old % d.n_experts);
+        ++r->evictions;
+      }
+      r->key[s] = kk;
+      r->where[kk] = s;
+      const char* src = (const char*)d.vault_host + (size_t)kk * d.vault_stride;
+      char* dst = (char*)d.slab_dev + (size_t)s * d.slot_stride;
+      he = hipMemcpyAsync(dst, src, d.slot_bytes, hipMemcpyHostToDevice, ps);
+      if (he == hipSuccess) he = hipEventRecord(r->fill_done[s], ps);
+      if (he != hipSuccess) return hip_err(he, "fill");
+      r->fill_recorded[s] = 1;
+      r->h2d_bytes += d.slot_bytes;
+      ev.kind = 1;
+      ++r->misses;
+    }
+    r->tick[s] = r->now++;
+    r->pinned[s] = 1;
+    r->held.push_back(s);
+    ev.slot = s;
+    if (r->log.size() < d.log_capacity) r->log.push_back(ev);
+    slot_ptrs[rank] = (const char*)d.slab_dev + (size_t)s * d.slot_stride;
+  }
+  // the compute stream may use a slot only once its latest fill has landed
+  for (int s : r->held) {
+    if (!r->fill_recorded[s]) continue;
+    he = hipStreamWaitEvent(cs, r->fill_done[s], 0);
+    if (he != hipSuccess) return hip_err(he, "hipStreamWaitEvent");
+  }
+  return SMOE_OK;
+}
+
+int smoe_ring_stats(const smoe_ring* r, uint64_t* hits, uint64_t* misses, uint64_t* evictions,
+                    uint64_t* h2d_bytes) {
+  if (!r) return fail(SMOE_EINVAL, "NULL ring");
+  if (hits) *hits = r->hits;
+  if (misses) *misses = r->misses;
+  if (evictions) *evictions = r->evictions;
+  if (h2d_bytes) *h2d_bytes = r->h2d_bytes;
+  return SMOE_OK;
+}
+
+int smoe_ring_log(const smoe_ring* r, smoe_ring_event* events, size_t cap, size_t* n_out) {
+  if (!r || !n_out || (cap && !events)) return fail(SMOE_EINVAL, "NULL argument");
+  const size_t n = r->log.size() < cap ? r->log.size() : cap;
+  if (n) memcpy(events, r->log.data(), n * sizeof(smoe_ring_event));
+  *n_out = n;
+  return SMOE_OK;
+}
+
+int smoe_ring_destroy(smoe_ring* r) {
+  if (!r) return SMOE_OK;
+  if (!r->held.empty()) return fail(SMOE_EBUSY, "slots are still held: release first");
+  // no copy into the caller's slab may outlive the handle
+  for (size_t i = 0; i < r->fill_done.size(); ++i) {
+    if (r->fill_recorded[i]) {
+      const hipError_t e = hipEventSynchronize(r->fill_done[i]);
+      if (e != hipSuccess) return hip_err(e, "waiting for pending fills");
+    }
+  }
+  for (hipEvent_t ev : r->fill_done) (void)hipEventDestroy(ev);
+  (void)hipEventDestroy(r->compute_mark);
+  delete r;
+  return SMOE_OK;
+}
+
+}  // extern "C"
