@@ -9,6 +9,11 @@ added into the residual, each step starting from a fresh N(0,1) bf16 hidden
 state.  The token's 282 kernels are captured once into a HIP graph and
 replayed; the step's input copy runs eagerly inside the timed region.
 
+Other workloads (one JSON line each): ``--workload prefill`` -- a 512-token
+prompt in chunks of 64 through the same 94 layers, layer-major, Zipf-biased
+routing; ``--workload ring`` -- decode with the experts in a 1536-slot HBM ring
+refilled from a vault in pinned host memory (Markov hidden states).
+
 Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
 one GPU.
 """
@@ -31,6 +36,43 @@ import synth  # noqa: E402
 from synth.device import DeviceStack  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+# sources of the decode gate/up kernel: a stored traffic figure counts only
+# while they are unchanged since its counters were read
+GATE_UP_SOURCES = ("quantised_routed_expert_amd/csrc/decode.hip", "quantised_routed_expert_amd/csrc/kernels.h",
+                   "quantised_routed_expert_amd/csrc/smoe_internal.h")
+TRAFFIC_FILE = "profiles/hbm_traffic_decode_gate_up_235b.txt"
+
+
+def sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary (FETCH_SIZE
+    + WRITE_SIZE, each scaled by the copy-kernel calibration), or None if there
+    is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != sources_digest(GATE_UP_SOURCES):
+        log("stored traffic figure is stale (kernel sources changed): traffic = null")
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -42,14 +84,16 @@ class HipEvents:
 
     def __init__(self, n):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             h = ctypes.c_void_p(0)
-            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            # timing-only events: no system-scope fence (no L2 writeback and
+            # invalidate around the timed kernel)
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
             self.ev.append(h.value)
 
     def elapsed_ms(self, a, b):
@@ -97,20 +141,7 @@ def cpu_baseline(stack, wl, budget_s=15.0):
                       f"{spent:.1f} s of oracle time; tokens/s extrapolated to all {wl.n_layers} layers"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--instrument-steps", type=int, default=4)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
-              "MI355X (no multi-GPU path exists in this build)", file=sys.stderr)
-        sys.exit(2)
-
+def bench_decode(args):
     wl = synth.CONFIGS[2]
     dims = wl.dims
     torch.cuda.set_device(0)
@@ -157,7 +188,11 @@ def main():
     tok_s = K / (ms / 1000.0)
     log(f"timed {K} steps: {ms:.3f} ms, {tok_s:.1f} tokens/s")
 
-    # per-kernel timing of the gate/up kernel (the dominant kernel), eager pass
+    # per-kernel timing of the gate/up kernel (the dominant kernel): the same
+    # token launched eagerly with hipExtLaunchKernel start/stop events on the
+    # library's stream.  A spin kernel ahead of it keeps the GPU busy while the
+    # host enqueues all of the token's launches, so they then run back to back
+    # as in the graph replays above.
     off = synth.blob_sections(dims)
     gate_up_bytes = (off["down_codes"] - off["gate_codes"]) + (off["down_params"] - off["gate_params"])
     per_launch = dims.top_k * gate_up_bytes
@@ -165,6 +200,7 @@ def main():
     durs = []
     for i in range(args.instrument_steps):
         resid.copy_(H[W + i % K])
+        torch.cuda._sleep(20_000_000)
         smoe.decode_layers(dims, wl.n_layers, resid, stack.router, None, stack.tables, ws, events=ev.ev)
         torch.cuda.synchronize()
         durs += [ev.elapsed_ms(2 * L, 2 * L + 1) for L in range(wl.n_layers)]
@@ -192,14 +228,283 @@ def main():
                    "vault_bytes": stack.vault.numel(), "parallelism": "single GPU"},
         "gbps_q4_expert_and_router_bytes": tok_s * bytes_per_token / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(),
                      "kernel": "decode_gate_up_kernel", "bytes_per_launch": per_launch,
-                     "avg_launch_us": gu_ms * 1000.0},
+                     "avg_launch_us": gu_ms * 1000.0, "launches_timed": len(durs),
+                     "timing": "hipExtLaunchKernel start/stop events, eager token with the queue pre-filled"},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(stack, wl, args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def graph_of(fn):
+    """Run ``fn`` once eagerly on a side stream (warm-up), then capture it."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(g, warmup, steps, before=None):
+    for i in range(warmup):
+        if before:
+            before(i)
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        if before:
+            before(warmup + i)
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_prefill(args):
+    """Layer-major prefill of a 512-token prompt in chunks of 64: for each chunk
+    and layer, route the chunk (Zipf-biased logits), build the expert union,
+    run the grouped expert FFN and combine into the residual.
+
+    Two readings of the per-layer input are timed.  ``value``: every layer's
+    MoE input is the prompt's own N(0,1) hidden state (the layers' routers and
+    Zipf permutations are independent, so each layer sees realistic unions).
+    ``chained``: layer L+1 reads layer L's output residual; with the synthetic
+    weights (mean -scale/2 per element) the residual drifts to one common
+    direction within ~10 layers and every token then routes alike, so the
+    unions collapse."""
+    wl = synth.CONFIGS[3]
+    dims = wl.dims
+    T, C = wl.steps, wl.prefill_chunk
+    n_chunks = T // C
+    NL = wl.n_layers
+    torch.cuda.set_device(0)
+    stack = DeviceStack(wl.seed, dims, NL, zipf_s=wl.zipf_s)
+    torch.cuda.synchronize()
+    log(f"stack ready: vault {stack.vault.numel() / 1e9:.2f} GB")
+    prompt = torch.from_numpy(np.stack([synth.hidden_bf16(wl.seed, 20_000 + t, dims.d_model)
+                                        for t in range(T)])).cuda()
+    resid = torch.empty_like(prompt)
+    mu = min(dims.n_experts, C * dims.top_k)
+    x = torch.empty((C, dims.d_model), dtype=torch.int16, device="cuda")
+    idx = torch.empty((C, dims.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, dims.top_k), dtype=torch.float32, device="cuda")
+    ucount = {m: torch.zeros((n_chunks, NL), dtype=torch.int32, device="cuda") for m in ("fresh", "chained")}
+    uids = torch.empty(mu, dtype=torch.int32, device="cuda")
+    offs = torch.empty(mu + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(C * dims.top_k, dtype=torch.int32, device="cuda")
+    ws = smoe.workspace(dims, C)
+
+    def layer(L, c, r, uc):
+        smoe.route(dims, r, x, stack.router_layer(L), stack.bias_layer(L), idx, w, ws)
+        smoe.moe_prefill_chunk(dims, x, idx, w, stack.table(L), r, uids, uc[c, L:L + 1], offs, perm, ws)
+
+    def prompt_fresh():
+        for c in range(n_chunks):
+            r = resid[c * C:(c + 1) * C]
+            for L in range(NL):
+                r.copy_(prompt[c * C:(c + 1) * C])
+                layer(L, c, r, ucount["fresh"])
+
+    def prompt_chained():
+        resid.copy_(prompt)
+        for c in range(n_chunks):
+            r = resid[c * C:(c + 1) * C]
+            for L in range(NL):
+                layer(L, c, r, ucount["chained"])
+
+    off = synth.blob_sections(dims)
+    flops_per_prompt = 6.0 * dims.d_model * dims.d_ff * dims.top_k * NL * T
+    res = {}
+    for mode, fn in (("fresh", prompt_fresh), ("chained", prompt_chained)):
+        g = graph_of(fn)
+        ms = time_replays(g, args.warmup, args.steps)
+        u = ucount[mode].cpu().numpy()
+        ub = int(u.sum()) * off["bytes"]
+        res[mode] = {"ms": ms, "tok_s": T / (ms / 1e3), "mean_union": float(u.mean()),
+                     "union_bytes": ub, "union_gbps": ub / (ms / 1e3) / 1e9,
+                     "mfma_utilisation": flops_per_prompt / (ms / 1e3) / 2.5e15}
+        log(f"prefill[{mode}]: {ms:.2f} ms/prompt, {res[mode]['tok_s']:.0f} tokens/s, "
+            f"mean |union| {u.mean():.1f}, {res[mode]['union_gbps']:.0f} GB/s on union bytes")
+        del g
+    f = res["fresh"]
+    out = {
+        "metric": "layer-major prefill prompt tokens/s + GB/s on union expert bytes (235B-shape, 512-token "
+                  "prompt, chunks of 64)",
+        "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4-affine weights dequantised to fp16, fp16 MFMA with fp32 accumulation; float64 router",
+        "data": "synthetic (seeded SplitMix64 codes/scales, N(0,0.02) router, Zipf(1.1) logit bias, N(0,1) bf16 "
+                "prompt hidden states fed to every layer)",
+        "config": {"workload": wl.name, "layers": NL, "prompt_tokens": T, "chunk": C,
+                   "parallelism": "single GPU"},
+        "mean_union": f["mean_union"], "union_bytes_per_prompt": f["union_bytes"], "union_gbps": f["union_gbps"],
+        "union_hbm_frac": f["union_gbps"] / HBM_PEAK_GBPS, "mfma_utilisation": f["mfma_utilisation"],
+        "chained": {k: res["chained"][k] for k in ("tok_s", "ms", "mean_union", "union_gbps", "mfma_utilisation")},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_ring(args):
+    """Decode with a 1536-slot HBM ring over a vault in pinned host memory.
+    Each layer's router input follows its own Markov chain over tokens
+    (h_t = 0.7 h_{t-1} + 0.3 z_t), so consecutive tokens share part of their
+    experts; the residual update of each layer is computed and discarded."""
+    wl = synth.CONFIGS[4]
+    dims = wl.dims
+    E, NL = dims.n_experts, wl.n_layers
+    torch.cuda.set_device(0)
+    off = synth.blob_sections(dims)
+    stride = off["stride"]
+    t0 = time.time()
+    from synth.device import fill_experts, router_stack, u16_to_device
+    # the vault: one host allocation per layer, drawn on the device and copied
+    # down.  Layers are page-locked (hipHostMalloc) up to --pinned-gib; the
+    # driver caps page-locked memory (64 GiB on the MI355X hosts measured), so
+    # the rest of a 128 GB vault stays pageable and its fills are staged by
+    # the HIP runtime.
+    pinned_budget = int(args.pinned_gib * (1 << 30))
+    vault, views = [], []
+    for L in range(NL):
+        buf = None
+        if (len(vault) + 1) * E * stride <= pinned_budget:
+            try:
+                buf = smoe.PinnedHost(E * stride)
+            except smoe.SmoeError:
+                pinned_budget = 0
+        if buf is not None:
+            vault.append(buf)
+            views.append(buf.tensor())
+        else:
+            views.append(torch.empty(E * stride, dtype=torch.uint8))
+    n_pinned = len(vault)
+    log(f"vault: {n_pinned} of {NL} layers page-locked ({n_pinned * E * stride / 1e9:.1f} GB) "
+        f"in {time.time() - t0:.1f} s")
+    stage = torch.empty(E * stride, dtype=torch.uint8, device="cuda")
+    for L in range(NL):
+        fill_experts(wl.seed, dims, L, 0, E, stage.data_ptr(), stride)
+        views[L].copy_(stage)
+    del stage
+    router = u16_to_device(router_stack(wl.seed, dims, NL))
+    keep, fresh = wl.markov
+    W, K = args.warmup, args.steps
+    hidden = torch.from_numpy(np.stack([synth.markov_hidden(wl.seed, W + K, dims.d_model, keep, fresh, lane=L)
+                                        for L in range(NL)])).cuda()          # [L][t][d]
+    log(f"vault and Markov states drawn in {time.time() - t0:.1f} s")
+    n_slots = wl.ring_slots
+    slab = torch.empty(n_slots * stride, dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    ring = smoe.Ring(n_slots, NL, E, dims.top_k, off["bytes"], stride, [v.data_ptr() for v in views], stride,
+                     slab.data_ptr(), copy_stream, 0)
+    ws = smoe.workspace(dims, 1)
+    x = torch.empty((1, dims.d_model), dtype=torch.int16, device="cuda")
+    idx = torch.empty((1, dims.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, dims.top_k), dtype=torch.float32, device="cuda")
+    idx_host = torch.empty((1, dims.top_k), dtype=torch.int32, pin_memory=True)
+    r = torch.empty((1, dims.d_model), dtype=torch.float32, device="cuda")
+    prev = [None] * NL
+    repeats = []
+
+    def token(t, count):
+        for L in range(NL):
+            r.copy_(hidden[L, t:t + 1])
+            smoe.route(dims, r, x, router[L], None, idx, w, ws)
+            idx_host.copy_(idx)
+            torch.cuda.current_stream().synchronize()
+            experts = idx_host.numpy()[0].tolist()
+            if count and prev[L] is not None:
+                repeats.append(len(set(experts) & set(prev[L])) / dims.top_k)
+            prev[L] = experts
+            ptrs = ring.acquire(L, experts)
+            smoe.moe_decode_slots(dims, x, w, ptrs, r, ws)
+
+    for t in range(W):
+        token(t, False)
+    torch.cuda.synchronize()
+    s0 = ring.stats()
+    t1 = time.time()
+    for t in range(K):
+        token(W + t, True)
+    torch.cuda.synchronize()
+    dt = time.time() - t1
+    s1 = ring.stats()
+    ring.release()
+    ring.destroy()
+    hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+    h2d = s1["h2d_bytes"] - s0["h2d_bytes"]
+    tok_s = K / dt
+    log(f"ring: {tok_s:.2f} tokens/s, hit rate {hits / max(1, hits + misses):.3f}, "
+        f"H2D {h2d / dt / 1e9:.1f} GB/s, repeat {np.mean(repeats):.3f}")
+    out = {
+        "metric": "ring-backed MoE decode tokens/s (235B-shape, 1536-slot HBM ring over a pinned-host vault)",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": dt * 1000.0 / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4-affine weights, f16 dot products with fp32 accumulation; float64 router",
+        "data": "synthetic (per-layer Markov router inputs h_t = 0.7 h_{t-1} + 0.3 z_t)",
+        "config": {"workload": wl.name, "layers": NL, "ring_slots": n_slots, "parallelism": "single GPU"},
+        "hit_rate": hits / max(1, hits + misses), "misses_per_token": misses / K,
+        "h2d_gbps": h2d / dt / 1e9, "expert_repeat_fraction": float(np.mean(repeats)),
+        "vault_layers_page_locked": n_pinned,
+    }
+    del views
+    for v in vault:
+        v.free()
+    print(json.dumps(out), flush=True)
+
+
+def bench_copy(args):
+    """A plain elementwise copy of a known size (1 GiB read + 1 GiB written per
+    launch): the calibration that turns FETCH_SIZE / WRITE_SIZE into bytes."""
+    n = 1 << 28
+    torch.cuda.set_device(0)
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(args.warmup):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        torch.neg(a, out=b)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    out = {"metric": "plain copy GB/s (read + write), counter calibration", "value": 2 * 4 * n / (ms / 1e3) / 1e9,
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "elementwise copy 1 GiB -> 1 GiB", "bytes_read": 4 * n, "bytes_written": 4 * n}}
+    print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", choices=["decode", "prefill", "ring", "copy"], default="decode")
+    ap.add_argument("--instrument-steps", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--pinned-gib", type=float, default=56.0, help="ring workload: page-locked vault budget")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
+              "MI355X (no multi-GPU path exists in this build)", file=sys.stderr)
+        sys.exit(2)
+    defaults = {"decode": (64, 8), "prefill": (3, 1), "ring": (256, 8), "copy": (10, 2)}[args.workload]
+    args.steps = defaults[0] if args.steps is None else args.steps
+    args.warmup = defaults[1] if args.warmup is None else args.warmup
+    {"decode": bench_decode, "prefill": bench_prefill, "ring": bench_ring, "copy": bench_copy}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -139,7 +139,8 @@ int smoe_moe_decode_slots(const smoe_dims* dims, const uint16_t* x, const float*
 /* n_layers chained decode layers for one token, all experts resident
  * ("What Happens at Each Generated Token Step"): for L = 0..n_layers-1,
  * smoe_route then smoe_moe_decode with layer L's weights, the residual carried
- * from layer to layer.  Three kernels per layer, no host synchronisation.
+ * from layer to layer.  Four kernels per layer (router logits, top-k, gate/up,
+ * down + combine), no host synchronisation; capturable into a HIP graph.
  *   residual       device fp32 [d_model], updated in place
  *   w_router       device bf16 [n_layers][E][d_model]
  *   bias           device fp32 [n_layers][E] or NULL
@@ -148,10 +149,11 @@ int smoe_moe_decode_slots(const smoe_dims* dims, const uint16_t* x, const float*
  *   idx_rec        device int32 [n_layers][k] or NULL: routing per layer
  *   w_rec          device fp32 [n_layers][k] or NULL: weights per layer
  *   events         host array [n_layers][2] of hipEvent_t, or NULL: when
- *                  given, the gate/up kernel of layer L is launched with
- *                  hipExtLaunchKernel recording events[2L] at its start and
- *                  events[2L+1] at its end (per-kernel timing, in the spirit
- *                  of the pages' --instrument panel) */
+ *                  given, layer L's gate/up kernel is launched with
+ *                  hipExtLaunchKernel, which records events[2L] at the
+ *                  kernel's start and events[2L+1] at its end (per-kernel
+ *                  timing, in the spirit of the pages' instrument panel; not
+ *                  for use under stream capture) */
 int smoe_decode_layers(const smoe_dims* dims, int32_t n_layers, float* residual,
                        const uint16_t* w_router, const float* bias,
                        const void* const* expert_tables, uint16_t* x_rec, int32_t* idx_rec,
@@ -185,7 +187,9 @@ int smoe_moe_prefill_chunk(const smoe_dims* dims, int32_t n_tok, const uint16_t*
  * least-recently-used and never touches a slot held by the current layer.
  * Every request (hit or load) stamps the slot with a fresh tick.  Empty slots
  * are used first, lowest index first.  Misses are copied with hipMemcpyAsync
- * on copy_stream; the compute stream waits on their completion events.
+ * on copy_stream, after all work already enqueued on the compute stream (so
+ * no slot is overwritten while a kernel may still read it); the compute
+ * stream then waits on the completion events of the slots it is handed.
  * ------------------------------------------------------------------------- */
 typedef struct smoe_ring smoe_ring;
 
@@ -196,8 +200,13 @@ typedef struct {
   int32_t top_k;          /* k                                             */
   size_t slot_bytes;      /* bytes copied per fill (the blob size)         */
   size_t slot_stride;     /* distance between slots in slab_dev (>= bytes) */
-  const void* vault_host; /* host: blob (L, e) at vault_host + (L*E+e)*vault_stride;
-                             pinned (hipHostMalloc) for asynchronous copies */
+  const void* const* vault_layers; /* host array [n_layers] of host pointers:
+                             blob (L, e) at vault_layers[L] + e*vault_stride.
+                             Pinned (hipHostMalloc) memory gives asynchronous
+                             full-rate copies; one allocation per layer keeps
+                             each under the driver's pinned-allocation limit.
+                             The array is copied at create; the memory it
+                             points to must outlive the ring. */
   size_t vault_stride;
   void* slab_dev;         /* device: n_slots * slot_stride bytes            */
   void* copy_stream;      /* hipStream_t used for fills                     */
@@ -217,11 +226,11 @@ typedef struct {
 int smoe_ring_create(const smoe_ring_desc* desc, smoe_ring** out);
 
 /* Acquire the k experts of `layer` (host array, rank order).  Drops the
- * previous acquisition's holds first (an implicit release), so the caller must
- * have synchronised with every kernel that read the previously acquired slots
- * -- the per-layer routing round trip does this.  On return slot_ptrs_host[r]
- * is the device blob pointer for rank r, and compute_stream will not run
- * later work until the fills are complete. */
+ * previous acquisition's holds first (an implicit release).  On return
+ * slot_ptrs_host[r] is the device blob pointer for rank r, and compute_stream
+ * will not run later work until the fills are complete.  Errors: SMOE_EINVAL
+ * (layer, k or an expert out of range, an expert twice), SMOE_ENOSLOT (every
+ * slot held), SMOE_EHIP (a copy or event call failed). */
 int smoe_ring_acquire(smoe_ring* ring, int32_t layer, const int32_t* experts_host, int32_t k,
                       const void** slot_ptrs_host, void* compute_stream);
 

@@ -4,4 +4,4 @@ expert ring.  The computation lives in the HIP library libsmoe.so; this package
 only binds it (see include/smoe.h for the C ABI)."""
 from .binding import (SmoeError, Ring, blob_bytes, blob_stride, workspace_bytes, workspace, route,
                       moe_decode, moe_decode_slots, decode_layers, moe_prefill_chunk, lib, dims_struct,
-                      EXPORTED, LIB_PATH)
+                      PinnedHost, EXPORTED, LIB_PATH)

@@ -39,7 +39,7 @@ class SmoeDims(ctypes.Structure):
 class SmoeRingDesc(ctypes.Structure):
     _fields_ = [("n_slots", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("slot_bytes", ctypes.c_size_t), ("slot_stride", ctypes.c_size_t),
-                ("vault_host", ctypes.c_void_p), ("vault_stride", ctypes.c_size_t),
+                ("vault_layers", ctypes.POINTER(ctypes.c_void_p)), ("vault_stride", ctypes.c_size_t),
                 ("slab_dev", ctypes.c_void_p), ("copy_stream", ctypes.c_void_p),
                 ("log_capacity", ctypes.c_size_t)]
 
@@ -177,10 +177,13 @@ def moe_prefill_chunk(dims, x, topk_idx, topk_w, expert_table, residual, union_i
 class Ring:
     """Host handle of an expert ring (see smoe.h)."""
 
-    def __init__(self, n_slots, n_layers, n_experts, top_k, slot_bytes, slot_stride, vault_host_ptr,
+    def __init__(self, n_slots, n_layers, n_experts, top_k, slot_bytes, slot_stride, vault_layer_ptrs,
                  vault_stride, slab_dev_ptr, copy_stream, log_capacity=0):
+        """vault_layer_ptrs: n_layers host addresses, the base of each layer's blobs."""
+        assert len(vault_layer_ptrs) == int(n_layers)
+        table = (ctypes.c_void_p * int(n_layers))(*[int(p) for p in vault_layer_ptrs])
         desc = SmoeRingDesc(int(n_slots), int(n_layers), int(n_experts), int(top_k), int(slot_bytes),
-                            int(slot_stride), int(vault_host_ptr), int(vault_stride), int(slab_dev_ptr),
+                            int(slot_stride), table, int(vault_stride), int(slab_dev_ptr),
                             _stream(copy_stream), int(log_capacity))
         h = ctypes.c_void_p(0)
         _check(lib().smoe_ring_create(ctypes.byref(desc), ctypes.byref(h)))
@@ -213,3 +216,28 @@ class Ring:
         if self.h:
             _check(lib().smoe_ring_destroy(self.h))
             self.h = None
+
+
+class PinnedHost:
+    """Page-locked host memory from hipHostMalloc (for the ring's vault: fills
+    then run as DMA at full PCIe rate).  ``tensor()`` is a CPU uint8 view."""
+
+    def __init__(self, nbytes):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        self._hip.hipHostFree.argtypes = [ctypes.c_void_p]
+        p = ctypes.c_void_p(0)
+        rc = self._hip.hipHostMalloc(ctypes.byref(p), ctypes.c_size_t(int(nbytes)), 0)
+        if rc != 0 or not p.value:
+            raise SmoeError(SMOE_ENOMEM, f"hipHostMalloc of {int(nbytes)} bytes failed (hipError {rc})")
+        self.ptr = int(p.value)
+        self.nbytes = int(nbytes)
+
+    def tensor(self):
+        buf = (ctypes.c_uint8 * self.nbytes).from_address(self.ptr)
+        return torch.frombuffer(buf, dtype=torch.uint8)
+
+    def free(self):
+        if self.ptr:
+            self._hip.hipHostFree(ctypes.c_void_p(self.ptr))
+            self.ptr = 0

@@ -36,6 +36,7 @@ struct smoe_ring {
   std::vector<hipEvent_t> fill_done;  // per slot, recorded after its latest fill
   std::vector<int> where;          // (layer * E + expert) -> slot, or -1
   std::vector<int> held;           // slots of the current acquisition
+  std::vector<const char*> vault;  // per layer: host base of its blobs
   hipEvent_t compute_mark;
   unsigned long long now = 0;
   int n_filled = 0;                // empty slots are exactly [n_filled, n_slots)
@@ -61,12 +62,17 @@ int smoe_ring_create(const smoe_ring_desc* d, smoe_ring** out) {
                 d->n_slots);
   if (d->slot_bytes == 0 || d->slot_stride < d->slot_bytes || d->slot_stride % 16)
     return fail(SMOE_EINVAL, "slot_bytes/slot_stride invalid (stride must be >= bytes, multiple of 16)");
-  if (!d->vault_host || d->vault_stride < d->slot_bytes || !d->slab_dev)
-    return fail(SMOE_EINVAL, "vault_host / vault_stride / slab_dev invalid");
+  if (!d->vault_layers || d->vault_stride < d->slot_bytes || !d->slab_dev)
+    return fail(SMOE_EINVAL, "vault_layers / vault_stride / slab_dev invalid");
+  for (int L = 0; L < d->n_layers; ++L)
+    if (!d->vault_layers[L]) return fail(SMOE_EINVAL, "vault_layers[%d] is NULL", L);
   if (((uintptr_t)d->slab_dev & 15u) != 0) return fail(SMOE_EINVAL, "slab_dev must be 16-byte aligned");
   smoe_ring* r = new (std::nothrow) smoe_ring();
   if (!r) return fail(SMOE_ENOMEM, "host allocation failed");
   r->desc = *d;
+  r->desc.vault_layers = nullptr;  // the caller's array need not outlive create
+  r->vault.resize((size_t)d->n_layers);
+  for (int L = 0; L < d->n_layers; ++L) r->vault[L] = (const char*)d->vault_layers[L];
   const size_t n = (size_t)d->n_slots;
   r->key.assign(n, -1);
   r->tick.assign(n, 0);
@@ -145,7 +151,7 @@ int smoe_ring_acquire(smoe_ring* r, int32_t layer, const int32_t* experts, int32
       }
       r->key[s] = kk;
       r->where[kk] = s;
-      const char* src = (const char*)d.vault_host + (size_t)kk * d.vault_stride;
+      const char* src = r->vault[layer] + (size_t)experts[rank] * d.vault_stride;
       char* dst = (char*)d.slab_dev + (size_t)s * d.slot_stride;
       he = hipMemcpyAsync(dst, src, d.slot_bytes, hipMemcpyHostToDevice, ps);
       if (he == hipSuccess) he = hipEventRecord(r->fill_done[s], ps);

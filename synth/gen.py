@@ -285,13 +285,15 @@ def zipf_bias(seed: int, dims: Dims, layer: int, s: float = 1.1) -> np.ndarray:
     return (-s * np.log(rank)).astype(np.float32)
 
 
-def markov_hidden(seed: int, n_steps: int, n: int, keep: float = 0.7, fresh: float = 0.3) -> np.ndarray:
+def markov_hidden(seed: int, n_steps: int, n: int, keep: float = 0.7, fresh: float = 0.3,
+                  lane: int = 0) -> np.ndarray:
     """Hidden states h_t = keep * h_{t-1} + fresh * z_t, h_0 = z_0 (float64
-    recursion, rounded to float32 at the end).  Shape [n_steps][n]."""
+    recursion, rounded to float32 at the end).  Shape [n_steps][n].  ``lane``
+    selects an independent chain (e.g. one per layer)."""
     out = np.empty((n_steps, n), dtype=np.float32)
     h = None
     for t in range(n_steps):
-        z = normal_vector(seed, t, n, sub=1)
+        z = normal_vector(seed, t, n, sub=1 + lane)
         h = z if h is None else keep * h + fresh * z
         out[t] = h.astype(np.float32)
     return out

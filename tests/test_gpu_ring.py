@@ -8,7 +8,7 @@ import torch
 import oracle
 import quantised_routed_expert_amd as smoe
 import synth
-from synth.device import DeviceStack
+from synth.device import DeviceStack, router_stack, u16_to_device
 from tests.gpu_common import need_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -26,8 +26,10 @@ def make_ring(dims, stack, n_slots, log_capacity=1 << 20):
     host.copy_(stack.vault)
     slab = torch.empty(n_slots * stride, dtype=torch.uint8, device="cuda")
     copy_stream = torch.cuda.Stream()
+    per_layer = dims.n_experts * stride
     ring = smoe.Ring(n_slots, stack.n_layers, dims.n_experts, dims.top_k, stack.blob_bytes, stride,
-                     host.data_ptr(), stride, slab.data_ptr(), copy_stream, log_capacity)
+                     [host.data_ptr() + L * per_layer for L in range(stack.n_layers)], stride, slab.data_ptr(),
+                     copy_stream, log_capacity)
     return ring, (host, slab, copy_stream)
 
 
@@ -118,3 +120,61 @@ def test_ring_argument_errors():
     ring.release()
     torch.cuda.synchronize()
     ring.destroy()
+
+
+def test_ring_lru_at_full_scale_with_markov_routing():
+    """The ring at the 235B ring workload's scale: 94 layers x 128 experts,
+    top-8, 1536 slots, every layer's router input its own Markov chain over
+    tokens (0.7 previous + 0.3 fresh), routing done on the GPU at d_model 4096.
+    The hit/miss/eviction log must equal the oracle's LRU simulation, and every
+    slot must end up holding its key's vault bytes.  The slots carry 4 KiB
+    stand-in blobs: the policy and the copies do not depend on blob size."""
+    dims = synth.Dims(4096, 1536, 128, 8, 64)
+    NL, T, n_slots, E, k = 94, 48, 1536, 128, 8
+    blob = 4096
+    routers = u16_to_device(router_stack(1337, dims, NL))
+    vault = torch.empty((NL, E, blob), dtype=torch.uint8, pin_memory=True)
+    vault.copy_(torch.from_numpy(np.random.default_rng(5).integers(0, 256, (NL, E, blob), dtype=np.uint8)))
+    slab = torch.full((n_slots, blob), 0, dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    ring = smoe.Ring(n_slots, NL, E, k, blob, blob, [vault[L].data_ptr() for L in range(NL)], blob,
+                     slab.data_ptr(), copy_stream, NL * T * k)
+    hidden = torch.from_numpy(np.stack([synth.markov_hidden(1337, T, dims.d_model, lane=L)
+                                        for L in range(NL)])).cuda()
+    ws = smoe.workspace(dims, 1)
+    x = torch.empty((1, dims.d_model), dtype=torch.int16, device="cuda")
+    idx = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    routing, repeats = [], []
+    for t in range(T):
+        layers = []
+        for L in range(NL):
+            smoe.route(dims, hidden[L, t:t + 1], x, routers[L], None, idx, w, ws)
+            experts = idx.cpu().numpy()[0].tolist()
+            layers.append(experts)
+            if t:
+                repeats.append(len(set(experts) & set(routing[-1][L])) / k)
+            ring.acquire(L, experts)
+        routing.append(layers)
+    ring.release()
+    torch.cuda.synchronize()
+    log = ring.log(NL * T * k)
+    stats = ring.stats()
+    ring.destroy()
+    ref_events, (h, m, ev) = oracle.ring_trace(routing, n_slots)
+    assert [e[1:] for e in ref_events] == log
+    assert (stats["hits"], stats["misses"], stats["evictions"]) == (h, m, ev)
+    say(f"[ring-full] hits {h} misses {m} evictions {ev}, repeat {np.mean(repeats):.3f}")
+    assert ev > 0                      # the workload overflows the ring
+    holder = {}
+    for (_, L, _, e, kind, slot, _) in ref_events:
+        if kind == 1:
+            holder[slot] = (L, e)
+    got = slab.cpu()
+    for slot, (L, e) in holder.items():
+        assert torch.equal(got[slot], vault[L, e]), (slot, L, e)
+    # a sample of the GPU routing against the oracle
+    for t, L in ((0, 0), (T - 1, NL - 1), (T // 2, 40)):
+        xv, _ = oracle.rmsnorm_bf16(hidden[L, t].cpu().numpy().astype(np.float64), dims.rms_eps)
+        ref_idx, _ = oracle.select_topk(oracle.router_logits(synth.router_bits(1337, dims, L), xv), k)
+        assert routing[t][L] == ref_idx

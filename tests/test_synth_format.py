@@ -93,6 +93,10 @@ def test_markov_recursion():
     z1 = synth.normal_vector(1337, 1, 64, sub=1)
     assert np.allclose(h[0], z0, rtol=1e-6)
     assert np.allclose(h[1], 0.7 * z0 + 0.3 * z1, rtol=1e-5, atol=1e-6)
+    # lanes are independent chains
+    h5 = synth.markov_hidden(1337, 2, 64, lane=5)
+    assert np.allclose(h5[0], synth.normal_vector(1337, 0, 64, sub=6), rtol=1e-6)
+    assert not np.allclose(h5[0], h[0])
 
 
 def test_golden_tiny_decode_reproduces():
