@@ -4,16 +4,17 @@
  * The library computes one routed Mixture-of-Experts FFN layer of an S-MoE
  * style engine, as the S-MoE documentation pages describe it:
  *   - the exact router: RMSNorm of the residual, an E x d_model bf16 gate
- *     matvec on that true hidden state, top-k selection and norm_topk_prob
- *     mixing weights as Qwen3 defines them ("Optimizations", section
- *     "Routing Is Exact"; "System Overview", per-token step table);
+ *     matvec on the actual (not predicted) hidden state, top-k selection and
+ *     Qwen3's norm_topk_prob weighting ("Optimizations", section "Routing Is
+ *     Exact"; "System Overview", per-token step table);
  *   - the fused SMOE-Q4 expert FFN: per-chunk affine dequant, gate and up in
  *     one pass, SwiGLU, down projection, and the gate-weighted sum of the
  *     experts' outputs into the residual ("Optimizations", section "Coalesced
  *     GPU Kernels"; "System Overview", step table, Metal-kernel row);
- *   - layer-major prefill of chunks of up to 64 tokens whose routed experts are
- *     deduplicated into a union read once per chunk ("Optimizations", section
- *     "Prefill Reads Each Expert Once");
+ *   - layer-major prefill: a chunk holds at most 64 tokens, and the set of
+ *     distinct experts its tokens route to is streamed once per chunk rather
+ *     than once per token ("Optimizations", section "Prefill Reads Each Expert
+ *     Once");
  *   - an LRU ring of expert slots in HBM, refilled from a vault in host memory
  *     ("Optimizations", section "The Ring Is an LRU Cache"; "System Overview",
  *     memory-budget paragraph on the [64, 4096] slot clamp).

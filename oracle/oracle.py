@@ -14,8 +14,8 @@ Overview" (docs.s-moe.com, v1) and the S-MoE diary feed.
 * RMSNorm of the residual into the bf16 router / expert input -- the per-layer
   norm that "The Dense Ceiling -- GPU-Resident Epilogue" (Optimizations) moves
   next to the router gate.  Gain 1, eps 1e-6 (reading: the pages give neither).
-* Exact router: a E x d_model gate matvec on the true hidden state, then
-  top-k selection and norm_topk_prob mixing weights "as Qwen3 defines them"
+* Exact router: an E x d_model gate matvec on the actual hidden state (no
+  predictor), then top-k selection and Qwen3's norm_topk_prob weighting
   (Optimizations, "Routing Is Exact"; System Overview, per-token step table).
   Qwen3's definition: softmax over all E logits, keep the k largest, and when
   norm_topk_prob is set divide the kept probabilities by their sum.
@@ -23,10 +23,10 @@ Overview" (docs.s-moe.com, v1) and the S-MoE diary feed.
   input, SwiGLU, down projection, and the gate-weighted sum of the k expert
   outputs added into the residual (Optimizations, "Coalesced GPU Kernels";
   System Overview, step table, "Metal Kernel" row).
-* Layer-major prefill: the chunk's routed experts deduplicated into a union
-  read once (Optimizations, "Prefill Reads Each Expert Once"); the union is
-  listed in first-touch order because each expert is fired "the moment the
-  first token routes to it" (same section).
+* Layer-major prefill: the distinct experts of a chunk form a union that is
+  streamed once (Optimizations, "Prefill Reads Each Expert Once"); the union
+  is listed in first-touch order because that section has each expert
+  dispatched as soon as some token of the chunk first selects it.
 * The LRU expert ring: hit = same (layer, expert) already resident, zero bytes
   read; lazy least-recently-used eviction that never evicts a slot the current
   layer holds (Optimizations, "The Ring Is an LRU Cache").
@@ -243,8 +243,9 @@ class LruRing:
       * otherwise MISS: the lowest-index empty slot, else the unpinned
         occupied slot with the smallest tick (evicted), is loaded: key set,
         tick := now, pinned.
-    Reading of "stamps fresh ticks on new loads" together with "least recently
-    used": every request, hit or load, stamps the slot (true LRU).  Slots are
+    Reading: the section says new loads get a fresh tick and also calls the
+    policy least-recently-used; here every request, hit or load, stamps the
+    slot (true LRU).  Slots are
     never wiped; retention spans tokens."""
 
     def __init__(self, n_slots: int):

@@ -1,4 +1,4 @@
-// Prefill (layer-major, one chunk of up to 64 tokens) argument block (internal).
+// Prefill (layer-major, one chunk of at most 64 tokens) argument block (internal).
 #pragma once
 
 #include "kernels.h"

@@ -1,6 +1,6 @@
-// Layer-major batched prefill of one chunk of up to 64 tokens through one MoE
+// Layer-major batched prefill of one chunk (at most 64 tokens) through one MoE
 // layer ("Prefill Reads Each Expert Once, Not Once Per Token", Optimizations
-// page): the chunk's routed experts are deduplicated into a union, each union
+// page): the distinct experts the chunk routes to form its union, each union
 // expert's blob is streamed once, and its tokens are processed together.
 //
 // Kernels (one launch each, in stream order):

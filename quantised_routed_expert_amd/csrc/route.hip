@@ -1,9 +1,9 @@
 // Exact router: RMSNorm -> bf16 x, float64 gate matvec, top-k, mixing weights.
 //
 // "Routing Is Exact" (Optimizations page) and the per-token step table of the
-// System Overview page: every MoE layer evaluates the real E x d_model router
-// gate on the true hidden state, then top-k and norm_topk_prob weights as
-// Qwen3 defines them (softmax over all E, keep the k largest, renormalise).
+// System Overview page: each MoE layer runs its own E x d_model router gate on
+// the actual hidden state (no predictor), then selects the top k with Qwen3's
+// weighting (softmax over all E, keep the k largest, renormalise).
 // The pages run this gate on the CPU; here the norm and the gate run on the
 // GPU, as the pages' own "GPU-Resident Epilogue" plan (Optimizations, "The
 // Dense Ceiling") proposes.
