@@ -140,8 +140,9 @@ int smoe_moe_decode_slots(const smoe_dims* dims, const uint16_t* x, const float*
 /* n_layers chained decode layers for one token, all experts resident
  * ("What Happens at Each Generated Token Step"): for L = 0..n_layers-1,
  * smoe_route then smoe_moe_decode with layer L's weights, the residual carried
- * from layer to layer.  Four kernels per layer (router logits, top-k, gate/up,
- * down + combine), no host synchronisation; capturable into a HIP graph.
+ * from layer to layer.  Three kernels per layer (router logits; top-k +
+ * gate/up + SwiGLU; down + combine), no host synchronisation; capturable into
+ * a HIP graph.  Results are bitwise equal to the per-layer calls.
  *   residual       device fp32 [d_model], updated in place
  *   w_router       device bf16 [n_layers][E][d_model]
  *   bias           device fp32 [n_layers][E] or NULL

@@ -228,25 +228,20 @@ int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, co
                        logits, 1, d->d_model, d->n_experts, d->rms_eps};
     hipError_t he = launch_route_logits(ra, s);
     if (he != hipSuccess) return hip_fail(he, "route_logits launch");
-    TopkArgs ta;
-    memset(&ta, 0, sizeof(ta));
-    ta.logits = logits;
-    ta.idx = reinterpret_cast<int32_t*>(base + L.idx);
-    ta.w = reinterpret_cast<float*>(base + L.w);
-    ta.table = expert_tables + (size_t)layer * E;
-    ta.ptr_out = reinterpret_cast<const void**>(base + L.ptr);
-    ta.idx_rec = idx_rec ? idx_rec + (size_t)layer * K : nullptr;
-    ta.w_rec = w_rec ? w_rec + (size_t)layer * K : nullptr;
-    ta.E = d->n_experts;
-    ta.k = d->top_k;
-    ta.norm = d->norm_topk_prob ? 1 : 0;
-    he = launch_route_topk(ta, 1, s);
-    if (he != hipSuccess) return hip_fail(he, "route_topk launch");
+    // the top-k selection runs inside the gate/up kernel, which publishes ids,
+    // weights and blob pointers for the down kernel
     DecodeArgs a = decode_args(d, base, L);
     a.x = xl;
     a.px = px;
-    a.ptrs = ta.ptr_out;
-    a.w = ta.w;
+    a.src.table = expert_tables + (size_t)layer * E;
+    a.sel.logits = logits;
+    a.sel.idx_out = reinterpret_cast<int32_t*>(base + L.idx);
+    a.sel.w_out = reinterpret_cast<float*>(base + L.w);
+    a.sel.ptr_out = reinterpret_cast<const void**>(base + L.ptr);
+    a.sel.idx_rec = idx_rec ? idx_rec + (size_t)layer * K : nullptr;
+    a.sel.w_rec = w_rec ? w_rec + (size_t)layer * K : nullptr;
+    a.ptrs = a.sel.ptr_out;
+    a.w = a.sel.w_out;
     a.residual = residual;
     if (layer + 1 < n_layers) a.pf_base = reinterpret_cast<const uint8_t*>(w_router + (size_t)(layer + 1) * E * D);
     he = events ? launch_decode_gate_up(a, s, (hipEvent_t)events[2 * layer], (hipEvent_t)events[2 * layer + 1])

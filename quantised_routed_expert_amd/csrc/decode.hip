@@ -104,41 +104,13 @@ __device__ __forceinline__ const void* expert_pointer(const DecodeArgs& a, int r
   return (e >= 0 && e < a.E) ? a.src.table[e] : nullptr;
 }
 
-// ---------------------------------------------------------------------------
-// Gate + up + SwiGLU.  One wave owns NP * (64 / LR) consecutive rows of the
-// flattened (rank, row) space, all inside one expert; LR lanes share a row.
-// Every load of the wave's rows is issued before
-// any is consumed.  grid = ceil(k * d_ff / (4 * rows per wave)), 256 threads.
-// ---------------------------------------------------------------------------
+// The NP * (64 / LR) rows of one wave (all in expert r, starting at row
+// n_begin): every weight load is issued before any is consumed.
 template <int LR, int NSEG, int NP, int CHUNK>
-__global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a) {
+__device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t* blob, int r, int n_begin, int li,
+                                             int grp, const uint4 (*xraw)[4]) {
   using Run = LaneRun<NSEG, CHUNK>;
-  constexpr int P = kWave / LR;  // rows per pass
-  constexpr int RPW = NP * P;    // rows per wave
-  __shared__ const void* s_ptr[kMaxTopK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane % LR, grp = lane / LR;
-
-  if (tid < a.k) s_ptr[tid] = expert_pointer(a, tid);
-  uint4 xraw[NSEG][4];
-  if (a.px) load_raw<NSEG>(a.px + li * (NSEG * 32), xraw);
-  else load_raw<NSEG>(a.x + li * (NSEG * 32), xraw);
-  __syncthreads();
-
-  const int gw = blockIdx.x * 4 + wave;
-  const int row0 = gw * RPW;
-  if (row0 >= a.k * a.f) return;
-  const int r = row0 / a.f;
-  const int n_begin = row0 - r * a.f;
-  const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
-  if (!blob) {  // an index outside [0, E): the rank contributes nothing
-    for (int it = lane; it < RPW; it += kWave) {
-      const int n = n_begin + it;
-      a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)0.0f;
-    }
-    return;
-  }
-
+  constexpr int P = kWave / LR;
   const size_t row_bytes = (size_t)a.d / 2;
   const size_t prow_bytes = (size_t)(a.d / CHUNK) * 4;
   const size_t first = (size_t)(n_begin + grp);
@@ -189,6 +161,78 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Gate + up + SwiGLU.  One wave owns NP * (64 / LR) consecutive rows of the
+// flattened (rank, row) space, all inside one expert; LR lanes share a row.
+// With a.sel.logits set, the workgroup first selects the top k itself from the
+// layer's logits (every workgroup reaches the same, deterministic selection)
+// and finds the blobs in src.table; workgroup 0 also publishes ids, weights and
+// pointers.  grid = ceil(k * d_ff / (4 * rows per wave)) workgroups of 4 waves.
+// ---------------------------------------------------------------------------
+template <int LR, int NSEG, int NP, int CHUNK>
+__global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a) {
+  constexpr int P = kWave / LR;  // rows per pass
+  constexpr int RPW = NP * P;    // rows per wave
+  __shared__ const void* s_ptr[kMaxTopK];
+  __shared__ TopkShared tk;
+  __shared__ const void* s_tab[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane % LR, grp = lane / LR;
+
+  const bool fused = a.sel.logits != nullptr;
+  double lv = 0.0;
+  const void* tv = nullptr;
+  if (fused) {
+    if (tid < a.E) {  // the layer's logits and blob table
+      lv = a.sel.logits[tid];
+      tv = a.src.table[tid];
+    }
+  } else if (tid < a.k) {
+    s_ptr[tid] = expert_pointer(a, tid);
+  }
+  uint4 xraw[NSEG][4];
+  if (a.px) load_raw<NSEG>(a.px + li * (NSEG * 32), xraw);
+  else load_raw<NSEG>(a.x + li * (NSEG * 32), xraw);
+  if (fused && tid < kMaxExperts) {  // stored after the input loads are issued
+    tk.log[tid] = tid < a.E ? lv : -__builtin_inf();
+    tk.logf[tid] = tid < a.E ? (float)lv : -__builtin_inff();
+    if (tid < a.E) s_tab[tid] = tv;
+    if (tid < kMaxTopK) tk.idx[tid] = -1;
+  }
+  __syncthreads();
+  if (fused) topk_select_fast(tk, a.E, a.k, s_tab, s_ptr);
+
+  const int gw = blockIdx.x * (blockDim.x >> 6) + wave;
+  const int row0 = gw * RPW;
+  if (row0 < a.k * a.f) {
+    const int r = row0 / a.f;
+    const int n_begin = row0 - r * a.f;
+    const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
+    if (blob) {
+      gate_up_rows<LR, NSEG, NP, CHUNK>(a, blob, r, n_begin, li, grp, xraw);
+    } else {  // an index outside [0, E) or a null table entry: the rank contributes nothing
+      for (int it = lane; it < RPW; it += kWave) {
+        const int n = n_begin + it;
+        a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)0.0f;
+      }
+    }
+  }
+
+  // Workgroup 0 publishes the selection for the down kernel after its own rows
+  // (uniform branch: every wave of the workgroup reaches the barriers inside).
+  if (fused && blockIdx.x == 0) {
+    topk_weights(tk, a.E, a.k, a.norm);
+    if (tid < a.k) {
+      const int e = tk.idx[tid];
+      a.sel.idx_out[tid] = e;
+      a.sel.w_out[tid] = tk.w[tid];
+      a.sel.ptr_out[tid] = s_tab[e];
+      if (a.sel.idx_rec) a.sel.idx_rec[tid] = e;
+      if (a.sel.w_rec) a.sel.w_rec[tid] = tk.w[tid];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Down projection + weighted combine into the residual.  A workgroup owns
 // NPASS * (64 / LR) output rows; its wave w handles ranks w, w + nw, ... so
 // that each wave keeps one expert's h in registers; per-row partial results
@@ -207,30 +251,38 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
   if (tid < a.k) {
-    s_w[tid] = a.w[tid];
-    s_ptr[tid] = expert_pointer(a, tid);
+    // both loads in flight before either is stored
+    const float w = a.w[tid];
+    const void* p = expert_pointer(a, tid);
+    s_w[tid] = w;
+    s_ptr[tid] = p;
   }
   // Pull the next layer's router rows into cache while this kernel streams:
-  // the router workgroup w (rows [16w, 16w + 16)) runs on XCD w % 8, so the
-  // down workgroups of that XCD each fetch one slice of those rows.
-  uint2 pf = make_uint2(0, 0);
+  // the router workgroup w (rows [4w, 4w + 4)) runs on XCD w % 8, so the down
+  // workgroups of that XCD each fetch one slice of those rows.  Each thread
+  // takes at most kPrefetchPerThread 16-byte pieces (out-of-range pieces read
+  // the first 16 bytes instead, harmlessly); the loads are issued after the
+  // weight loads and their values are only folded at the very end.
+  constexpr int kPrefetchPerThread = 2;
+  const uint8_t* pf_addr[kPrefetchPerThread];
   if (a.pf_base) {
     const size_t row_bytes = (size_t)a.d * 2, blk = (size_t)kRouteRowsPerWG * row_bytes;
     const size_t total = (size_t)a.E * row_bytes;
     const int x = blockIdx.x % kXcds, q = blockIdx.x / kXcds, Q = (gridDim.x + kXcds - 1) / kXcds;
     const int rw = (a.E + kRouteRowsPerWG - 1) / kRouteRowsPerWG;
     const int cx = x < rw ? (rw - x + kXcds - 1) / kXcds : 0;
-    const size_t bx = (size_t)cx * blk, share = (bx + Q - 1) / Q;
+    const size_t bx = (size_t)cx * blk, share = ((bx + Q - 1) / Q + 15) & ~(size_t)15;
     const size_t lo = (size_t)q * share, hi = lo + share < bx ? lo + share : bx;
-    for (size_t o = lo + (size_t)tid * 8; o < hi; o += (size_t)blockDim.x * 8) {
+#pragma unroll
+    for (int i = 0; i < kPrefetchPerThread; ++i) {
+      const size_t o = lo + ((size_t)i * blockDim.x + tid) * 16;
       const size_t addr = (size_t)(x + kXcds * (int)(o / blk)) * blk + o % blk;
-      if (addr + 8 <= total) {
-        const uint2 v = *reinterpret_cast<const uint2*>(a.pf_base + addr);
-        pf.x ^= v.x;
-        pf.y ^= v.y;
-      }
+      pf_addr[i] = a.pf_base + ((o < hi && addr + 16 <= total) ? addr : 0);
     }
   }
+  uint4 pf[kPrefetchPerThread];
+#pragma unroll
+  for (int i = 0; i < kPrefetchPerThread; ++i) pf[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   const int li = lane % LR, grp = lane / LR;
@@ -238,7 +290,7 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   const size_t row_bytes = (size_t)a.f / 2;
   const size_t prow_bytes = (size_t)(a.f / CHUNK) * 4;
 
-  for (int r = wave; r < a.k; r += nw) {
+  for (int r = wave, it = 0; r < a.k; r += nw, ++it) {
     const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
     if (!blob) {
       for (int row = lane; row < ROWS; row += kWave) ylds[r][row] = 0.f;
@@ -248,20 +300,20 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     const uint8_t* par = blob + a.lay.down_params;
     uint4 hraw[NSEG][4];
     load_raw<NSEG>(a.h + (size_t)r * a.f + li * (NSEG * 32), hraw);
+    __builtin_amdgcn_sched_barrier(0);  // h first: the math can start when it lands
     uint4 c[NPASS][NSEG];
     uint32_t pr[NPASS][Run::NPL];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      const int n = n0 + p * P + grp;
-      const bool ok = n < a.d;
+      const int n = n0 + p * P + grp;  // < d: the launcher checks d % ROWS == 0
 #pragma unroll
-      for (int s = 0; s < NSEG; ++s)
-        c[p][s] = ok ? gload16(codes + (size_t)n * row_bytes + s * 16)
-                     : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+      for (int s = 0; s < NSEG; ++s) c[p][s] = gload16(codes + (size_t)n * row_bytes + s * 16);
 #pragma unroll
-      for (int j = 0; j < Run::NPL; ++j)
-        pr[p][j] = ok ? gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, j) * 4)
-                      : 0u;
+      for (int j = 0; j < Run::NPL; ++j) pr[p][j] = gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, j) * 4);
+    }
+    if (it == 0 && a.pf_base) {
+#pragma unroll
+      for (int i = 0; i < kPrefetchPerThread; ++i) pf[i] = gload16(pf_addr[i]);
     }
     __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
     // h_r for this lane's columns (already pair-ordered) and its segment sums
@@ -281,12 +333,14 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   __syncthreads();
   for (int row = tid; row < ROWS; row += blockDim.x) {
     const int n = n0 + row;
-    if (n >= a.d) break;
     float acc = 0.f;
     for (int r = 0; r < a.k; ++r) acc = fmaf(s_w[r], ylds[r][row], acc);
     a.residual[n] += acc;
   }
-  asm volatile("" ::"v"(pf.x), "v"(pf.y));  // keeps the prefetch loads alive
+  // keeps the prefetch loads alive (all four words, so that no register of a
+  // pending load is reused early, which would force a wait for it)
+#pragma unroll
+  for (int i = 0; i < kPrefetchPerThread; ++i) asm volatile("" ::"v"(pf[i].x), "v"(pf[i].y), "v"(pf[i].z), "v"(pf[i].w));
 }
 
 // ---------------------------------------------------------------------------
@@ -346,13 +400,16 @@ hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t 
   const int total = a.k * a.f;
   const int np = gate_up_np(sp.lr, total, a.f);
   const int waves = total / (np * (64 / sp.lr));
-  const dim3 grid((waves + 3) / 4);
+  // 4 waves per workgroup (measured: 12-wave workgroups, one per CU, spend
+  // longer in the shared selection than they save); launch bounds match
+  constexpr int nw = 4;
+  const dim3 grid((waves + nw - 1) / nw);
   SMOE_CHUNK_SWITCH(a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
       if (start || stop) {
-        hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(256), 0, s, start, stop,
-                              0, a);
+        hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(64 * nw), 0, s, start,
+                              stop, 0, a);
       } else {
-        hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(64 * nw), 0, s, a);
       }))));
   return hipGetLastError();
 }
@@ -363,8 +420,9 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   int np = 1;
   while (np * 2 <= SMOE_DN_PASSES_MAX && a.d / (P * np * 2) >= SMOE_DN_MIN_WG) np *= 2;
   const int rows = np * P;
+  if (a.d % rows) return hipErrorInvalidValue;  // every workgroup owns full rows
   const int nw = a.k < 8 ? a.k : 8;
-  const dim3 grid((a.d + rows - 1) / rows);
+  const dim3 grid(a.d / rows);
   SMOE_CHUNK_SWITCH(a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NPASS,
       hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK>), grid, dim3(64 * nw), 0, s, a)))));
   return hipGetLastError();

@@ -20,6 +20,7 @@ constexpr int kTopkMaxSlices = 8;
 
 struct TopkShared {
   double log[kMaxExperts];
+  float logf[kMaxExperts];  // the logits rounded to float (topk_select_fast)
   int part[kTopkMaxSlices][kMaxExperts];
   int idx[kMaxTopK];
   double val[kMaxTopK];
@@ -27,7 +28,8 @@ struct TopkShared {
   float w[kMaxTopK];
 };
 
-__device__ inline void topk_block(TopkShared& s, int E, int k, int norm) {
+// Selection only: s.idx / s.val in rank order (ends with a barrier).
+__device__ inline void topk_select(TopkShared& s, int E, int k) {
   const int t = threadIdx.x, nt = blockDim.x;
   const int ep = E <= 128 ? 128 : 256;  // experts per slice row
   int slices = nt / ep;
@@ -55,6 +57,74 @@ __device__ inline void topk_block(TopkShared& s, int E, int k, int norm) {
     }
   }
   __syncthreads();
+}
+
+// The same selection, fast path, for a workgroup of NW >= ceil(E / 64) waves.
+// Experts are split into G = ceil(E / 64) groups of 64 (one per lane) and the
+// logits into S = NW / G slices (multiples of 16); wave w takes group w % G
+// and slice w / G and counts, per expert i, c_i = #{j : f_j >= f_i} over its
+// slice, where f = the logits rounded to float (monotone, so f_j > f_i implies
+// l_j > l_i and f_j < f_i implies l_j < l_i).  Slices are read from LDS at
+// wave-uniform addresses (broadcast reads, 16 in flight).  Without float ties
+// touching the top k, rank_i = c_i - 1 exactly, and each expert of rank < k
+// writes its id, logit and table entry to its rank's slot.  Any tie that
+// touches the top k (float or exact) leaves some slot unclaimed, since every
+// member of a tied group claims the group's last rank; the workgroup then
+// falls back to the exact float64 rank counting of topk_select.
+// Before the call: s.log / s.logf hold the E logits followed by -inf up to
+// kMaxExperts, s.idx[0..k) = -1, and a barrier has made them visible.  `tab`
+// (E entries, may be null) is looked up into `slot_ptr` (k entries, shared
+// memory).  Ends with a barrier.
+__device__ inline void topk_select_fast(TopkShared& s, int E, int k, const void* const* tab,
+                                        const void** slot_ptr) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int nw = blockDim.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int G = (E + 63) >> 6;
+  int S = nw / G < kTopkMaxSlices ? nw / G : kTopkMaxSlices;
+  int span = (((E + S - 1) / S) + 15) & ~15;
+  while (S > 1 && S * span > kMaxExperts) {
+    --S;
+    span = (((E + S - 1) / S) + 15) & ~15;
+  }
+  const int g = w % G, sl = w / G;
+  if (sl < S) {
+    const int i = 64 * g + lane;
+    const float x = i < E ? s.logf[i] : __builtin_inff();
+    const int j0 = sl * span;
+    int c = 0;
+    for (int j = j0; j < j0 + span; j += 16) {
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = s.logf[j + q];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) c += (v[q] >= x) ? 1 : 0;
+    }
+    s.part[sl][i] = c;
+  }
+  __syncthreads();
+  if (t < E) {
+    int c = 0;
+    for (int q = 0; q < S; ++q) c += s.part[q][t];
+    if (c - 1 < k) {
+      s.idx[c - 1] = t;
+      s.val[c - 1] = s.log[t];
+      if (tab) slot_ptr[c - 1] = tab[t];
+    }
+  }
+  __syncthreads();
+  bool ok = true;
+  for (int r = 0; r < k; ++r) ok &= s.idx[r] >= 0;
+  if (!ok) {  // uniform: every thread read the same slots
+    topk_select(s, E, k);
+    if (tab && t < k) slot_ptr[t] = tab[s.idx[t]];
+    __syncthreads();
+  }
+}
+
+// Mixing weights of the selected experts: s.w (ends with a barrier).
+__device__ inline void topk_weights(TopkShared& s, int E, int k, int norm) {
+  const int t = threadIdx.x;
   const double lmax = s.val[0];
   if (norm) {
     if (t < k) s.ex[t] = exp(s.val[t] - lmax);
@@ -70,6 +140,11 @@ __device__ inline void topk_block(TopkShared& s, int E, int k, int norm) {
     s.w[t] = (float)(num / den);
   }
   __syncthreads();
+}
+
+__device__ inline void topk_block(TopkShared& s, int E, int k, int norm) {
+  topk_select(s, E, k);
+  topk_weights(s, E, k, norm);
 }
 
 struct RouteArgs {
@@ -109,10 +184,24 @@ struct ExpertSource {
 constexpr int kRouteRowsPerWG = 4;
 constexpr int kXcds = 8;  // MI355X: workgroup i is dispatched to XCD i % 8
 
+// Selection inside the gate/up kernel: every workgroup ranks the layer's E
+// logits itself (the selection is deterministic, so all agree) and looks its
+// experts up in src.table; workgroup 0 publishes ids, weights and pointers for
+// the down kernel and the optional records.
+struct FusedTopk {
+  const double* logits;     // [E], or null: the experts come from src / ptrs
+  int32_t* idx_out;         // [k]
+  float* w_out;             // [k]
+  const void** ptr_out;     // [k]
+  int32_t* idx_rec;         // [k] or null
+  float* w_rec;             // [k] or null
+};
+
 struct DecodeArgs {
   const uint16_t* x;        // [d] bf16
   const _Float16* px;       // [d] x as f16 in pair order, or null (then x is converted)
   ExpertSource src;
+  FusedTopk sel;
   const float* w;           // [k] mixing weights (device), read by the down kernel
   const void* const* ptrs;   // [k] device blob pointers from the router, or null
   _Float16* h;              // [k][d_ff], pair-ordered within groups of 8

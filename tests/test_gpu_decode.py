@@ -218,3 +218,51 @@ def test_invalid_arguments_are_rejected():
             smoe.route(bad, r, x, wr, None, idx, w, ws)
     with pytest.raises(smoe.SmoeError):
         smoe.route(dims, r, x, wr, None, idx, w, ws[:16])
+
+
+@pytest.mark.parametrize("case", ["exact_tie", "float_tie", "tie_at_boundary"])
+def test_decode_layers_selection_with_ties_matches_oracle(case):
+    """The chained entry point selects inside the gate/up kernel with a float
+    fast path; ties (exact, or equal only after rounding to float) in the top k
+    must take the exact float64 path and agree with the oracle and with
+    smoe_route."""
+    dims = synth.Dims(256, 128, 128, 8, 32)
+    stack = DeviceStack(1337, dims, 1)
+    rng = np.random.default_rng({"exact_tie": 21, "float_tie": 22, "tie_at_boundary": 23}[case])
+    res = random_residual(rng, 1, dims.d_model)[0]
+    j_small = 17
+    res[j_small] = 1e-6 * np.abs(res).max()      # an input element too small to move a float logit
+    xv, _ = oracle.rmsnorm_bf16(res.astype(np.float64), dims.rms_eps)
+    wr = stack.router_bits[0].copy()
+    big = synth.bf16_bits_from_f64(0.03 * np.sign(xv) + 0.0)
+    if case == "exact_tie":
+        for e in (5, 9, 40):
+            wr[e] = big                          # three equal logits at the top
+    elif case == "float_tie":
+        wr[5] = big
+        wr[9] = big.copy()
+        wr[9][j_small] = np.uint16(int(wr[9][j_small]) + 1)  # one bf16 ulp on a tiny input
+    else:
+        # seven clear winners and a tie for the last place
+        for n, e in enumerate((2, 3, 4, 6, 7, 8, 10)):
+            wr[e] = synth.bf16_bits_from_f64((0.05 + 0.001 * n) * np.sign(xv))
+        wr[60] = wr[61] = big
+    stack.router_bits[0] = wr
+    stack.router[0].copy_(u16_to_device(wr))
+    lg = oracle.router_logits(wr, xv)
+    ref_idx, ref_w = oracle.select_topk(lg, dims.top_k, dims.norm_topk_prob)
+    if case == "float_tie":
+        assert lg[5] != lg[9] and np.float32(lg[5]) == np.float32(lg[9])
+    # chained entry point (selection inside gate/up)
+    r = torch.from_numpy(res.copy()).cuda()
+    i_rec = torch.empty((1, dims.top_k), dtype=torch.int32, device="cuda")
+    w_rec = torch.empty((1, dims.top_k), dtype=torch.float32, device="cuda")
+    smoe.decode_layers(dims, 1, r, stack.router, None, stack.tables, smoe.workspace(dims, 1), None, i_rec, w_rec)
+    torch.cuda.synchronize()
+    got = i_rec.cpu().numpy()[0].tolist()
+    assert got == ref_idx, (got, ref_idx)
+    assert np.allclose(w_rec.cpu().numpy()[0], ref_w, rtol=2e-6, atol=1e-7)
+    # and the separate router agrees bit for bit
+    xb, ig, wg, r_out = _decode_one_layer(dims, stack, 0, res)
+    assert list(ig) == got and np.array_equal(wg, w_rec.cpu().numpy()[0])
+    assert np.array_equal(r_out, r.cpu().numpy())
