@@ -258,7 +258,7 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     s_ptr[tid] = p;
   }
   // Pull the next layer's router rows into cache while this kernel streams:
-  // the router workgroup w (rows [4w, 4w + 4)) runs on XCD w % 8, so the down
+  // the router workgroup w (rows [2w, 2w + 2)) runs on XCD w % 8, so the down
   // workgroups of that XCD each fetch one slice of those rows.  Each thread
   // takes at most kPrefetchPerThread 16-byte pieces (out-of-range pieces read
   // the first 16 bytes instead, harmlessly); the loads are issued after the
@@ -266,10 +266,10 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   constexpr int kPrefetchPerThread = 2;
   const uint8_t* pf_addr[kPrefetchPerThread];
   if (a.pf_base) {
-    const size_t row_bytes = (size_t)a.d * 2, blk = (size_t)kRouteRowsPerWG * row_bytes;
+    const size_t row_bytes = (size_t)a.d * 2, blk = (size_t)kRouteDecRowsPerWG * row_bytes;
     const size_t total = (size_t)a.E * row_bytes;
     const int x = blockIdx.x % kXcds, q = blockIdx.x / kXcds, Q = (gridDim.x + kXcds - 1) / kXcds;
-    const int rw = (a.E + kRouteRowsPerWG - 1) / kRouteRowsPerWG;
+    const int rw = (a.E + kRouteDecRowsPerWG - 1) / kRouteDecRowsPerWG;
     const int cx = x < rw ? (rw - x + kXcds - 1) / kXcds : 0;
     const size_t bx = (size_t)cx * blk, share = ((bx + Q - 1) / Q + 15) & ~(size_t)15;
     const size_t lo = (size_t)q * share, hi = lo + share < bx ? lo + share : bx;

@@ -179,9 +179,9 @@ struct ExpertSource {
   const void* direct[kMaxTopK];     // blob pointers passed by value (ring slots)
 };
 
-// Router rows per workgroup of the logits kernel (one per wave); the down
-// kernel uses it to prefetch the next layer's router rows per XCD.
-constexpr int kRouteRowsPerWG = 4;
+// Router rows per workgroup of the one-token logits kernel; the down kernel
+// uses it to prefetch the next layer's router rows per XCD.
+constexpr int kRouteDecRowsPerWG = 2;
 constexpr int kXcds = 8;  // MI355X: workgroup i is dispatched to XCD i % 8
 
 // Selection inside the gate/up kernel: every workgroup ranks the layer's E

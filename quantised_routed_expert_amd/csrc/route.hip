@@ -131,6 +131,109 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm + logits for one token (decode).  grid = ceil(E / 2) workgroups of
+// 4 waves; wave w of workgroup b takes router row 2b + w / 2 and half w % 2 of
+// the d columns.  Within its half, lane l owns the 8 consecutive columns
+// m * 512 + 8 l for m < d / 1024, so each lane normalises exactly the columns it
+// multiplies: x never goes through LDS.  Waves 0 and 1 cover every column once;
+// their float64 partial sums of squares (fixed order) give the norm.  The row's
+// two half dot products (float64) are added half 0 + half 1.  Workgroup 0
+// writes x (bf16) and its pair-ordered f16 copy with 16-byte stores.
+// ---------------------------------------------------------------------------
+constexpr int kRouteDecPieces = 8;  // 16-byte router pieces per lane: d <= 8192
+
+__global__ __launch_bounds__(256) void route_logits_decode_kernel(RouteArgs a) {
+  __shared__ double red[4];
+  __shared__ double part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = a.d, hd = d >> 1, M = d >> 10;
+  const int e = blockIdx.x * kRouteDecRowsPerWG + (wave >> 1);
+  const int half = wave & 1;
+  const bool has_e = e < a.E;
+
+  uint4 wv[kRouteDecPieces];
+  float4 rv[2 * kRouteDecPieces];
+  const uint16_t* wrow = a.w_router + (size_t)(has_e ? e : 0) * d + half * hd;
+  const float* rr = a.residual + half * hd;
+#pragma unroll
+  for (int m = 0; m < kRouteDecPieces; ++m) {
+    if (m < M) {
+      const int j = m * 512 + lane * 8;
+      wv[m] = has_e ? gload16(wrow + j) : make_uint4(0, 0, 0, 0);
+      rv[2 * m] = *reinterpret_cast<const float4*>(rr + j);
+      rv[2 * m + 1] = *reinterpret_cast<const float4*>(rr + j + 4);
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int m = 0; m < 2 * kRouteDecPieces; ++m)
+    if (m < 2 * M)
+      ss += ((double)rv[m].x * rv[m].x + (double)rv[m].y * rv[m].y) +
+            ((double)rv[m].z * rv[m].z + (double)rv[m].w * rv[m].w);
+  ss = group_sum_f64<64>(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const double den = sqrt((red[0] + red[1]) / (double)d + (double)a.eps);
+  const float inv = (float)(1.0 / den);
+
+  // x (bf16 pairs) for this lane's columns
+  uint32_t xb[kRouteDecPieces][4];
+#pragma unroll
+  for (int m = 0; m < kRouteDecPieces; ++m) {
+    if (m < M) {
+      const float v[8] = {rv[2 * m].x, rv[2 * m].y, rv[2 * m].z, rv[2 * m].w,
+                          rv[2 * m + 1].x, rv[2 * m + 1].y, rv[2 * m + 1].z, rv[2 * m + 1].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xb[m][i] = bf16_of_quotient(v[2 * i], den, inv) | (bf16_of_quotient(v[2 * i + 1], den, inv) << 16);
+    }
+  }
+  if (blockIdx.x == 0 && wave < 2) {
+#pragma unroll
+    for (int m = 0; m < kRouteDecPieces; ++m) {
+      if (m < M) {
+        const int j = half * hd + m * 512 + lane * 8;
+        if (a.x_out) *reinterpret_cast<uint4*>(a.x_out + j) = make_uint4(xb[m][0], xb[m][1], xb[m][2], xb[m][3]);
+        if (a.px_out) {
+          // dword p of the group holds (e_p, e_{p+4}) as f16
+          uint32_t pw[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = (xb[m][p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+            const uint32_t hi = (xb[m][2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
+            pw[p] = f16_bits(bf16_to_f32(lo)) | (f16_bits(bf16_to_f32(hi)) << 16);
+          }
+          *reinterpret_cast<uint4*>(a.px_out + j) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        }
+      }
+    }
+  }
+
+  // this half row's dot product: four float64 chains
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int m = 0; m < kRouteDecPieces; ++m) {
+    if (m < M) {
+      const uint32_t ww[4] = {wv[m].x, wv[m].y, wv[m].z, wv[m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // products of two bf16 values are exact in fp32
+        const float p0 = bf16_to_f32(ww[i] & 0xFFFF) * bf16_to_f32(xb[m][i] & 0xFFFF);
+        const float p1 = bf16_to_f32(ww[i] >> 16) * bf16_to_f32(xb[m][i] >> 16);
+        acc[i] += (double)p0 + (double)p1;
+      }
+    }
+  }
+  const double v = group_sum_f64<64>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (tid < kRouteDecRowsPerWG) {
+    const int row = blockIdx.x * kRouteDecRowsPerWG + tid;
+    if (row < a.E) a.logits[row] = (part[2 * tid] + part[2 * tid + 1]) + (a.bias ? (double)a.bias[row] : 0.0);
+  }
+}
+
 // Top-k for each token: one workgroup of 1024 threads per token (the rank
 // count is spread over 8 slices of the experts).  Optionally also publishes the
 // selected blob pointers from the layer's table and copies of the routing.
@@ -154,7 +257,10 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(TopkArgs a) {
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
   const int eb = (a.E + 3) / 4;
   // tokens per workgroup: the normalised inputs of TB tokens live in LDS
-  if (a.n_tok <= 1) {
+  if (a.n_tok == 1 && a.d % 1024 == 0) {
+    hipLaunchKernelGGL(route_logits_decode_kernel, dim3((a.E + kRouteDecRowsPerWG - 1) / kRouteDecRowsPerWG),
+                       dim3(256), 0, s, a);
+  } else if (a.n_tok <= 1) {
     hipLaunchKernelGGL(route_logits_kernel<1>, dim3(eb, a.n_tok), dim3(256), (size_t)a.d * 2, s, a);
   } else if (a.d > 4096) {
     hipLaunchKernelGGL(route_logits_kernel<2>, dim3(eb, (a.n_tok + 1) / 2), dim3(256), (size_t)a.d * 2 * 2,
