@@ -48,7 +48,7 @@ int check_dims(const smoe_dims* d) {
 
 // Workspace carve-up (offsets from the workspace base, 256-byte aligned).
 struct Workspace {
-  size_t logits, idx, w, ptr, x, px, h, ph, py, pinv, end;
+  size_t logits, idx, w, ptr, x, px, h, ph, py, pinv, slices, end;
 };
 
 Workspace ws_layout(const smoe_dims* d, int max_tokens) {
@@ -66,6 +66,7 @@ Workspace ws_layout(const smoe_dims* d, int max_tokens) {
   w.ph = o;     o = align_up(o + T * k * F * 2, 256);
   w.py = o;     o = align_up(o + T * k * D * 4, 256);
   w.pinv = o;   o = align_up(o + T * k * 4, 256);
+  w.slices = o; o = align_up(o + ((T * k + 15) / 16 + (E < T * k ? E : T * k) + 1) * 4, 256);
   w.end = o;
   return w;
 }
@@ -279,6 +280,8 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
   a.offsets = offsets;
   a.perm = perm;
   a.invperm = reinterpret_cast<int32_t*>(base + L.pinv);
+  a.slices = reinterpret_cast<int32_t*>(base + L.slices);
+  a.n_slices = a.slices + prefill_max_slices(n_tok, d->top_k, d->n_experts);
   a.H = reinterpret_cast<_Float16*>(base + L.ph);
   a.Y = reinterpret_cast<float*>(base + L.py);
   a.T = n_tok;

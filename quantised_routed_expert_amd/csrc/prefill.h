@@ -16,6 +16,9 @@ struct PrefillArgs {
   int32_t* offsets;           // [min(E, T*k) + 1]
   int32_t* perm;              // [T*k]
   int32_t* invperm;           // [T*k] position of entry t*k+r in perm (workspace)
+  int32_t* slices;            // [T*k/16 + min(E, T*k)] (u << 8 | s): slice s = entries
+                              // 16 s .. 16 s + 15 of union expert u (workspace)
+  int32_t* n_slices;          // [1] (workspace)
   _Float16* H;                // [T*k][f] SwiGLU activations, fp16 pair order
   float* Y;                   // [T*k][d] per-entry expert outputs
   int T, d, f, E, k, chunk;
@@ -23,5 +26,8 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+// Upper bound on the number of 16-entry slices of a chunk's union experts.
+inline int prefill_max_slices(int T, int k, int E) { return (T * k + 15) / 16 + (E < T * k ? E : T * k); }
 
 }  // namespace smoe

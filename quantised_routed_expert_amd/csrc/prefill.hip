@@ -35,6 +35,7 @@ __global__ __launch_bounds__(1024) void prefill_union_kernel(PrefillArgs a) {
   __shared__ int rank_of[kMaxExperts];
   __shared__ int uid[kMaxExperts];
   __shared__ int scan[2][kMaxExperts + 1];
+  __shared__ int sscan[2][kMaxExperts + 1];
   __shared__ int s_nu;
   const int tid = threadIdx.x;
   const int n = a.T * a.k;
@@ -91,6 +92,21 @@ __global__ __launch_bounds__(1024) void prefill_union_kernel(PrefillArgs a) {
     a.offsets[0] = 0;
     *a.union_count = nu;
   }
+  // slices of 16 entries per union expert, in union order (inclusive scan)
+  if (tid < nu) sscan[0][tid] = (cnt[uid[tid]] + 15) / 16;
+  __syncthreads();
+  int ssrc = 0;
+  for (int off = 1; off < nu; off <<= 1) {
+    if (tid < nu) sscan[ssrc ^ 1][tid] = sscan[ssrc][tid] + (tid >= off ? sscan[ssrc][tid - off] : 0);
+    __syncthreads();
+    ssrc ^= 1;
+  }
+  if (tid < nu) {
+    const int end = sscan[ssrc][tid], ns = (cnt[uid[tid]] + 15) / 16;
+    for (int q = 0; q < ns; ++q) a.slices[end - ns + q] = (tid << 8) | q;
+    if (tid == nu - 1) *a.n_slices = end;
+  }
+  if (tid == 0 && nu == 0) *a.n_slices = 0;
   if (tid < n) {
     int pos = -1;
     if (e >= 0) {
@@ -143,187 +159,213 @@ __device__ __forceinline__ void params_f16(uint32_t p, h2_t& s, h2_t& s16, h2_t&
   m = h2_t{mv, mv};
 }
 
-constexpr int kPfKT = 128;      // K per iteration (4 MFMA steps)
-constexpr int kPfMaxMT = 4;     // up to 64 tokens per expert = 4 M tiles of 16
 
-// Rows of the union expert's tokens in LDS, fp16 pair order within groups of 8,
-// for one K block: xs[mt][row][kPfKT].
-template <bool FROM_BF16>
-__device__ __forceinline__ void stage_rows(_Float16 (*xs)[16][kPfKT], const void* src, size_t row_elems,
-                                           const int* rows, int n_rows, int mt_count, int kb) {
-  const int tid = threadIdx.x;  // 256 threads: 16 rows x 16 groups of 8 per M tile
-  const int r = tid >> 4, c8 = (tid & 15) * 8;
-  for (int mt = 0; mt < mt_count; ++mt) {
-    const int m = mt * 16 + r;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < n_rows) {
-      const size_t off = (size_t)rows[m] * row_elems + kb + c8;
-      v = gload16(reinterpret_cast<const uint16_t*>(src) + off);
-    }
-    uint4 o;
-    if (FROM_BF16) {
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      float f[8];
+// ---------------------------------------------------------------------------
+// 2-3. Grouped GEMMs over slices: a slice is up to 16 consecutive entries of
+// one union expert (one MFMA M tile).  grid = (N / 64, max slices), 256
+// threads; workgroup (nt, s) computes features [64 nt, 64 nt + 64) of slice s,
+// wave w the 16 features 64 nt + 16 w .. + 15.  An expert with more than 16
+// entries has several slices whose workgroups run side by side, so its
+// weights come from HBM once and from cache for the others.
+//
+// K advances in blocks of KT.  In a block, lane (nl = l % 16, g = l / 16)
+// holds the KT / 4 consecutive codes of row nl starting at kb + g KT / 4
+// (KT / 64 16-byte loads, so a row is read in runs of KT / 2 bytes), and MFMA
+// step t (0 .. KT / 32 - 1) takes k = kb + g KT / 4 + 8 t + i (i < 8) from
+// lane group g; the A fragments in LDS use the same k order.  Token rows and
+// weights of block i + 1 are requested before block i is computed.
+// ---------------------------------------------------------------------------
+template <int KT>
+struct KBlock {
+  static constexpr int KPL = KT / 4;      // codes per lane per block
+  static constexpr int NC = KPL / 32;     // 16-byte code loads per lane
+  static constexpr int STEPS = KT / 32;   // MFMA steps per block
+};
+
+// A slice's token rows for one K block (16 rows x KT fp16) staged in LDS.
+// Thread (r = tid / 16, c = tid % 16) moves KT / 16 consecutive values of row
+// r; load() and store() are separate so the loads run a block ahead.
+template <bool FROM_BF16, int KT>
+struct RowStage {
+  static constexpr int V = KT / 16 / 8;  // uint4 (8 values) per thread
+  uint4 v[V];
+
+  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
+    const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * (KT / 16);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        f[2 * p] = bf16_to_f32(w4[p] & 0xFFFF);
-        f[2 * p + 1] = bf16_to_f32(w4[p] >> 16);
-      }
-      o.x = f16_bits(f[0]) | (f16_bits(f[4]) << 16);
-      o.y = f16_bits(f[1]) | (f16_bits(f[5]) << 16);
-      o.z = f16_bits(f[2]) | (f16_bits(f[6]) << 16);
-      o.w = f16_bits(f[3]) | (f16_bits(f[7]) << 16);
-    } else {
-      o = v;  // already fp16 in pair order
+    for (int j = 0; j < V; ++j) {
+      v[j] = make_uint4(0, 0, 0, 0);
+      if (r < n_rows) v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + c + 8 * j);
     }
-    *reinterpret_cast<uint4*>(&xs[mt][r][c8]) = o;
   }
-}
 
-// One wave: 16 output features (rows n0..n0+15 of a matrix) x all M tiles,
-// one K block.  Lane (nl = l % 16, g = l / 16) dequantises 32 codes of row
-// n0 + nl at K [kb + 32 g, kb + 32 g + 32): dword t feeds MFMA step t.
-template <int CHUNK, int MT>
-__device__ __forceinline__ void mma_block(float4_t (*acc)[1], const uint8_t* codes_row, const uint8_t* par_row,
-                                          _Float16 (*xs)[16][kPfKT], int kb, int lane) {
+  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8]) const {
+    const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * (KT / 16);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      uint4 o;
+      if (FROM_BF16) {
+        const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float f[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          f[2 * p] = bf16_to_f32(w4[p] & 0xFFFF);
+          f[2 * p + 1] = bf16_to_f32(w4[p] >> 16);
+        }
+        o.x = f16_bits(f[0]) | (f16_bits(f[4]) << 16);
+        o.y = f16_bits(f[1]) | (f16_bits(f[5]) << 16);
+        o.z = f16_bits(f[2]) | (f16_bits(f[6]) << 16);
+        o.w = f16_bits(f[3]) | (f16_bits(f[7]) << 16);
+      } else {
+        o = v[j];  // already fp16 in pair order
+      }
+      *reinterpret_cast<uint4*>(&xs[r][c + 8 * j]) = o;
+    }
+  }
+};
+
+// One K block of one weight row per lane (codes and the (scale, min) words of
+// the chunks they fall in).
+template <int CHUNK, int KT>
+struct WBlock {
+  static constexpr int NC = KBlock<KT>::NC;
+  static constexpr int NP = (KBlock<KT>::KPL + CHUNK - 1) / CHUNK;  // chunks per lane run
+  uint4 c[NC];
+  uint32_t p[NP];
+
+  __device__ __forceinline__ void load(const uint8_t* codes_row, const uint8_t* par_row, int kb, int lane) {
+    const int k0 = kb + (lane >> 4) * KBlock<KT>::KPL;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) c[j] = gload16(codes_row + k0 / 2 + 16 * j);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) p[j] = gload4(par_row + (k0 / CHUNK + j) * 4);
+  }
+};
+
+// acc += A (16 rows in xs, k order as above) x B (one N tile), one K block.
+template <int CHUNK, int KT>
+__device__ __forceinline__ void mma_kblock(float4_t& acc, const WBlock<CHUNK, KT>& w, _Float16 (*xs)[KT + 8],
+                                           int lane) {
   const int g = lane >> 4, ml = lane & 15;
-  const uint4 c = gload16(codes_row + kb / 2 + 16 * g);
-  const uint32_t p = gload4(par_row + ((kb + 32 * g) / CHUNK) * 4);
-  h2_t s, s16, m;
-  params_f16(p, s, s16, m);
-  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const half8_t b = dequant8(cw[t], s, s16, m);
+  for (int j = 0; j < KBlock<KT>::NC; ++j) {
+    // 32 codes (4 MFMA steps) of this lane; their chunk
+    const int pj = (32 * j) / CHUNK;
+    h2_t sc, sc16, mn;
+    params_f16(w.p[pj], sc, sc16, mn);
+    const uint32_t cw[4] = {w.c[j].x, w.c[j].y, w.c[j].z, w.c[j].w};
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const half8_t av = *reinterpret_cast<const half8_t*>(&xs[mt][ml][32 * g + 8 * t]);
-      acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, acc[mt][0], 0, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+      const half8_t av =
+          *reinterpret_cast<const half8_t*>(&xs[ml][g * KBlock<KT>::KPL + 32 * j + 8 * t]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, dequant8(cw[t], sc, sc16, mn), acc, 0, 0, 0);
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// 2. Grouped gate/up GEMM + SwiGLU.  grid = (d_ff / 64, min(E, T*k)),
-// 256 threads (4 waves x 16 features).  Workgroup (nt, u) handles union expert
-// u (exits when u >= |union|) and features [64 nt, 64 nt + 64).
-// ---------------------------------------------------------------------------
-template <int CHUNK, int MT>
-__device__ void gate_up_body(const PrefillArgs& a, const uint8_t* blob, int o, int n_u, const int* rows,
-                             _Float16 (*xs)[kPfMaxMT][16][kPfKT]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 64 + wave * 16;
-  const size_t row_bytes = (size_t)a.d / 2, prow = (size_t)(a.d / CHUNK) * 4;
-  const uint8_t* gc = blob + (size_t)(n0 + (lane & 15)) * row_bytes;
-  const uint8_t* uc = blob + a.lay.up_codes + (size_t)(n0 + (lane & 15)) * row_bytes;
-  const uint8_t* gp = blob + a.lay.gate_params + (size_t)(n0 + (lane & 15)) * prow;
-  const uint8_t* up = blob + a.lay.up_params + (size_t)(n0 + (lane & 15)) * prow;
-  float4_t accg[MT][1], accu[MT][1];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    accg[mt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-    accu[mt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  int buf = 0;
-  stage_rows<true>(xs[0], a.x, (size_t)a.d, rows, n_u, MT, 0);
-  __syncthreads();
-  for (int kb = 0; kb < a.d; kb += kPfKT) {
-    if (kb + kPfKT < a.d) stage_rows<true>(xs[buf ^ 1], a.x, (size_t)a.d, rows, n_u, MT, kb + kPfKT);
-    mma_block<CHUNK, MT>(accg, gc, gp, xs[buf], kb, lane);
-    mma_block<CHUNK, MT>(accu, uc, up, xs[buf], kb, lane);
-    __syncthreads();
-    buf ^= 1;
-  }
-  // epilogue: lane holds rows 4 (l / 16) + i of each M tile, feature n0 + l % 16
-  const int n = n0 + (lane & 15);
-  const int hcol = (n & ~7) + pair_slot(n & 7);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = mt * 16 + 4 * (lane >> 4) + i;
-      if (row < n_u) {
-        const float gv = accg[mt][0][i], uv = accu[mt][0][i];
-        a.H[(size_t)(o + row) * a.f + hcol] = (_Float16)(silu_f32(gv) * uv);
-      }
-    }
-  }
+struct SliceInfo {
+  int u, o, n_rows;
+};
+
+__device__ __forceinline__ bool slice_info(const PrefillArgs& a, SliceInfo& si) {
+  const int sidx = blockIdx.y;
+  if (sidx >= *a.n_slices) return false;
+  const int packed = a.slices[sidx];
+  si.u = packed >> 8;
+  const int q = packed & 255;
+  const int o = a.offsets[si.u], n_u = a.offsets[si.u + 1] - o;
+  si.o = o + 16 * q;
+  si.n_rows = n_u - 16 * q < 16 ? n_u - 16 * q : 16;
+  return si.n_rows > 0;
 }
 
-template <int CHUNK>
+template <int CHUNK, int KT>
 __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
-  __shared__ _Float16 xs[2][kPfMaxMT][16][kPfKT];
-  __shared__ int rows[kMaxPrefillTokens];
-  const int u = blockIdx.y;
-  if (u >= *a.union_count) return;
-  const int e = a.union_ids[u];
-  const int o = a.offsets[u], n_u = a.offsets[u + 1] - o;
-  if (e < 0 || e >= a.E || n_u <= 0) return;
+  __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
+  __shared__ int rows[16];
+  SliceInfo si;
+  if (!slice_info(a, si)) return;
+  const int e = a.union_ids[si.u];
+  if (e < 0 || e >= a.E) return;
   const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.table[e]);
-  if (threadIdx.x < n_u) rows[threadIdx.x] = a.perm[o + threadIdx.x] / a.k;  // token of each entry
-  __syncthreads();
-  const int mt = (n_u + 15) / 16;
-  switch (mt) {
-    case 1: gate_up_body<CHUNK, 1>(a, blob, o, n_u, rows, xs); break;
-    case 2: gate_up_body<CHUNK, 2>(a, blob, o, n_u, rows, xs); break;
-    case 3: gate_up_body<CHUNK, 3>(a, blob, o, n_u, rows, xs); break;
-    default: gate_up_body<CHUNK, 4>(a, blob, o, n_u, rows, xs); break;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 3. Grouped down GEMM.  grid = (d_model / 64, min(E, T*k)), 256 threads.
-// A = H rows o..o+n_u-1 (fp16, pair order), B = D rows (output features).
-// ---------------------------------------------------------------------------
-template <int CHUNK, int MT>
-__device__ void down_body(const PrefillArgs& a, const uint8_t* blob, int o, int n_u, const int* rows,
-                          _Float16 (*xs)[kPfMaxMT][16][kPfKT]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 64 + wave * 16;
-  const size_t row_bytes = (size_t)a.f / 2, prow = (size_t)(a.f / CHUNK) * 4;
-  const uint8_t* dc = blob + a.lay.down_codes + (size_t)(n0 + (lane & 15)) * row_bytes;
-  const uint8_t* dp = blob + a.lay.down_params + (size_t)(n0 + (lane & 15)) * prow;
-  float4_t acc[MT][1];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-  int buf = 0;
-  stage_rows<false>(xs[0], a.H, (size_t)a.f, rows, n_u, MT, 0);
+  if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
   __syncthreads();
-  for (int kb = 0; kb < a.f; kb += kPfKT) {
-    if (kb + kPfKT < a.f) stage_rows<false>(xs[buf ^ 1], a.H, (size_t)a.f, rows, n_u, MT, kb + kPfKT);
-    mma_block<CHUNK, MT>(acc, dc, dp, xs[buf], kb, lane);
-    __syncthreads();
-    buf ^= 1;
-  }
-  const int n = n0 + (lane & 15);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = mt * 16 + 4 * (lane >> 4) + i;
-      if (row < n_u) a.Y[(size_t)(o + row) * a.d + n] = acc[mt][0][i];
+  const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const size_t row_bytes = (size_t)a.d / 2, prow = (size_t)(a.d / CHUNK) * 4;
+  const uint8_t* gc = blob + (size_t)n0 * row_bytes;
+  const uint8_t* uc = blob + a.lay.up_codes + (size_t)n0 * row_bytes;
+  const uint8_t* gp = blob + a.lay.gate_params + (size_t)n0 * prow;
+  const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
+  float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
+  const int nk = a.d / KT;
+  RowStage<true, KT> xr;
+  WBlock<CHUNK, KT> g0, u0, g1, u1;
+  xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
+  g0.load(gc, gp, 0, lane);
+  u0.load(uc, up, 0, lane);
+  xr.store(xs[0]);
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) {  // rows first, then weights, of block i + 1
+      xr.load(a.x, (size_t)a.d, rows, si.n_rows, (i + 1) * KT);
+      g1.load(gc, gp, (i + 1) * KT, lane);
+      u1.load(uc, up, (i + 1) * KT, lane);
     }
+    mma_kblock<CHUNK, KT>(ag, g0, xs[i & 1], lane);
+    mma_kblock<CHUNK, KT>(au, u0, xs[i & 1], lane);
+    if (i + 1 < nk) xr.store(xs[(i + 1) & 1]);
+    g0 = g1;
+    u0 = u1;
+    __syncthreads();
+  }
+  // epilogue: lane holds rows 4 (l / 16) + i of the tile, feature n0
+  const int hcol = (n0 & ~7) + pair_slot(n0 & 7);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    if (row < si.n_rows) a.H[(size_t)(si.o + row) * a.f + hcol] = (_Float16)(silu_f32(ag[i]) * au[i]);
   }
 }
 
-template <int CHUNK>
+template <int CHUNK, int KT>
 __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
-  __shared__ _Float16 xs[2][kPfMaxMT][16][kPfKT];
-  __shared__ int rows[kMaxPrefillTokens];
-  const int u = blockIdx.y;
-  if (u >= *a.union_count) return;
-  const int e = a.union_ids[u];
-  const int o = a.offsets[u], n_u = a.offsets[u + 1] - o;
-  if (e < 0 || e >= a.E || n_u <= 0) return;
+  __shared__ _Float16 xs[2][16][KT + 8];
+  __shared__ int rows[16];
+  SliceInfo si;
+  if (!slice_info(a, si)) return;
+  const int e = a.union_ids[si.u];
+  if (e < 0 || e >= a.E) return;
   const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.table[e]);
-  if (threadIdx.x < n_u) rows[threadIdx.x] = o + threadIdx.x;  // H rows of this expert
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
   __syncthreads();
-  const int mt = (n_u + 15) / 16;
-  switch (mt) {
-    case 1: down_body<CHUNK, 1>(a, blob, o, n_u, rows, xs); break;
-    case 2: down_body<CHUNK, 2>(a, blob, o, n_u, rows, xs); break;
-    case 3: down_body<CHUNK, 3>(a, blob, o, n_u, rows, xs); break;
-    default: down_body<CHUNK, 4>(a, blob, o, n_u, rows, xs); break;
+  const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const size_t row_bytes = (size_t)a.f / 2, prow = (size_t)(a.f / CHUNK) * 4;
+  const uint8_t* dc = blob + a.lay.down_codes + (size_t)n0 * row_bytes;
+  const uint8_t* dp = blob + a.lay.down_params + (size_t)n0 * prow;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int nk = a.f / KT;
+  RowStage<false, KT> hr;
+  WBlock<CHUNK, KT> w0, w1;
+  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
+  w0.load(dc, dp, 0, lane);
+  hr.store(xs[0]);
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) {
+      hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT);
+      w1.load(dc, dp, (i + 1) * KT, lane);
+    }
+    mma_kblock<CHUNK, KT>(acc, w0, xs[i & 1], lane);
+    if (i + 1 < nk) hr.store(xs[(i + 1) & 1]);
+    w0 = w1;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    if (row < si.n_rows) a.Y[(size_t)(si.o + row) * a.d + n0] = acc[i];
   }
 }
 
@@ -346,12 +388,21 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const int max_union = a.E < a.T * a.k ? a.E : a.T * a.k;
   hipLaunchKernelGGL(prefill_union_kernel, dim3(1), dim3(1024), 0, s, a);
+  const int ms = prefill_max_slices(a.T, a.k, a.E);
+  (void)max_union;
+  const dim3 gu(a.f / 64, ms), dn(a.d / 64, ms);
+  // K blocks of 256 codes for gate/up (two matrices in registers), 512 for
+  // down, when K allows (runs of 128 / 256 bytes per row); else 128
   if (a.chunk == 64) {
-    hipLaunchKernelGGL(prefill_gate_up_kernel<64>, dim3(a.f / 64, max_union), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(prefill_down_kernel<64>, dim3(a.d / 64, max_union), dim3(256), 0, s, a);
+    if (a.d % 256 == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<64, 256>), gu, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_gate_up_kernel<64, 128>), gu, dim3(256), 0, s, a);
+    if (a.f % 512 == 0) hipLaunchKernelGGL((prefill_down_kernel<64, 512>), dn, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_down_kernel<64, 128>), dn, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(prefill_gate_up_kernel<32>, dim3(a.f / 64, max_union), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(prefill_down_kernel<32>, dim3(a.d / 64, max_union), dim3(256), 0, s, a);
+    if (a.d % 256 == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<32, 256>), gu, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_gate_up_kernel<32, 128>), gu, dim3(256), 0, s, a);
+    if (a.f % 512 == 0) hipLaunchKernelGGL((prefill_down_kernel<32, 512>), dn, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_down_kernel<32, 128>), dn, dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((a.d + 255) / 256, a.T), dim3(256), 0, s, a);
   return hipGetLastError();
