@@ -108,6 +108,53 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def read_references(per_launch, instrument_steps):
+    """Attainable read bandwidth, from the plain streaming-read kernel in
+    synth/probe.hip: (a) over a 4 GiB buffer, far beyond the 256 MB MALL;
+    (b) one launch over ``per_launch`` bytes, each launch on a different
+    region of that buffer, timed like the gate/up kernel (hipExtLaunchKernel
+    events, queue pre-filled).  Returns GB/s for both."""
+    from synth.device import stream_read
+    big = 4 << 30
+    buf = torch.empty(big, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1024, dtype=torch.int32, device="cuda")
+    n_big = 10
+    ev = HipEvents(2 * n_big)
+    for _ in range(2):
+        stream_read(buf, big, sink=sink)
+    torch.cuda._sleep(5_000_000)
+    for i in range(n_big):
+        stream_read(buf, big, sink=sink, start=ev.ev[2 * i], stop=ev.ev[2 * i + 1])
+    torch.cuda.synchronize()
+    big_ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_big)]))
+    ev.close()
+    per = (per_launch + 255) // 256 * 256
+    regions = big // per
+    n_small = max(1, min(regions, 8 * instrument_steps))
+    ev = HipEvents(2 * n_small)
+    torch.cuda._sleep(5_000_000)
+    for i in range(n_small):
+        stream_read(buf, per_launch, offset=i * per, sink=sink, start=ev.ev[2 * i], stop=ev.ev[2 * i + 1])
+    torch.cuda.synchronize()
+    small_ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(n_small)]))
+    ev.close()
+    del buf
+    return {"stream_4gib_gbps": big / (big_ms / 1e3) / 1e9,
+            "one_launch_same_bytes_gbps": per_launch / (small_ms / 1e3) / 1e9,
+            "one_launch_same_bytes_us": small_ms * 1e3}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(stack, wl, budget_s=15.0):
     """The float64 oracle on the host cores: one token through as many of the
     stack's layers as fit in ``budget_s`` of oracle time (input drawing is not
@@ -136,7 +183,7 @@ def cpu_baseline(stack, wl, budget_s=15.0):
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     per_token = spent / n * wl.n_layers
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"1 decode token through the first {n} of {wl.n_layers} layers, float64 numpy oracle, "
                       f"{spent:.1f} s of oracle time; tokens/s extrapolated to all {wl.n_layers} layers"}
 
@@ -208,6 +255,9 @@ def bench_decode(args):
     gu_ms = float(np.mean(durs))
     achieved = per_launch / (gu_ms / 1000.0) / 1e9
     log(f"gate/up kernel: {gu_ms * 1000:.2f} us avg over {len(durs)} launches, {achieved:.0f} GB/s")
+    refs = read_references(per_launch, args.instrument_steps)
+    log(f"plain reads: 4 GiB stream {refs['stream_4gib_gbps']:.0f} GB/s; one launch of the same "
+        f"{per_launch} B {refs['one_launch_same_bytes_us']:.2f} us = {refs['one_launch_same_bytes_gbps']:.0f} GB/s")
 
     bytes_per_token = wl.n_layers * (dims.top_k * off["bytes"] + dims.n_experts * dims.d_model * 2)
     out = {
@@ -231,7 +281,10 @@ def bench_decode(args):
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(),
                      "kernel": "decode_gate_up_kernel", "bytes_per_launch": per_launch,
                      "avg_launch_us": gu_ms * 1000.0, "launches_timed": len(durs),
-                     "timing": "hipExtLaunchKernel start/stop events, eager token with the queue pre-filled"},
+                     "timing": "hipExtLaunchKernel start/stop events, eager token with the queue pre-filled",
+                     "attainable": dict(refs, frac_of_stream_4gib=achieved / refs["stream_4gib_gbps"],
+                                        frac_of_one_launch_same_bytes=achieved
+                                        / refs["one_launch_same_bytes_gbps"])},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -373,6 +426,8 @@ def bench_ring(args):
     # driver caps page-locked memory (64 GiB on the MI355X hosts measured), so
     # the rest of a 128 GB vault stays pageable and its fills are staged by
     # the HIP runtime.
+    link = h2d_references()
+    log(f"host link: pinned H2D {link['pinned_h2d_gbps']:.1f} GB/s, pageable H2D {link['pageable_h2d_gbps']:.1f} GB/s")
     pinned_budget = int(args.pinned_gib * (1 << 30))
     vault, views = [], []
     for L in range(NL):
@@ -455,11 +510,37 @@ def bench_ring(args):
         "hit_rate": hits / max(1, hits + misses), "misses_per_token": misses / K,
         "h2d_gbps": h2d / dt / 1e9, "expert_repeat_fraction": float(np.mean(repeats)),
         "vault_layers_page_locked": n_pinned,
+        "host_link": dict(link, h2d_frac_of_pinned=h2d / dt / 1e9 / link["pinned_h2d_gbps"]),
     }
     del views
     for v in vault:
         v.free()
     print(json.dumps(out), flush=True)
+
+
+def h2d_references(nbytes=1 << 30, reps=4):
+    """Host-to-device copy rates of the ring's two vault kinds: hipMemcpyAsync
+    from page-locked memory (hipHostMalloc) and from pageable memory."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pinned = smoe.PinnedHost(nbytes)
+    pageable = torch.ones(nbytes, dtype=torch.uint8)
+    out = {}
+    s = torch.cuda.current_stream()
+    for name, src in (("pinned_h2d_gbps", pinned.ptr), ("pageable_h2d_gbps", pageable.data_ptr())):
+        assert hip.hipMemcpyAsync(ctypes.c_void_p(dev.data_ptr()), ctypes.c_void_p(src), nbytes, 1,
+                                  ctypes.c_void_p(s.cuda_stream)) == 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            assert hip.hipMemcpyAsync(ctypes.c_void_p(dev.data_ptr()), ctypes.c_void_p(src), nbytes, 1,
+                                      ctypes.c_void_p(s.cuda_stream)) == 0
+        torch.cuda.synchronize()
+        out[name] = reps * nbytes / (time.perf_counter() - t0) / 1e9
+    pinned.free()
+    del dev, pageable
+    return out
 
 
 def bench_copy(args):
@@ -499,7 +580,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
-              "MI355X (no multi-GPU path exists in this build)", file=sys.stderr)
+              "MI355X (the layer has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     defaults = {"decode": (64, 8), "prefill": (3, 1), "ring": (256, 8), "copy": (10, 2)}[args.workload]
     args.steps = defaults[0] if args.steps is None else args.steps

@@ -1,4 +1,5 @@
-"""Builds synth/libsmoe_synth.so (the device-side input generator) with hipcc."""
+"""Builds synth/libsmoe_synth.so (the device-side input generator and the
+streaming-read bandwidth reference) with hipcc."""
 import os
 import subprocess
 import sys
@@ -10,7 +11,7 @@ LIB = os.path.join(HERE, "libsmoe_synth.so")
 def build(verbose: bool = False) -> str:
     cmd = ["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           os.path.join(HERE, "synth_dev.hip"), "-o", LIB + ".tmp"]
+           os.path.join(HERE, "synth_dev.hip"), os.path.join(HERE, "probe.hip"), "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -27,6 +27,9 @@ def lib():
         L.synth_fill_experts.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]
+        L.synth_stream_read.restype = ctypes.c_int
+        L.synth_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -37,6 +40,21 @@ def fill_experts(seed, dims, layer, e_begin, n_exp, dst_ptr, stride, stream=None
                                   int(n_exp), int(dst_ptr), int(stride), s)
     if rc != 0:
         raise RuntimeError(f"synth_fill_experts failed: {rc}")
+
+
+def stream_read(buf: torch.Tensor, nbytes: int, offset: int = 0, grid: int = 0, sink=None, stream=None,
+                start=None, stop=None):
+    """One launch of the plain streaming-read reference over ``nbytes`` of the
+    device tensor ``buf`` from byte ``offset``; ``start``/``stop`` are raw HIP
+    events bracketing the launch (or None)."""
+    if offset < 0 or offset % 16 or nbytes % 16 or offset + nbytes > buf.numel() * buf.element_size():
+        raise ValueError("stream_read: range outside the buffer or not 16-byte aligned")
+    if sink is None:
+        sink = torch.empty(1024, dtype=torch.int32, device=buf.device)
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream
+    rc = lib().synth_stream_read(buf.data_ptr() + offset, nbytes, int(grid), sink.data_ptr(), s, start, stop)
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_read failed: {rc}")
 
 
 def router_stack(seed, dims, n_layers, threads=8) -> np.ndarray:
