@@ -6,9 +6,13 @@
 // Overview step table adds the gate-weighted sum into the residual.  The pages'
 // Metal design (one 32-lane simdgroup per output row, input staged per 8-row
 // threadgroup) is prior art; on gfx950 a row is split over LR lanes of a
-// wave64, each lane streaming one contiguous run of NSEG 16-byte segments of
-// packed nibbles (global_load_dwordx4), the input held in registers as f16
-// pairs for v_dot2_f32_f16, and rows reduced with DPP.
+// wave64, each lane loading NSEG 16-byte segments of packed nibbles
+// (global_load_dwordx4), the input held in registers as f16 pairs for
+// v_dot2_f32_f16, and rows reduced with DPP.  Segment s of lane li sits at
+// byte s * LR * 16 + li * 16 of the row, so the LR lanes of one load
+// instruction read LR * 16 contiguous bytes (whole cache lines); a lane-major
+// run (each lane NSEG adjacent segments) makes every instruction touch each
+// line of the row at half width, which measured markedly slower.
 //
 // Affine folding: a 16-byte segment (32 codes) lies inside one chunk, so its
 // contribution is scale * sum(q x) + min * sum(x); sum(x) over the segment is
@@ -17,6 +21,9 @@
 
 #include "kernels.h"
 
+#ifndef SMOE_GU_WAVES
+#define SMOE_GU_WAVES 4        // waves per gate/up workgroup (a multiple of 2)
+#endif
 #ifndef SMOE_GU_ROWS_MAX
 #define SMOE_GU_ROWS_MAX 4     // rows per wave of the gate/up kernel (upper bound)
 #endif
@@ -32,33 +39,30 @@
 
 namespace smoe {
 
-// Per-lane layout of one row: lane li owns bytes [li*CW, li*CW + CW) of the
-// row's codes (NSEG segments) and the (scale, min) records of the chunks they
-// fall in.
-template <int NSEG, int CHUNK>
+// Per-lane layout of one row: lane li owns the NSEG 16-byte code segments at
+// row bytes s * STRIDE + li * 16 (s < NSEG) and the (scale, min) record of the
+// chunk each falls in.  A segment (32 codes) never straddles a chunk, and two
+// segments of a lane are STRIDE >= 32 bytes apart, so each has its own record.
+template <int LR, int CHUNK>
 struct LaneRun {
-  static constexpr int CW = NSEG * 16;              // code bytes per lane
-  static constexpr int CB = CHUNK / 2;              // code bytes per chunk
-  static constexpr bool ONE = CW <= CB;             // the run sits in one chunk
-  static constexpr bool ALIGNED = CW % CB == 0;     // the run is whole chunks
-  static constexpr int NPL = ONE ? 1 : (ALIGNED ? CW / CB : NSEG);  // param dwords
-  __device__ static int param_of_seg(int s) { return ONE ? 0 : (ALIGNED ? (16 * s) / CB : s); }
-  // chunk index (within the row) of param dword j of lane li
-  __device__ static int chunk_of(int li, int j) {
-    return ONE ? (li * CW) / CB : (ALIGNED ? (li * CW) / CB + j : (li * CW + 16 * j) / CB);
-  }
+  static constexpr int STRIDE = LR * 16;  // bytes between a lane's segments
+  static constexpr int CB = CHUNK / 2;    // code bytes per chunk
+  __device__ static int chunk_of(int li, int s) { return (s * STRIDE + li * 16) / CB; }
 };
 
-// Pair-ordered f16 input of one lane run (NSEG segments of 32 values) and the
+// Pair-ordered f16 input of a lane's NSEG segments (32 values each, the
+// columns of its code segments: 32 * (s * LR + li) onwards) and the
 // per-segment sums, from bf16 (x) or pair-ordered f16 (h) storage.  The raw
 // loads are separate from the conversion so that the weight loads can be
-// issued in between.
-template <int NSEG>
+// issued in between.  `base` points at the lane's first segment; segments are
+// LR * 64 bytes apart (32 two-byte values per lane).
+template <int LR, int NSEG>
 __device__ __forceinline__ void load_raw(const void* base, uint4 (*raw)[4]) {
 #pragma unroll
   for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) raw[s][q] = gload16(reinterpret_cast<const uint8_t*>(base) + s * 64 + q * 16);
+    for (int q = 0; q < 4; ++q)
+      raw[s][q] = gload16(reinterpret_cast<const uint8_t*>(base) + (size_t)s * LR * 64 + q * 16);
 }
 
 template <int NSEG>
@@ -109,30 +113,30 @@ __device__ __forceinline__ const void* expert_pointer(const DecodeArgs& a, int r
 template <int LR, int NSEG, int NP, int CHUNK>
 __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t* blob, int r, int n_begin, int li,
                                              int grp, const uint4 (*xraw)[4]) {
-  using Run = LaneRun<NSEG, CHUNK>;
+  using Run = LaneRun<LR, CHUNK>;
   constexpr int P = kWave / LR;
   const size_t row_bytes = (size_t)a.d / 2;
   const size_t prow_bytes = (size_t)(a.d / CHUNK) * 4;
   const size_t first = (size_t)(n_begin + grp);
-  const uint8_t* gcodes = blob + first * row_bytes + li * Run::CW;
-  const uint8_t* ucodes = blob + a.lay.up_codes + first * row_bytes + li * Run::CW;
+  const uint8_t* gcodes = blob + first * row_bytes + li * 16;
+  const uint8_t* ucodes = blob + a.lay.up_codes + first * row_bytes + li * 16;
   const uint8_t* gpar = blob + a.lay.gate_params + first * prow_bytes;
   const uint8_t* upar = blob + a.lay.up_params + first * prow_bytes;
 
   uint4 cg[NP][NSEG], cu[NP][NSEG];
-  uint32_t pg[NP][Run::NPL], pu[NP][Run::NPL];
+  uint32_t pg[NP][NSEG], pu[NP][NSEG];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      cg[p][s] = gload16(gcodes + (size_t)p * P * row_bytes + s * 16);
-      cu[p][s] = gload16(ucodes + (size_t)p * P * row_bytes + s * 16);
+      cg[p][s] = gload16(gcodes + (size_t)p * P * row_bytes + s * Run::STRIDE);
+      cu[p][s] = gload16(ucodes + (size_t)p * P * row_bytes + s * Run::STRIDE);
     }
 #pragma unroll
-    for (int j = 0; j < Run::NPL; ++j) {
-      const size_t po = (size_t)p * P * prow_bytes + Run::chunk_of(li, j) * 4;
-      pg[p][j] = gload4(gpar + po);
-      pu[p][j] = gload4(upar + po);
+    for (int s = 0; s < NSEG; ++s) {
+      const size_t po = (size_t)p * P * prow_bytes + Run::chunk_of(li, s) * 4;
+      pg[p][s] = gload4(gpar + po);
+      pu[p][s] = gload4(upar + po);
     }
   }
   __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
@@ -148,8 +152,8 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      g += seg_contrib(cg[p][s], xp[s], xseg[s], pg[p][Run::param_of_seg(s)]);
-      u += seg_contrib(cu[p][s], xp[s], xseg[s], pu[p][Run::param_of_seg(s)]);
+      g += seg_contrib(cg[p][s], xp[s], xseg[s], pg[p][s]);
+      u += seg_contrib(cu[p][s], xp[s], xseg[s], pu[p][s]);
     }
     g = group_sum<LR>(g);
     u = group_sum<LR>(u);
@@ -169,7 +173,7 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
 // pointers.  grid = ceil(k * d_ff / (4 * rows per wave)) workgroups of 4 waves.
 // ---------------------------------------------------------------------------
 template <int LR, int NSEG, int NP, int CHUNK>
-__global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(DecodeArgs a) {
   constexpr int P = kWave / LR;  // rows per pass
   constexpr int RPW = NP * P;    // rows per wave
   __shared__ const void* s_ptr[kMaxTopK];
@@ -190,16 +194,21 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a) {
     s_ptr[tid] = expert_pointer(a, tid);
   }
   uint4 xraw[NSEG][4];
-  if (a.px) load_raw<NSEG>(a.px + li * (NSEG * 32), xraw);
-  else load_raw<NSEG>(a.x + li * (NSEG * 32), xraw);
+  if (a.px) load_raw<LR, NSEG>(a.px + li * 32, xraw);
+  else load_raw<LR, NSEG>(a.x + li * 32, xraw);
   if (fused && tid < kMaxExperts) {  // stored after the input loads are issued
-    tk.log[tid] = tid < a.E ? lv : -__builtin_inf();
-    tk.logf[tid] = tid < a.E ? (float)lv : -__builtin_inff();
+    // padding, and a NaN logit (from a non-finite residual), rank as -inf
+    const double l = (tid < a.E && lv == lv) ? lv : -__builtin_inf();
+    tk.log[tid] = l;
+    tk.logf[tid] = (float)l;
     if (tid < a.E) s_tab[tid] = tv;
     if (tid < kMaxTopK) tk.idx[tid] = -1;
   }
   __syncthreads();
-  if (fused) topk_select_fast(tk, a.E, a.k, s_tab, s_ptr);
+  if (fused) {
+    if (a.E <= 128) topk_select_fast128<64 * SMOE_GU_WAVES>(tk, a.E, a.k, s_tab, s_ptr);
+    else topk_select_fast(tk, a.E, a.k, s_tab, s_ptr);
+  }
 
   const int gw = blockIdx.x * (blockDim.x >> 6) + wave;
   const int row0 = gw * RPW;
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 template <int LR, int NSEG, int NPASS, int CHUNK>
 __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
-  using Run = LaneRun<NSEG, CHUNK>;
+  using Run = LaneRun<LR, CHUNK>;
   constexpr int P = kWave / LR;
   constexpr int ROWS = NPASS * P;
   __shared__ float ylds[kMaxTopK][ROWS];
@@ -296,20 +305,20 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
       for (int row = lane; row < ROWS; row += kWave) ylds[r][row] = 0.f;
       continue;
     }
-    const uint8_t* codes = blob + a.lay.down_codes + li * Run::CW;
+    const uint8_t* codes = blob + a.lay.down_codes + li * 16;
     const uint8_t* par = blob + a.lay.down_params;
     uint4 hraw[NSEG][4];
-    load_raw<NSEG>(a.h + (size_t)r * a.f + li * (NSEG * 32), hraw);
+    load_raw<LR, NSEG>(a.h + (size_t)r * a.f + li * 32, hraw);
     __builtin_amdgcn_sched_barrier(0);  // h first: the math can start when it lands
     uint4 c[NPASS][NSEG];
-    uint32_t pr[NPASS][Run::NPL];
+    uint32_t pr[NPASS][NSEG];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       const int n = n0 + p * P + grp;  // < d: the launcher checks d % ROWS == 0
 #pragma unroll
-      for (int s = 0; s < NSEG; ++s) c[p][s] = gload16(codes + (size_t)n * row_bytes + s * 16);
+      for (int s = 0; s < NSEG; ++s) c[p][s] = gload16(codes + (size_t)n * row_bytes + s * Run::STRIDE);
 #pragma unroll
-      for (int j = 0; j < Run::NPL; ++j) pr[p][j] = gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, j) * 4);
+      for (int s = 0; s < NSEG; ++s) pr[p][s] = gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, s) * 4);
     }
     if (it == 0 && a.pf_base) {
 #pragma unroll
@@ -325,7 +334,7 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
       float y = 0.f;
 #pragma unroll
       for (int s = 0; s < NSEG; ++s)
-        y += seg_contrib(c[p][s], hp[s], xseg[s], pr[p][Run::param_of_seg(s)]);
+        y += seg_contrib(c[p][s], hp[s], xseg[s], pr[p][s]);
       y = group_sum<LR>(y);
       if (li == 0) ylds[r][p * P + grp] = y;
     }
@@ -400,9 +409,8 @@ hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t 
   const int total = a.k * a.f;
   const int np = gate_up_np(sp.lr, total, a.f);
   const int waves = total / (np * (64 / sp.lr));
-  // 4 waves per workgroup (measured: 12-wave workgroups, one per CU, spend
-  // longer in the shared selection than they save); launch bounds match
-  constexpr int nw = 4;
+  // the launch bounds and the selection's thread count are SMOE_GU_WAVES waves
+  constexpr int nw = SMOE_GU_WAVES;
   const dim3 grid((waves + nw - 1) / nw);
   SMOE_CHUNK_SWITCH(a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
       if (start || stop) {

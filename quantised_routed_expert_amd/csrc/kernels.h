@@ -18,9 +18,9 @@ namespace smoe {
 // ---------------------------------------------------------------------------
 constexpr int kTopkMaxSlices = 8;
 
-struct TopkShared {
+struct alignas(16) TopkShared {
   double log[kMaxExperts];
-  float logf[kMaxExperts];  // the logits rounded to float (topk_select_fast)
+  alignas(16) float logf[kMaxExperts];  // the logits rounded to float (topk_select_fast*)
   int part[kTopkMaxSlices][kMaxExperts];
   int idx[kMaxTopK];
   double val[kMaxTopK];
@@ -106,7 +106,7 @@ __device__ inline void topk_select_fast(TopkShared& s, int E, int k, const void*
   if (t < E) {
     int c = 0;
     for (int q = 0; q < S; ++q) c += s.part[q][t];
-    if (c - 1 < k) {
+    if (c >= 1 && c <= k) {
       s.idx[c - 1] = t;
       s.val[c - 1] = s.log[t];
       if (tab) slot_ptr[c - 1] = tab[t];
@@ -115,6 +115,51 @@ __device__ inline void topk_select_fast(TopkShared& s, int E, int k, const void*
   __syncthreads();
   bool ok = true;
   for (int r = 0; r < k; ++r) ok &= s.idx[r] >= 0;
+  if (!ok) {  // uniform: every thread read the same slots
+    topk_select(s, E, k);
+    if (tab && t < k) slot_ptr[t] = tab[s.idx[t]];
+    __syncthreads();
+  }
+}
+
+// The same fast path for E <= 128 on a workgroup of exactly NT threads (a
+// multiple of 128), with every bound fixed at compile time: thread t counts
+// for expert t % 128 over slice t / 128 of the (padded) float logits, read
+// from LDS four at a time at wave-uniform addresses; the slices' counts are
+// added once.  Preconditions as for topk_select_fast, with s.logf padded with
+// -inf up to S * SPAN.
+template <int NT>
+__device__ inline void topk_select_fast128(TopkShared& s, int E, int k, const void* const* tab,
+                                           const void** slot_ptr) {
+  constexpr int S = NT / 128;                          // slices
+  constexpr int SPAN = ((128 + S - 1) / S + 3) & ~3;   // logits per slice, a multiple of 4
+  static_assert(NT % 128 == 0 && S <= kTopkMaxSlices && S * SPAN <= kMaxExperts, "slice layout");
+  const int t = threadIdx.x;
+  const int i = t & 127, h = t >> 7;
+  const float x = s.logf[i];
+  const float4* v4 = reinterpret_cast<const float4*>(s.logf + SPAN * h);
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < SPAN / 4; ++q) {
+    const float4 v = v4[q];
+    c += (v.x >= x ? 1 : 0) + (v.y >= x ? 1 : 0) + (v.z >= x ? 1 : 0) + (v.w >= x ? 1 : 0);
+  }
+  s.part[h][i] = c;
+  __syncthreads();
+  if (t < E) {
+    c = 0;
+#pragma unroll
+    for (int q = 0; q < S; ++q) c += s.part[q][t];
+    if (c >= 1 && c <= k) {
+      s.idx[c - 1] = t;
+      s.val[c - 1] = s.log[t];
+      if (tab) slot_ptr[c - 1] = tab[t];
+    }
+  }
+  __syncthreads();
+  bool ok = true;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) ok &= (r >= k) || (s.idx[r] >= 0);
   if (!ok) {  // uniform: every thread read the same slots
     topk_select(s, E, k);
     if (tab && t < k) slot_ptr[t] = tab[s.idx[t]];

@@ -240,7 +240,10 @@ __global__ __launch_bounds__(256) void route_logits_decode_kernel(RouteArgs a) {
 __global__ __launch_bounds__(1024) void route_topk_kernel(TopkArgs a) {
   __shared__ TopkShared tk;
   const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < a.E) tk.log[tid] = a.logits[(size_t)t * a.E + tid];
+  if (tid < a.E) {  // a NaN logit (from a non-finite residual) ranks as -inf
+    const double l = a.logits[(size_t)t * a.E + tid];
+    tk.log[tid] = l == l ? l : -__builtin_inf();
+  }
   __syncthreads();
   topk_block(tk, a.E, a.k, a.norm);
   if (tid < a.k) {

@@ -266,3 +266,45 @@ def test_decode_layers_selection_with_ties_matches_oracle(case):
     xb, ig, wg, r_out = _decode_one_layer(dims, stack, 0, res)
     assert list(ig) == got and np.array_equal(wg, w_rec.cpu().numpy()[0])
     assert np.array_equal(r_out, r.cpu().numpy())
+
+
+@pytest.mark.parametrize("E,k", [(256, 8), (16, 16), (24, 3)])
+def test_decode_layers_selection_other_expert_counts(E, k):
+    """The in-kernel selection has a compile-time path for E <= 128 and a
+    general one above; both must agree with the separate router and the oracle."""
+    dims = synth.Dims(256, 128, E, k, 32)
+    n_layers = 2
+    stack = DeviceStack(1337, dims, n_layers)
+    h0 = random_residual(np.random.default_rng(E + k), 1, dims.d_model)[0]
+    r = torch.from_numpy(h0.copy()).cuda()
+    i_rec = torch.empty((n_layers, k), dtype=torch.int32, device="cuda")
+    w_rec = torch.empty((n_layers, k), dtype=torch.float32, device="cuda")
+    smoe.decode_layers(dims, n_layers, r, stack.router, None, stack.tables, smoe.workspace(dims, 1), None,
+                       i_rec, w_rec)
+    torch.cuda.synchronize()
+    res = h0.copy()
+    for L in range(n_layers):
+        xb, ig, wg, res_next = _decode_one_layer(dims, stack, L, res)
+        ref = oracle.moe_layer(res.astype(np.float64), stack.router_bits[L], LazyExperts(1337, dims, L), dims)
+        assert list(ig) == ref["idx"]
+        assert np.array_equal(ig, i_rec.cpu().numpy()[L])
+        assert np.array_equal(wg, w_rec.cpu().numpy()[L])
+        res = res_next
+    assert np.array_equal(res, r.cpu().numpy())
+
+
+def test_decode_layers_non_finite_residual_still_selects_valid_experts():
+    """A NaN in the residual makes every logit NaN; the selection ranks NaN as
+    -inf, so ties break by index and the experts are 0..k-1 (no invalid id ever
+    reaches a blob lookup)."""
+    dims = SHAPES["tiny"]
+    stack = DeviceStack(1337, dims, 1)
+    h0 = random_residual(np.random.default_rng(5), 1, dims.d_model)[0]
+    h0[3] = np.nan
+    r = torch.from_numpy(h0.copy()).cuda()
+    i_rec = torch.empty((1, dims.top_k), dtype=torch.int32, device="cuda")
+    smoe.decode_layers(dims, 1, r, stack.router, None, stack.tables, smoe.workspace(dims, 1), None, i_rec, None)
+    torch.cuda.synchronize()
+    assert i_rec.cpu().numpy()[0].tolist() == list(range(dims.top_k))
+    _, ig, _, _ = _decode_one_layer(dims, stack, 0, h0)
+    assert list(ig) == list(range(dims.top_k))
