@@ -109,7 +109,9 @@ int smoe_workspace_bytes(const smoe_dims* dims, int32_t max_tokens, size_t* byte
  *   topk_w    device fp32 [n_tok][k]                    (written) softmax over
  *             all E logits at the selected experts, renormalised over the k
  *             when dims->norm_topk_prob
- * Logits are accumulated in float64 (each bf16*bf16 product is exact).
+ * Logits are accumulated in float64 (each bf16*bf16 product is exact); for
+ * 2..64 tokens on float64 MFMA, as d_model / 128 partial sums added in a fixed
+ * order.  A NaN logit (from a non-finite residual) ranks as -inf.
  * 0 <= n_tok <= 64; n_tok == 0 does nothing.  Pointers 16-byte aligned. */
 int smoe_route(const smoe_dims* dims, int32_t n_tok, const float* residual, uint16_t* x_out,
                const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w,

@@ -48,7 +48,7 @@ int check_dims(const smoe_dims* d) {
 
 // Workspace carve-up (offsets from the workspace base, 256-byte aligned).
 struct Workspace {
-  size_t logits, idx, w, ptr, x, px, h, ph, py, pinv, slices, end;
+  size_t logits, plog, idx, w, ptr, x, px, h, ph, py, pinv, slices, end;
 };
 
 Workspace ws_layout(const smoe_dims* d, int max_tokens) {
@@ -57,6 +57,7 @@ Workspace ws_layout(const smoe_dims* d, int max_tokens) {
   const size_t E = d->n_experts, k = d->top_k, D = d->d_model, F = d->d_ff;
   size_t o = 0;
   w.logits = o; o = align_up(o + T * E * 8, 256);
+  w.plog = o;   o = align_up(o + (size_t)(d->d_model / kRouteGroupCols) * T * E * 8, 256);
   w.idx = o;    o = align_up(o + k * 4, 256);
   w.w = o;      o = align_up(o + k * 4, 256);
   w.ptr = o;    o = align_up(o + k * 8, 256);
@@ -140,12 +141,19 @@ int smoe_route(const smoe_dims* d, int32_t n_tok, const float* residual, uint16_
   if (n_tok == 0) return SMOE_OK;
   hipStream_t s = (hipStream_t)stream;
   double* logits = reinterpret_cast<double*>((char*)ws + L.logits);
-  RouteArgs ra{residual, x_out, nullptr, w_router, bias, logits, n_tok, d->d_model, d->n_experts, d->rms_eps};
-  hipError_t he = launch_route_logits(ra, s);
+  double* partial = reinterpret_cast<double*>((char*)ws + L.plog);
+  RouteArgs ra{residual, x_out, nullptr, w_router, bias, logits, n_tok, d->d_model, d->n_experts, d->rms_eps,
+               partial};
+  int groups = 0;
+  hipError_t he = launch_route_logits(ra, s, &groups);
   if (he != hipSuccess) return hip_fail(he, "route_logits launch");
   TopkArgs ta;
   memset(&ta, 0, sizeof(ta));
   ta.logits = logits;
+  ta.partial = partial;
+  ta.groups = groups;
+  ta.bias = bias;
+  ta.n_tok = n_tok;
   ta.idx = topk_idx;
   ta.w = topk_w;
   ta.E = d->n_experts;
@@ -226,8 +234,9 @@ int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, co
     uint16_t* xl = x_rec ? x_rec + (size_t)layer * D : xbuf;
     _Float16* px = reinterpret_cast<_Float16*>(base + L.px);
     const RouteArgs ra{residual, xl, px, w_router + (size_t)layer * E * D, bias ? bias + (size_t)layer * E : nullptr,
-                       logits, 1, d->d_model, d->n_experts, d->rms_eps};
-    hipError_t he = launch_route_logits(ra, s);
+                       logits, 1, d->d_model, d->n_experts, d->rms_eps, nullptr};
+    int groups = 0;  // one token: the logits are written directly
+    hipError_t he = launch_route_logits(ra, s, &groups);
     if (he != hipSuccess) return hip_fail(he, "route_logits launch");
     // the top-k selection runs inside the gate/up kernel, which publishes ids,
     // weights and blob pointers for the down kernel

@@ -201,12 +201,23 @@ struct RouteArgs {
   double* logits;           // [n_tok][E]
   int n_tok, d, E;
   float eps;
+  double* partial;          // [d / kRouteGroupCols][n_tok][E] workspace for the MFMA path, or null
 };
 
-hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s);
+// Columns per workgroup of the multi-token MFMA router: its partial logits
+// are added (bias last) by the top-k kernel.
+constexpr int kRouteGroupCols = 128;
+
+// Launches the logits kernel for a.n_tok tokens.  *groups = 0 when the logits
+// were written to a.logits (bias included), else the number of column-group
+// partials written to a.partial (no bias) that the top-k kernel must add.
+hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s, int* groups);
 
 struct TopkArgs {
-  const double* logits;      // [n_tok][E]
+  const double* logits;      // [n_tok][E] (groups == 0)
+  const double* partial;     // [groups][n_tok][E] partial logits, added in order (groups > 0)
+  const float* bias;         // [E] added to the partial sums, or null
+  int groups, n_tok;
   int32_t* idx;              // [n_tok][k]
   float* w;                  // [n_tok][k]
   const void* const* table;  // [E] blob pointers of the layer (with ptr_out)

@@ -234,6 +234,94 @@ __global__ __launch_bounds__(256) void route_logits_decode_kernel(RouteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm for 2..64 tokens: one workgroup of 256 threads per token.  The sum of
+// squares is float64 in a fixed order (per thread, then per wave, then waves
+// 0..3); x = bf16(r / den) is written to x_out for the logits kernel below and
+// for the expert FFN.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_norm_kernel(RouteArgs a) {
+  __shared__ double red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = a.d;
+  const float* r = a.residual + (size_t)blockIdx.x * d;
+  float4 rv[kRouteMaxR];
+#pragma unroll
+  for (int q = 0; q < kRouteMaxR; ++q) {
+    const int j = tid * 4 + 1024 * q;
+    rv[q] = j < d ? *reinterpret_cast<const float4*>(r + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < kRouteMaxR; ++q)
+    s += ((double)rv[q].x * rv[q].x + (double)rv[q].y * rv[q].y) + ((double)rv[q].z * rv[q].z + (double)rv[q].w * rv[q].w);
+  s = group_sum_f64<64>(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  const double den = sqrt(((red[0] + red[1]) + (red[2] + red[3])) / (double)d + (double)a.eps);
+  const float inv = (float)(1.0 / den);
+  uint16_t* xo = a.x_out + (size_t)blockIdx.x * d;
+#pragma unroll
+  for (int q = 0; q < kRouteMaxR; ++q) {
+    const int j = tid * 4 + 1024 * q;
+    if (j < d) {
+      const uint32_t b0 = bf16_of_quotient(rv[q].x, den, inv), b1 = bf16_of_quotient(rv[q].y, den, inv);
+      const uint32_t b2 = bf16_of_quotient(rv[q].z, den, inv), b3 = bf16_of_quotient(rv[q].w, den, inv);
+      *reinterpret_cast<uint2*>(xo + j) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Logits for 2..64 tokens on float64 MFMA (v_mfma_f64_16x16x4f64), from the
+// bf16 x that route_norm_kernel wrote.  grid = (ceil(n_tok / 16), d / 128),
+// block = 64 * ceil(E / 16) threads.  Workgroup (m, g) owns tokens 16m.. and
+// columns 128g..; lane l of wave w feeds 32 columns of token 16m + (l & 15)
+// (columns 128g + 32 (l >> 4) + [0, 32)) as the A operand and the same
+// columns of router row 16w + (l & 15) as the B operand.  MFMA step s takes
+// offset s of every lane's run, so the four k of a step are 32 columns apart.
+// The bf16 products are exact and the 128 of them are summed in float64; the
+// partial logits of the column group go to partial[g][t][e], and the top-k
+// kernel adds the d / 128 partials in order, then the bias.
+// ---------------------------------------------------------------------------
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(1024) void route_logits_mfma_kernel(RouteArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d = a.d, t0 = blockIdx.x * 16, k0 = blockIdx.y * kRouteGroupCols;
+  const int nt = min(16, a.n_tok - t0);
+  const int j = lane & 15, kq = lane >> 4;
+  const int e = wave * 16 + j;
+  const bool tok_ok = j < nt;
+  uint4 wv[4], xv[4];
+  const uint16_t* wrow = a.w_router + (size_t)(e < a.E ? e : 0) * d + k0 + 32 * kq;
+  const uint16_t* xrow = a.x_out + (size_t)(t0 + (tok_ok ? j : 0)) * d + k0 + 32 * kq;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    wv[q] = e < a.E ? *reinterpret_cast<const uint4*>(wrow + 8 * q) : make_uint4(0, 0, 0, 0);
+    xv[q] = tok_ok ? *reinterpret_cast<const uint4*>(xrow + 8 * q) : make_uint4(0, 0, 0, 0);
+  }
+  const uint32_t xb[16] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w,
+                           xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
+  const uint32_t wb[16] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
+                           wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w};
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    const double xa = (double)bf16_to_f32((xb[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+    const double wbv = (double)bf16_to_f32((wb[s >> 1] >> (16 * (s & 1))) & 0xFFFFu);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa, wbv, acc, 0, 0, 0);
+  }
+  // D layout (measured): lane l, register r holds row 4 r + (l >> 4) (token),
+  // column l & 15 (expert)
+  double* out = a.partial + (size_t)blockIdx.y * a.n_tok * a.E;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tt = 4 * r + kq;
+    if (tt < nt && e < a.E) out[(size_t)(t0 + tt) * a.E + e] = acc[r];
+  }
+}
+
 // Top-k for each token: one workgroup of 1024 threads per token (the rank
 // count is spread over 8 slices of the experts).  Optionally also publishes the
 // selected blob pointers from the layer's table and copies of the routing.
@@ -241,7 +329,23 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(TopkArgs a) {
   __shared__ TopkShared tk;
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < a.E) {  // a NaN logit (from a non-finite residual) ranks as -inf
-    const double l = a.logits[(size_t)t * a.E + tid];
+    double l;
+    if (a.groups > 0) {  // the partials in order, eight loads in flight at a time
+      const double* p = a.partial + (size_t)t * a.E + tid;
+      const size_t step = (size_t)a.n_tok * a.E;
+      l = 0.0;
+      for (int g0 = 0; g0 < a.groups; g0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = g0 + u < a.groups ? p[(size_t)(g0 + u) * step] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (g0 + u < a.groups) l = (g0 + u == 0) ? v[u] : l + v[u];
+      }
+      if (a.bias) l += (double)a.bias[tid];
+    } else {
+      l = a.logits[(size_t)t * a.E + tid];
+    }
     tk.log[tid] = l == l ? l : -__builtin_inf();
   }
   __syncthreads();
@@ -257,20 +361,22 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(TopkArgs a) {
   }
 }
 
-hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s, int* groups) {
   const int eb = (a.E + 3) / 4;
-  // tokens per workgroup: the normalised inputs of TB tokens live in LDS
-  if (a.n_tok == 1 && a.d % 1024 == 0) {
+  *groups = 0;
+  if (a.n_tok >= 2) {  // d % 128 == 0 and E <= 256 are checked with the dims
+    if (!a.partial || !a.x_out || a.d % kRouteGroupCols || a.d > 1024 * kRouteMaxR || a.E > 256 ||
+        a.n_tok > 64)
+      return hipErrorInvalidValue;
+    *groups = a.d / kRouteGroupCols;
+    hipLaunchKernelGGL(route_norm_kernel, dim3(a.n_tok), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(route_logits_mfma_kernel, dim3((a.n_tok + 15) / 16, *groups), dim3(64 * ((a.E + 15) / 16)),
+                       0, s, a);
+  } else if (a.n_tok == 1 && a.d % 1024 == 0) {
     hipLaunchKernelGGL(route_logits_decode_kernel, dim3((a.E + kRouteDecRowsPerWG - 1) / kRouteDecRowsPerWG),
                        dim3(256), 0, s, a);
-  } else if (a.n_tok <= 1) {
-    hipLaunchKernelGGL(route_logits_kernel<1>, dim3(eb, a.n_tok), dim3(256), (size_t)a.d * 2, s, a);
-  } else if (a.d > 4096) {
-    hipLaunchKernelGGL(route_logits_kernel<2>, dim3(eb, (a.n_tok + 1) / 2), dim3(256), (size_t)a.d * 2 * 2,
-                       s, a);
   } else {
-    hipLaunchKernelGGL(route_logits_kernel<4>, dim3(eb, (a.n_tok + 3) / 4), dim3(256), (size_t)a.d * 2 * 4,
-                       s, a);
+    hipLaunchKernelGGL(route_logits_kernel<1>, dim3(eb, a.n_tok), dim3(256), (size_t)a.d * 2, s, a);
   }
   return hipGetLastError();
 }
