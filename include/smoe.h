@@ -112,7 +112,8 @@ int smoe_workspace_bytes(const smoe_dims* dims, int32_t max_tokens, size_t* byte
  * Logits are accumulated in float64 (each bf16*bf16 product is exact); for
  * 2..64 tokens on float64 MFMA, as d_model / 128 partial sums added in a fixed
  * order.  A NaN logit (from a non-finite residual) ranks as -inf.
- * 0 <= n_tok <= 64; n_tok == 0 does nothing.  Pointers 16-byte aligned. */
+ * 0 <= n_tok <= 64; n_tok == 0 does nothing (and accepts NULL buffers).
+ * Pointers 16-byte aligned. */
 int smoe_route(const smoe_dims* dims, int32_t n_tok, const float* residual, uint16_t* x_out,
                const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w,
                void* workspace, size_t workspace_bytes, void* stream);
@@ -145,6 +146,7 @@ int smoe_moe_decode_slots(const smoe_dims* dims, const uint16_t* x, const float*
  * from layer to layer.  Three kernels per layer (router logits; top-k +
  * gate/up + SwiGLU; down + combine), no host synchronisation; capturable into
  * a HIP graph.  Results are bitwise equal to the per-layer calls.
+ * n_layers == 0 does nothing (and accepts NULL buffers).
  *   residual       device fp32 [d_model], updated in place
  *   w_router       device bf16 [n_layers][E][d_model]
  *   bias           device fp32 [n_layers][E] or NULL

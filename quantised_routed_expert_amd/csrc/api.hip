@@ -132,13 +132,13 @@ int smoe_route(const smoe_dims* d, int32_t n_tok, const float* residual, uint16_
   if (int e = check_dims(d)) return e;
   if (n_tok < 0 || n_tok > kMaxPrefillTokens)
     return fail(SMOE_EINVAL, "n_tok=%d must be in [0, %d]", n_tok, kMaxPrefillTokens);
+  if (n_tok == 0) return SMOE_OK;  // nothing to route; the buffers may be NULL
   if (!residual || !x_out || !w_router || !topk_idx || !topk_w)
     return fail(SMOE_EINVAL, "NULL tensor argument");
   if (!aligned16(residual) || !aligned16(x_out) || !aligned16(w_router))
     return fail(SMOE_EINVAL, "residual, x_out and w_router must be 16-byte aligned");
   Workspace L;
   if (int e = check_ws(d, n_tok, ws, ws_bytes, &L)) return e;
-  if (n_tok == 0) return SMOE_OK;
   hipStream_t s = (hipStream_t)stream;
   double* logits = reinterpret_cast<double*>((char*)ws + L.logits);
   double* partial = reinterpret_cast<double*>((char*)ws + L.plog);
@@ -220,6 +220,7 @@ int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, co
   g_err[0] = 0;
   if (int e = check_dims(d)) return e;
   if (n_layers < 0) return fail(SMOE_EINVAL, "n_layers=%d < 0", n_layers);
+  if (n_layers == 0) return SMOE_OK;  // nothing to run; the buffers may be NULL
   if (!residual || !w_router || !expert_tables) return fail(SMOE_EINVAL, "NULL tensor argument");
   if (!aligned16(residual) || !aligned16(w_router) || (x_rec && !aligned16(x_rec)))
     return fail(SMOE_EINVAL, "residual, w_router and x_rec must be 16-byte aligned");

@@ -1,0 +1,95 @@
+"""GPU edge cases through the C ABI: empty calls, and every size bound of the
+layer at its maximum (d_model 8192, d_ff 8192, 256 experts with k = 16),
+each against the CPU oracle.  Each bound is taken with small other sizes so
+that the float64 oracle stays quick."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantised_routed_expert_amd as smoe
+import synth
+from synth.device import DeviceStack
+from tests.gpu_common import LazyExperts, check_moe_output, need_gpu, random_residual, say
+from tests.test_gpu_decode import _decode_one_layer
+from tests.test_gpu_prefill import check_union, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    torch.cuda.init()
+
+
+def test_route_zero_tokens_writes_nothing():
+    dims = synth.Dims(256, 128, 16, 4, 32)
+    stack = DeviceStack(1337, dims, 1)
+    r = torch.zeros((1, dims.d_model), device="cuda")
+    x = torch.full((1, dims.d_model), -3, dtype=torch.int16, device="cuda")
+    idx = torch.full((1, dims.top_k), -5, dtype=torch.int32, device="cuda")
+    w = torch.full((1, dims.top_k), -7.0, dtype=torch.float32, device="cuda")
+    smoe.route(dims, r[:0], x[:0], stack.router_layer(0), None, idx[:0], w[:0], smoe.workspace(dims, 1))
+    torch.cuda.synchronize()
+    assert bool((x == -3).all()) and bool((idx == -5).all()) and bool((w == -7.0).all())
+
+
+def test_decode_layers_zero_layers_leaves_the_residual():
+    dims = synth.Dims(256, 128, 16, 4, 32)
+    stack = DeviceStack(1337, dims, 1)
+    h = random_residual(np.random.default_rng(3), 1, dims.d_model)[0]
+    r = torch.from_numpy(h.copy()).cuda()
+    smoe.decode_layers(dims, 0, r, stack.router, None, stack.tables, smoe.workspace(dims, 1))
+    torch.cuda.synchronize()
+    assert np.array_equal(r.cpu().numpy(), h)
+
+
+BOUNDS = {
+    "d_model_8192": synth.Dims(8192, 256, 32, 4, 32),
+    "d_ff_8192": synth.Dims(256, 8192, 16, 4, 64),
+    "e256_k16": synth.Dims(512, 256, 256, 16, 32),
+}
+
+
+@pytest.mark.parametrize("name", list(BOUNDS))
+def test_size_bound_decode_matches_oracle(name):
+    dims = BOUNDS[name]
+    say(f"[bound] decode {name}: {dims}")
+    stack = DeviceStack(1337, dims, 1)
+    experts = LazyExperts(1337, dims, 0)
+    rng = np.random.default_rng(17)
+    for t in range(2):
+        res = random_residual(rng, 1, dims.d_model, scale=1.5)[0]
+        xb, ig, wg, r_out = _decode_one_layer(dims, stack, 0, res)
+        ref = oracle.moe_layer(res.astype(np.float64), stack.router_bits[0], experts, dims)
+        assert np.array_equal(xb, ref["x_bits"])
+        assert list(ig) == ref["idx"]
+        assert np.allclose(wg, ref["w"], rtol=2e-6, atol=1e-7)
+        check_moe_output(r_out.astype(np.float64) - res.astype(np.float64), ref["y"], f"{name} t{t}")
+    # the chained entry point (selection inside the gate/up kernel) agrees bit for bit
+    r = torch.from_numpy(res.copy()).cuda()
+    i_rec = torch.empty((1, dims.top_k), dtype=torch.int32, device="cuda")
+    smoe.decode_layers(dims, 1, r, stack.router, None, stack.tables, smoe.workspace(dims, 1), None, i_rec, None)
+    torch.cuda.synchronize()
+    assert i_rec.cpu().numpy()[0].tolist() == list(ig)
+    assert np.array_equal(r.cpu().numpy(), r_out)
+
+
+@pytest.mark.parametrize("name,T,sample", [("d_model_8192", 20, [0, 7, 19]), ("d_ff_8192", 33, [0, 16, 32]),
+                                           ("e256_k16", 64, [0, 21, 42, 63])])
+def test_size_bound_prefill_matches_oracle(name, T, sample):
+    dims = BOUNDS[name]
+    say(f"[bound] prefill {name}: T={T}")
+    stack = DeviceStack(1337, dims, 1)
+    res = random_residual(np.random.default_rng(T), T, dims.d_model, scale=1.5)
+    got = run_prefill(dims, stack, 0, res)
+    n_union = check_union(got, T, dims.top_k)
+    say(f"[bound] |union| = {n_union}")
+    experts = LazyExperts(1337, dims, 0)
+    for t in sample:
+        ref = oracle.moe_layer(res[t].astype(np.float64), stack.router_bits[0], experts, dims)
+        assert got["idx"][t].tolist() == ref["idx"], f"token {t}"
+        assert np.allclose(got["w"][t], ref["w"], rtol=2e-6, atol=1e-7)
+        y = got["r_out"][t].astype(np.float64) - res[t].astype(np.float64)
+        check_moe_output(y, ref["y"], f"{name} t{t}")
