@@ -200,10 +200,11 @@ int smoe_moe_prefill_chunk(const smoe_dims* dims, int32_t n_tok, const uint16_t*
 typedef struct smoe_ring smoe_ring;
 
 typedef struct {
-  int32_t n_slots;        /* 64..4096 (the pages' clamp), >= k              */
+  int32_t n_slots;        /* 64..4096 (the pages' clamp), >= top_k          */
   int32_t n_layers;       /* >= 1                                          */
   int32_t n_experts;      /* E                                             */
-  int32_t top_k;          /* k                                             */
+  int32_t top_k;          /* k of a decode step (validated; an acquisition
+                             may hold up to min(E, n_slots) experts)       */
   size_t slot_bytes;      /* bytes copied per fill (the blob size)         */
   size_t slot_stride;     /* distance between slots in slab_dev (>= bytes) */
   const void* const* vault_layers; /* host array [n_layers] of host pointers:
@@ -231,14 +232,27 @@ typedef struct {
 
 int smoe_ring_create(const smoe_ring_desc* desc, smoe_ring** out);
 
-/* Acquire the k experts of `layer` (host array, rank order).  Drops the
- * previous acquisition's holds first (an implicit release).  On return
- * slot_ptrs_host[r] is the device blob pointer for rank r, and compute_stream
- * will not run later work until the fills are complete.  Errors: SMOE_EINVAL
- * (layer, k or an expert out of range, an expert twice), SMOE_ENOSLOT (every
- * slot held), SMOE_EHIP (a copy or event call failed). */
+/* Acquire k experts of `layer` (host array, in request order): a decode
+ * step's k routed experts in rank order, or a prefill chunk's expert union in
+ * first-touch order (1 <= k <= min(E, n_slots)).  Drops the previous
+ * acquisition's holds first (an implicit release).  Fills are issued in
+ * request order.  On return slot_ptrs_host[r] is the device blob pointer of
+ * request r, and compute_stream will not run later work until the fills are
+ * complete.  Errors: SMOE_EINVAL (layer, k or an expert out of range, an
+ * expert twice), SMOE_ENOSLOT (every slot held), SMOE_EHIP (a copy or event
+ * call failed). */
 int smoe_ring_acquire(smoe_ring* ring, int32_t layer, const int32_t* experts_host, int32_t k,
                       const void** slot_ptrs_host, void* compute_stream);
+
+/* smoe_ring_acquire, then the layer's expert table for the kernels that find
+ * blobs through one ("Prefill Reads Each Expert Once"; ring-backed prefill):
+ * table_dev (device, [E] blob pointers, caller-owned) gets the slot pointer of
+ * every requested expert and NULL for every other one, written by a kernel on
+ * compute_stream after the fills' waits (stream-ordered; the pointers travel
+ * as kernel arguments, so no host buffer must outlive the call).  Errors as
+ * smoe_ring_acquire, plus SMOE_EINVAL for a NULL or unaligned table_dev. */
+int smoe_ring_acquire_table(smoe_ring* ring, int32_t layer, const int32_t* experts_host, int32_t k,
+                            void* table_dev, void* compute_stream);
 
 /* Drop the current holds (the slots stay resident for later hits). */
 int smoe_ring_release(smoe_ring* ring);

@@ -20,7 +20,7 @@ EXPORTED = [
     "smoe_last_error", "smoe_version", "smoe_q4_blob_bytes", "smoe_q4_blob_stride",
     "smoe_workspace_bytes", "smoe_route", "smoe_moe_decode", "smoe_moe_decode_slots",
     "smoe_decode_layers", "smoe_moe_prefill_chunk", "smoe_ring_create", "smoe_ring_acquire",
-    "smoe_ring_release", "smoe_ring_stats", "smoe_ring_log", "smoe_ring_destroy",
+    "smoe_ring_release", "smoe_ring_stats", "smoe_ring_log", "smoe_ring_destroy", "smoe_ring_acquire_table",
 ]
 
 
@@ -77,6 +77,7 @@ def lib():
             "smoe_ring_create": (I, [P(SmoeRingDesc), P(VP)]),
             "smoe_ring_acquire": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, P(VP), VP]),
             "smoe_ring_release": (I, [VP]),
+            "smoe_ring_acquire_table": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, VP, VP]),
             "smoe_ring_stats": (I, [VP, P(ctypes.c_uint64), P(ctypes.c_uint64), P(ctypes.c_uint64),
                                     P(ctypes.c_uint64)]),
             "smoe_ring_log": (I, [VP, P(SmoeRingEvent), S, P(S)]),
@@ -195,6 +196,12 @@ class Ring:
         out = (ctypes.c_void_p * len(experts))()
         _check(lib().smoe_ring_acquire(self.h, int(layer), ex, len(experts), out, _stream(stream)))
         return [int(p) for p in out]
+
+    def acquire_table(self, layer, experts, table, stream=None):
+        """Acquire ``experts`` (request order) and write the layer's [E] device
+        table of blob pointers (NULL for the experts not requested)."""
+        ex = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
+        _check(lib().smoe_ring_acquire_table(self.h, int(layer), ex, len(experts), _ptr(table), _stream(stream)))
 
     def release(self):
         _check(lib().smoe_ring_release(self.h))

@@ -228,6 +228,12 @@ struct TopkArgs {
 };
 hipError_t launch_route_topk(const TopkArgs& a, int n_tok, hipStream_t s);
 
+// A layer's expert table, passed by value (2 KiB of kernel arguments).
+struct RingTable {
+  const void* ptr[kMaxExperts];
+};
+hipError_t launch_ring_table(const RingTable& t, const void** table, int E, hipStream_t s);
+
 // Where the k experts of a decode step come from.
 struct ExpertSource {
   const int32_t* idx;               // [k] device (rank order), used when direct[0] == null

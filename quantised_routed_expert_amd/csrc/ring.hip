@@ -27,6 +27,20 @@ int fail(int code, const char* fmt, ...);
 }
 using smoe::fail;
 
+namespace smoe {
+
+// Writes a layer's [E] expert table from pointers passed by value.
+__global__ __launch_bounds__(256) void ring_table_kernel(RingTable t, const void** table, int E) {
+  if ((int)threadIdx.x < E) table[threadIdx.x] = t.ptr[threadIdx.x];
+}
+
+hipError_t launch_ring_table(const RingTable& t, const void** table, int E, hipStream_t s) {
+  hipLaunchKernelGGL(ring_table_kernel, dim3(1), dim3(256), 0, s, t, table, E);
+  return hipGetLastError();
+}
+
+}  // namespace smoe
+
 struct smoe_ring {
   smoe_ring_desc desc;
   std::vector<long long> key;      // per slot: layer * E + expert, or -1 when empty
@@ -106,7 +120,8 @@ int smoe_ring_acquire(smoe_ring* r, int32_t layer, const int32_t* experts, int32
   if (!r || !experts || !slot_ptrs) return fail(SMOE_EINVAL, "NULL argument");
   const smoe_ring_desc& d = r->desc;
   if (layer < 0 || layer >= d.n_layers) return fail(SMOE_EINVAL, "layer=%d out of range", layer);
-  if (k < 1 || k > d.top_k) return fail(SMOE_EINVAL, "k=%d must be in [1, %d]", k, d.top_k);
+  const int kmax = d.n_experts < d.n_slots ? d.n_experts : d.n_slots;
+  if (k < 1 || k > kmax) return fail(SMOE_EINVAL, "k=%d must be in [1, %d]", k, kmax);
   for (int i = 0; i < k; ++i) {
     if (experts[i] < 0 || experts[i] >= d.n_experts) return fail(SMOE_EINVAL, "expert %d out of range", experts[i]);
     for (int j = 0; j < i; ++j)
@@ -174,6 +189,21 @@ int smoe_ring_acquire(smoe_ring* r, int32_t layer, const int32_t* experts, int32
     he = hipStreamWaitEvent(cs, r->fill_done[s], 0);
     if (he != hipSuccess) return hip_err(he, "hipStreamWaitEvent");
   }
+  return SMOE_OK;
+}
+
+int smoe_ring_acquire_table(smoe_ring* r, int32_t layer, const int32_t* experts, int32_t k, void* table_dev,
+                            void* compute_stream) {
+  if (!r || !experts) return fail(SMOE_EINVAL, "NULL argument");
+  if (!table_dev || ((uintptr_t)table_dev & 7u)) return fail(SMOE_EINVAL, "table_dev must be 8-byte aligned");
+  smoe::RingTable t;
+  memset(&t, 0, sizeof(t));
+  std::vector<const void*> ptrs((size_t)(k > 0 ? k : 1));
+  if (int e = smoe_ring_acquire(r, layer, experts, k, ptrs.data(), compute_stream)) return e;
+  for (int i = 0; i < k; ++i) t.ptr[experts[i]] = ptrs[i];
+  const hipError_t he = smoe::launch_ring_table(t, reinterpret_cast<const void**>(table_dev), r->desc.n_experts,
+                                                (hipStream_t)compute_stream);
+  if (he != hipSuccess) return hip_err(he, "expert table launch");
   return SMOE_OK;
 }
 

@@ -1,6 +1,7 @@
 """The HBM expert ring on the GPU: its hit/miss/eviction log must equal the
-oracle's LRU simulation of the same routing trace, and ring-backed decode must
-be bitwise equal to decode with every expert resident."""
+oracle's LRU simulation of the same routing trace, and ring-backed decode and
+ring-backed prefill must be bitwise equal to the same work with every expert
+resident."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import oracle
 import quantised_routed_expert_amd as smoe
 import synth
 from synth.device import DeviceStack, router_stack, u16_to_device
-from tests.gpu_common import need_gpu, say
+from tests.gpu_common import need_gpu, random_residual, say
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +179,85 @@ def test_ring_lru_at_full_scale_with_markov_routing():
         xv, _ = oracle.rmsnorm_bf16(hidden[L, t].cpu().numpy().astype(np.float64), dims.rms_eps)
         ref_idx, _ = oracle.select_topk(oracle.router_logits(synth.router_bits(1337, dims, L), xv), k)
         assert routing[t][L] == ref_idx
+
+
+def prefill_layers(dims, stack, chunk, ring=None):
+    """Layer-major prefill of one chunk through every layer of the stack, each
+    layer fed the chunk's own residual (as the prefill workload does).  With a
+    ring, each layer's expert union is acquired in first-touch order and the
+    GEMMs find the blobs through the ring's table.  Returns the per-layer
+    outputs and unions."""
+    T = chunk.shape[0]
+    E, k = dims.n_experts, dims.top_k
+    ws = smoe.workspace(dims, T)
+    x = torch.empty((T, dims.d_model), dtype=torch.int16, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    mu = min(E, T * k)
+    uids = torch.empty(mu, dtype=torch.int32, device="cuda")
+    ucount = torch.zeros(1, dtype=torch.int32, device="cuda")
+    offs = torch.empty(mu + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    table = torch.empty(E, dtype=torch.int64, device="cuda")
+    outs, unions = [], []
+    for L in range(stack.n_layers):
+        r = torch.from_numpy(chunk.copy()).cuda()
+        smoe.route(dims, r, x, stack.router_layer(L), stack.bias_layer(L), idx, w, ws)
+        union = oracle.expert_union(idx.cpu().numpy().tolist())[0]   # synchronises with the router
+        unions.append(union)
+        if ring is None:
+            tab = stack.table(L)
+        else:
+            ring.acquire_table(L, union, table)
+            tab = table
+        smoe.moe_prefill_chunk(dims, x, idx, w, tab, r, uids, ucount, offs, perm, ws)
+        torch.cuda.synchronize()
+        assert uids.cpu().numpy()[: int(ucount.item())].tolist() == union
+        outs.append(r.cpu().numpy())
+    return outs, unions
+
+
+@pytest.mark.parametrize("n_slots", [64, 150])
+def test_ring_backed_prefill_matches_resident_and_oracle_log(n_slots):
+    """Ring-backed layer-major prefill: acquisitions are whole chunk unions
+    (up to min(E, n_slots) experts, fills issued in first-touch order)."""
+    dims = synth.Dims(256, 128, 64, 4, 32)
+    n_layers, T = 4, 20
+    stack = DeviceStack(1337, dims, n_layers, zipf_s=1.1)
+    rng = np.random.default_rng(5)
+    chunks = [random_residual(rng, T, dims.d_model, scale=1.5) for _ in range(3)]
+    ring, keep = make_ring(dims, stack, n_slots)
+    ref = oracle.LruRing(n_slots)
+    ref_events = []
+    for c, chunk in enumerate(chunks):
+        got, unions = prefill_layers(dims, stack, chunk, ring)
+        want, unions_res = prefill_layers(dims, stack, chunk)
+        assert unions == unions_res
+        for L in range(n_layers):
+            assert np.array_equal(got[L], want[L]), f"chunk {c} layer {L}"
+            ref.release()
+            ref_events.extend(ref.acquire(L, unions[L]))
+    log = ring.log(1 << 20)
+    stats = ring.stats()
+    ring.release()
+    ring.destroy()
+    assert log == ref_events
+    assert (stats["hits"], stats["misses"], stats["evictions"]) == (ref.hits, ref.misses, ref.evictions)
+    assert stats["h2d_bytes"] == ref.misses * stack.blob_bytes
+    say(f"[ring-prefill] slots={n_slots}: unions {[len(u) for u in unions]}, hits {ref.hits} misses {ref.misses} "
+        f"evictions {ref.evictions}")
+
+
+def test_ring_acquire_table_rejects_oversized_unions():
+    dims = synth.Dims(256, 128, 128, 8, 32)
+    stack = DeviceStack(1337, dims, 1)
+    ring, keep = make_ring(dims, stack, 64)
+    table = torch.empty(dims.n_experts, dtype=torch.int64, device="cuda")
+    with pytest.raises(smoe.SmoeError):
+        ring.acquire_table(0, list(range(65)), table)   # more experts than slots
+    ring.acquire_table(0, list(range(64)), table)       # a full ring is fine
+    torch.cuda.synchronize()
+    t = table.cpu().numpy()
+    assert (t[:64] != 0).all() and (t[64:] == 0).all()
+    ring.release()
+    ring.destroy()
