@@ -408,26 +408,18 @@ def bench_prefill(args):
     print(json.dumps(out), flush=True)
 
 
-def bench_ring(args):
-    """Decode with a 1536-slot HBM ring over a vault in pinned host memory.
-    Each layer's router input follows its own Markov chain over tokens
-    (h_t = 0.7 h_{t-1} + 0.3 z_t), so consecutive tokens share part of their
-    experts; the residual update of each layer is computed and discarded."""
-    wl = synth.CONFIGS[4]
+def host_vault(wl, args):
+    """The expert vault in host memory, one allocation per layer, drawn on the
+    device and copied down.  Layers are page-locked (hipHostMalloc) up to
+    --pinned-gib; the driver caps page-locked memory (64 GiB on the MI355X
+    hosts measured), so the rest of a 128 GB vault stays pageable and its fills
+    are staged by the HIP runtime.  Returns (pinned buffers, per-layer views,
+    number of page-locked layers)."""
+    from synth.device import fill_experts
     dims = wl.dims
     E, NL = dims.n_experts, wl.n_layers
-    torch.cuda.set_device(0)
-    off = synth.blob_sections(dims)
-    stride = off["stride"]
+    stride = synth.blob_sections(dims)["stride"]
     t0 = time.time()
-    from synth.device import fill_experts, router_stack, u16_to_device
-    # the vault: one host allocation per layer, drawn on the device and copied
-    # down.  Layers are page-locked (hipHostMalloc) up to --pinned-gib; the
-    # driver caps page-locked memory (64 GiB on the MI355X hosts measured), so
-    # the rest of a 128 GB vault stays pageable and its fills are staged by
-    # the HIP runtime.
-    link = h2d_references()
-    log(f"host link: pinned H2D {link['pinned_h2d_gbps']:.1f} GB/s, pageable H2D {link['pageable_h2d_gbps']:.1f} GB/s")
     pinned_budget = int(args.pinned_gib * (1 << 30))
     vault, views = [], []
     for L in range(NL):
@@ -443,13 +435,32 @@ def bench_ring(args):
         else:
             views.append(torch.empty(E * stride, dtype=torch.uint8))
     n_pinned = len(vault)
-    log(f"vault: {n_pinned} of {NL} layers page-locked ({n_pinned * E * stride / 1e9:.1f} GB) "
-        f"in {time.time() - t0:.1f} s")
     stage = torch.empty(E * stride, dtype=torch.uint8, device="cuda")
     for L in range(NL):
         fill_experts(wl.seed, dims, L, 0, E, stage.data_ptr(), stride)
         views[L].copy_(stage)
     del stage
+    log(f"vault: {n_pinned} of {NL} layers page-locked ({n_pinned * E * stride / 1e9:.1f} GB), "
+        f"drawn in {time.time() - t0:.1f} s")
+    return vault, views, n_pinned
+
+
+def bench_ring(args):
+    """Decode with a 1536-slot HBM ring over a vault in pinned host memory.
+    Each layer's router input follows its own Markov chain over tokens
+    (h_t = 0.7 h_{t-1} + 0.3 z_t), so consecutive tokens share part of their
+    experts; the residual update of each layer is computed and discarded."""
+    wl = synth.CONFIGS[4]
+    dims = wl.dims
+    E, NL = dims.n_experts, wl.n_layers
+    torch.cuda.set_device(0)
+    off = synth.blob_sections(dims)
+    stride = off["stride"]
+    t0 = time.time()
+    from synth.device import router_stack, u16_to_device
+    link = h2d_references()
+    log(f"host link: pinned H2D {link['pinned_h2d_gbps']:.1f} GB/s, pageable H2D {link['pageable_h2d_gbps']:.1f} GB/s")
+    vault, views, n_pinned = host_vault(wl, args)
     router = u16_to_device(router_stack(wl.seed, dims, NL))
     keep, fresh = wl.markov
     W, K = args.warmup, args.steps
@@ -518,6 +529,127 @@ def bench_ring(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_ring_prefill(args):
+    """Layer-major prefill through the 1536-slot HBM ring over the host vault:
+    the 512-token prompt in chunks of 64 with the Zipf(1.1) logit bias, every
+    layer fed the prompt (as the prefill workload does).  Per chunk and layer
+    the routing is read back, the expert union is acquired in first-touch
+    order (its fills go out on the copy stream in that order, the first-touched
+    expert first) and the grouped GEMMs find the blobs through the ring's
+    expert table.  One warm-up prompt fills the ring; the timed prompts follow.
+
+    Two schedules, same results: ``value`` takes the chunks in turn, each
+    through all layers (the pages' order: a union is read once per chunk);
+    ``layer_outer`` takes the layers in turn, each over all chunks, so that a
+    layer's union is loaded once and the later chunks hit it in the ring."""
+    from synth.device import router_stack, u16_to_device
+    wl = synth.CONFIGS[3]
+    dims = wl.dims
+    E, NL, k = dims.n_experts, wl.n_layers, dims.top_k
+    T, C = wl.steps, wl.prefill_chunk
+    n_chunks = T // C
+    n_slots = synth.CONFIGS[4].ring_slots
+    torch.cuda.set_device(0)
+    off = synth.blob_sections(dims)
+    stride = off["stride"]
+    link = h2d_references()
+    log(f"host link: pinned H2D {link['pinned_h2d_gbps']:.1f} GB/s, pageable H2D {link['pageable_h2d_gbps']:.1f} GB/s")
+    vault, views, n_pinned = host_vault(wl, args)
+    router = u16_to_device(router_stack(wl.seed, dims, NL))
+    bias = torch.from_numpy(np.stack([synth.gen.zipf_bias(wl.seed, dims, L, wl.zipf_s) for L in range(NL)])).cuda()
+    prompt = torch.from_numpy(np.stack([synth.hidden_bf16(wl.seed, 20_000 + t, dims.d_model)
+                                        for t in range(T)])).cuda()
+    resid = torch.empty_like(prompt)
+    slab = torch.empty(n_slots * stride, dtype=torch.uint8, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    ring = smoe.Ring(n_slots, NL, E, k, off["bytes"], stride, [v.data_ptr() for v in views], stride,
+                     slab.data_ptr(), copy_stream, 0)
+    ws = smoe.workspace(dims, C)
+    x = torch.empty((C, dims.d_model), dtype=torch.int16, device="cuda")
+    idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, k), dtype=torch.float32, device="cuda")
+    idx_host = torch.empty((C, k), dtype=torch.int32, pin_memory=True)
+    mu = min(E, C * k)
+    uids = torch.empty(mu, dtype=torch.int32, device="cuda")
+    ucount = torch.zeros(1, dtype=torch.int32, device="cuda")
+    offs = torch.empty(mu + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(C * k, dtype=torch.int32, device="cuda")
+    table = torch.empty(E, dtype=torch.int64, device="cuda")
+    unions = []
+
+    def chunk_layer(c, L):
+        r = resid[c * C:(c + 1) * C]
+        r.copy_(prompt[c * C:(c + 1) * C])
+        smoe.route(dims, r, x, router[L], bias[L], idx, w, ws)
+        idx_host.copy_(idx)
+        torch.cuda.current_stream().synchronize()
+        flat = idx_host.numpy().reshape(-1)              # entry t * k + r
+        first = np.unique(flat, return_index=True)[1]
+        union = flat[np.sort(first)].tolist()            # first-touch order
+        unions.append(len(union))
+        ring.acquire_table(L, union, table)
+        smoe.moe_prefill_chunk(dims, x, idx, w, table, r, uids, ucount, offs, perm, ws)
+
+    def prompt_run(tag, order):
+        if order == "chunk":
+            for c in range(n_chunks):
+                for L in range(NL):
+                    chunk_layer(c, L)
+                torch.cuda.synchronize()
+                log(f"{tag}: chunk {c + 1}/{n_chunks} done")
+        else:
+            for L in range(NL):
+                for c in range(n_chunks):
+                    chunk_layer(c, L)
+                if L % 16 == 15 or L == NL - 1:
+                    torch.cuda.synchronize()
+                    log(f"{tag}: layer {L + 1}/{NL} done")
+
+    K = args.steps
+    res = {}
+    for order in ("chunk", "layer"):
+        for i in range(args.warmup):
+            prompt_run(f"{order}-order warm-up prompt {i + 1}", order)
+        s0 = ring.stats()
+        n_u0 = len(unions)
+        t1 = time.time()
+        for i in range(K):
+            prompt_run(f"{order}-order timed prompt {i + 1}", order)
+        torch.cuda.synchronize()
+        dt = time.time() - t1
+        s1 = ring.stats()
+        hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+        h2d = s1["h2d_bytes"] - s0["h2d_bytes"]
+        res[order] = {"tok_s": K * T / dt, "ms": dt * 1000.0 / K, "mean_union": float(np.mean(unions[n_u0:])),
+                      "hit_rate": hits / max(1, hits + misses), "misses_per_prompt": misses / K,
+                      "h2d_bytes_per_prompt": h2d / K, "h2d_gbps": h2d / dt / 1e9,
+                      "h2d_frac_of_pinned": h2d / dt / 1e9 / link["pinned_h2d_gbps"]}
+        log(f"ring prefill, {order} order: {res[order]['tok_s']:.1f} prompt tokens/s, hit rate "
+            f"{res[order]['hit_rate']:.3f}, H2D {res[order]['h2d_gbps']:.1f} GB/s")
+    ring.release()
+    ring.destroy()
+    f = res["chunk"]
+    out = {
+        "metric": "ring-backed layer-major prefill prompt tokens/s (235B-shape, 512-token prompt, chunks of 64, "
+                  "1536-slot HBM ring over a host vault)",
+        "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4-affine weights dequantised to fp16, fp16 MFMA with fp32 accumulation; float64 router",
+        "data": "synthetic (Zipf(1.1) logit bias, N(0,1) bf16 prompt hidden states fed to every layer)",
+        "config": {"workload": wl.name + "-ring1536", "layers": NL, "prompt_tokens": T, "chunk": C,
+                   "ring_slots": n_slots, "parallelism": "single GPU"},
+        "mean_union": f["mean_union"], "hit_rate": f["hit_rate"], "misses_per_prompt": f["misses_per_prompt"],
+        "h2d_bytes_per_prompt": f["h2d_bytes_per_prompt"], "h2d_gbps": f["h2d_gbps"],
+        "vault_layers_page_locked": n_pinned,
+        "host_link": dict(link, h2d_frac_of_pinned=f["h2d_frac_of_pinned"]),
+        "layer_outer": res["layer"],
+    }
+    del views
+    for v in vault:
+        v.free()
+    print(json.dumps(out), flush=True)
+
+
 def h2d_references(nbytes=1 << 30, reps=4):
     """Host-to-device copy rates of the ring's two vault kinds: hipMemcpyAsync
     from page-locked memory (hipHostMalloc) and from pageable memory."""
@@ -572,7 +704,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", choices=["decode", "prefill", "ring", "copy"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "prefill", "ring", "ring-prefill", "copy"], default="decode")
     ap.add_argument("--instrument-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -582,10 +714,12 @@ def main():
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
               "MI355X (the layer has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
-    defaults = {"decode": (64, 8), "prefill": (3, 1), "ring": (256, 8), "copy": (10, 2)}[args.workload]
+    defaults = {"decode": (64, 8), "prefill": (3, 1), "ring": (256, 8), "ring-prefill": (1, 1),
+                "copy": (10, 2)}[args.workload]
     args.steps = defaults[0] if args.steps is None else args.steps
     args.warmup = defaults[1] if args.warmup is None else args.warmup
-    {"decode": bench_decode, "prefill": bench_prefill, "ring": bench_ring, "copy": bench_copy}[args.workload](args)
+    {"decode": bench_decode, "prefill": bench_prefill, "ring": bench_ring, "ring-prefill": bench_ring_prefill,
+     "copy": bench_copy}[args.workload](args)
 
 
 if __name__ == "__main__":
