@@ -212,6 +212,12 @@ typedef struct {
                              Pinned (hipHostMalloc) memory gives asynchronous
                              full-rate copies; one allocation per layer keeps
                              each under the driver's pinned-allocation limit.
+                             A pageable layer is detected at create and filled
+                             through the ring's own pipeline (host threads copy
+                             each blob into one of 4 page-locked staging
+                             buffers of slot_bytes, allocated by the ring,
+                             while the previous blob's DMA runs); acquire then
+                             blocks for those host copies.
                              The array is copied at create; the memory it
                              points to must outlive the ring. */
   size_t vault_stride;

@@ -14,10 +14,18 @@
 // already enqueued on the compute stream (so no slot is overwritten while an
 // earlier kernel may still read it); after them, the compute stream waits on
 // the completion event of every slot it is handed.
+// A vault layer in page-locked memory is copied directly.  A pageable layer
+// goes through the ring's own pipeline: a pool of host threads copies the
+// blob into one of kStages page-locked staging buffers while the DMA of the
+// previous blob runs (the HIP runtime's own staging of pageable copies
+// reaches about half of the link's page-locked rate).
 #include <stdlib.h>
 #include <string.h>
 
+#include <condition_variable>
+#include <mutex>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "kernels.h"
@@ -41,6 +49,78 @@ hipError_t launch_ring_table(const RingTable& t, const void** table, int E, hipS
 
 }  // namespace smoe
 
+namespace {
+
+constexpr int kStages = 4;         // page-locked staging buffers for pageable layers
+constexpr int kCopyThreads = 8;    // host threads that fill a staging buffer
+
+// A fixed pool of host threads that copy one buffer in parallel parts.
+class CopyPool {
+ public:
+  explicit CopyPool(int n) {
+    for (int i = 0; i < n; ++i) th_.emplace_back([this, i] { run(i + 1); });
+  }
+  ~CopyPool() {
+    {
+      std::lock_guard<std::mutex> g(m_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (std::thread& t : th_) t.join();
+  }
+  // Copies `bytes` from src to dst with every pool thread and the caller.
+  void copy(char* dst, const char* src, size_t bytes) {
+    const int parts = (int)th_.size() + 1;
+    {
+      std::lock_guard<std::mutex> g(m_);
+      dst_ = dst;
+      src_ = src;
+      bytes_ = bytes;
+      parts_ = parts;
+      pending_ = (int)th_.size();
+      ++gen_;
+    }
+    cv_.notify_all();
+    part(0);
+    std::unique_lock<std::mutex> l(m_);
+    done_.wait(l, [this] { return pending_ == 0; });
+  }
+
+ private:
+  void part(int i) {
+    const size_t per = ((bytes_ + parts_ - 1) / parts_ + 63) & ~(size_t)63;
+    const size_t lo = (size_t)i * per;
+    if (lo < bytes_) memcpy(dst_ + lo, src_ + lo, (bytes_ - lo < per ? bytes_ - lo : per));
+  }
+  void run(int i) {
+    unsigned long long seen = 0;
+    for (;;) {
+      {
+        std::unique_lock<std::mutex> l(m_);
+        cv_.wait(l, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+      }
+      part(i);
+      {
+        std::lock_guard<std::mutex> g(m_);
+        if (--pending_ == 0) done_.notify_one();
+      }
+    }
+  }
+  std::vector<std::thread> th_;
+  std::mutex m_;
+  std::condition_variable cv_, done_;
+  char* dst_ = nullptr;
+  const char* src_ = nullptr;
+  size_t bytes_ = 0;
+  int parts_ = 1, pending_ = 0;
+  unsigned long long gen_ = 0;
+  bool stop_ = false;
+};
+
+}  // namespace
+
 struct smoe_ring {
   smoe_ring_desc desc;
   std::vector<long long> key;      // per slot: layer * E + expert, or -1 when empty
@@ -51,6 +131,12 @@ struct smoe_ring {
   std::vector<int> where;          // (layer * E + expert) -> slot, or -1
   std::vector<int> held;           // slots of the current acquisition
   std::vector<const char*> vault;  // per layer: host base of its blobs
+  std::vector<unsigned char> pageable;  // per layer: not page-locked (staged)
+  char* stage[kStages] = {};       // page-locked staging buffers (only with pageable layers)
+  hipEvent_t stage_done[kStages] = {};
+  unsigned char stage_used[kStages] = {};
+  int next_stage = 0;
+  CopyPool* pool = nullptr;
   hipEvent_t compute_mark;
   unsigned long long now = 0;
   int n_filled = 0;                // empty slots are exactly [n_filled, n_slots)
@@ -86,7 +172,16 @@ int smoe_ring_create(const smoe_ring_desc* d, smoe_ring** out) {
   r->desc = *d;
   r->desc.vault_layers = nullptr;  // the caller's array need not outlive create
   r->vault.resize((size_t)d->n_layers);
-  for (int L = 0; L < d->n_layers; ++L) r->vault[L] = (const char*)d->vault_layers[L];
+  r->pageable.assign((size_t)d->n_layers, 0);
+  bool any_pageable = false;
+  for (int L = 0; L < d->n_layers; ++L) {
+    r->vault[L] = (const char*)d->vault_layers[L];
+    hipPointerAttribute_t at;
+    const hipError_t pe = hipPointerGetAttributes(&at, d->vault_layers[L]);
+    if (pe != hipSuccess) (void)hipGetLastError();  // unregistered host memory
+    r->pageable[L] = !(pe == hipSuccess && at.type == hipMemoryTypeHost);
+    any_pageable |= r->pageable[L] != 0;
+  }
   const size_t n = (size_t)d->n_slots;
   r->key.assign(n, -1);
   r->tick.assign(n, 0);
@@ -97,12 +192,25 @@ int smoe_ring_create(const smoe_ring_desc* d, smoe_ring** out) {
   r->log.reserve(d->log_capacity);
   hipError_t e = hipEventCreateWithFlags(&r->compute_mark, hipEventDisableTiming);
   for (size_t i = 0; e == hipSuccess && i < n; ++i) e = hipEventCreateWithFlags(&r->fill_done[i], hipEventDisableTiming);
+  for (int i = 0; e == hipSuccess && any_pageable && i < kStages; ++i) {
+    e = hipEventCreateWithFlags(&r->stage_done[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipHostMalloc((void**)&r->stage[i], d->slot_bytes, hipHostMallocDefault);
+  }
+  if (e == hipSuccess && any_pageable) {
+    r->pool = new (std::nothrow) CopyPool(kCopyThreads);
+    if (!r->pool) e = hipErrorOutOfMemory;
+  }
   if (e != hipSuccess) {
     for (hipEvent_t ev : r->fill_done)
       if (ev) (void)hipEventDestroy(ev);
+    for (int i = 0; i < kStages; ++i) {
+      if (r->stage_done[i]) (void)hipEventDestroy(r->stage_done[i]);
+      if (r->stage[i]) (void)hipHostFree(r->stage[i]);
+    }
     if (r->compute_mark) (void)hipEventDestroy(r->compute_mark);
+    delete r->pool;
     delete r;
-    return hip_err(e, "hipEventCreate");
+    return hip_err(e, "ring set-up (events, staging buffers)");
   }
   *out = r;
   return SMOE_OK;
@@ -168,7 +276,20 @@ int smoe_ring_acquire(smoe_ring* r, int32_t layer, const int32_t* experts, int32
       r->where[kk] = s;
       const char* src = r->vault[layer] + (size_t)experts[rank] * d.vault_stride;
       char* dst = (char*)d.slab_dev + (size_t)s * d.slot_stride;
-      he = hipMemcpyAsync(dst, src, d.slot_bytes, hipMemcpyHostToDevice, ps);
+      if (r->pageable[layer]) {
+        // host copy into a free staging buffer while earlier DMAs run
+        const int q = r->next_stage;
+        r->next_stage = (q + 1) % kStages;
+        he = r->stage_used[q] ? hipEventSynchronize(r->stage_done[q]) : hipSuccess;
+        if (he == hipSuccess) {
+          r->pool->copy(r->stage[q], src, d.slot_bytes);
+          he = hipMemcpyAsync(dst, r->stage[q], d.slot_bytes, hipMemcpyHostToDevice, ps);
+        }
+        if (he == hipSuccess) he = hipEventRecord(r->stage_done[q], ps);
+        r->stage_used[q] = 1;
+      } else {
+        he = hipMemcpyAsync(dst, src, d.slot_bytes, hipMemcpyHostToDevice, ps);
+      }
       if (he == hipSuccess) he = hipEventRecord(r->fill_done[s], ps);
       if (he != hipSuccess) return hip_err(he, "fill");
       r->fill_recorded[s] = 1;
@@ -235,7 +356,18 @@ int smoe_ring_destroy(smoe_ring* r) {
       if (e != hipSuccess) return hip_err(e, "waiting for pending fills");
     }
   }
+  for (int i = 0; i < kStages; ++i) {
+    if (r->stage_used[i]) {
+      const hipError_t e = hipEventSynchronize(r->stage_done[i]);
+      if (e != hipSuccess) return hip_err(e, "waiting for staged fills");
+    }
+  }
   for (hipEvent_t ev : r->fill_done) (void)hipEventDestroy(ev);
+  for (int i = 0; i < kStages; ++i) {
+    if (r->stage_done[i]) (void)hipEventDestroy(r->stage_done[i]);
+    if (r->stage[i]) (void)hipHostFree(r->stage[i]);
+  }
+  delete r->pool;
   (void)hipEventDestroy(r->compute_mark);
   delete r;
   return SMOE_OK;

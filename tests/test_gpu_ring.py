@@ -21,17 +21,22 @@ def _gpu():
     torch.cuda.init()
 
 
-def make_ring(dims, stack, n_slots, log_capacity=1 << 20):
+def make_ring(dims, stack, n_slots, log_capacity=1 << 20, pageable_layers=()):
+    """A ring over a host copy of the stack's vault: page-locked memory, except
+    for the layers in ``pageable_layers`` (ordinary memory, filled through the
+    ring's staging pipeline)."""
     stride = stack.stride
     host = torch.empty(stack.vault.numel(), dtype=torch.uint8, pin_memory=True)
     host.copy_(stack.vault)
+    plain = torch.empty(stack.vault.numel(), dtype=torch.uint8)
+    plain.copy_(stack.vault)
     slab = torch.empty(n_slots * stride, dtype=torch.uint8, device="cuda")
     copy_stream = torch.cuda.Stream()
     per_layer = dims.n_experts * stride
-    ring = smoe.Ring(n_slots, stack.n_layers, dims.n_experts, dims.top_k, stack.blob_bytes, stride,
-                     [host.data_ptr() + L * per_layer for L in range(stack.n_layers)], stride, slab.data_ptr(),
-                     copy_stream, log_capacity)
-    return ring, (host, slab, copy_stream)
+    ptrs = [(plain if L in pageable_layers else host).data_ptr() + L * per_layer for L in range(stack.n_layers)]
+    ring = smoe.Ring(n_slots, stack.n_layers, dims.n_experts, dims.top_k, stack.blob_bytes, stride, ptrs, stride,
+                     slab.data_ptr(), copy_stream, log_capacity)
+    return ring, (host, plain, slab, copy_stream)
 
 
 def ring_decode(dims, stack, ring, hidden):
@@ -261,3 +266,34 @@ def test_ring_acquire_table_rejects_oversized_unions():
     assert (t[:64] != 0).all() and (t[64:] == 0).all()
     ring.release()
     ring.destroy()
+
+
+def test_ring_with_pageable_layers_matches_resident():
+    """Layers in ordinary (pageable) host memory are filled through the ring's
+    staging buffers; decode and prefill through such a ring equal the resident
+    results, and the decisions still equal the oracle's."""
+    dims = synth.Dims(256, 128, 64, 4, 32)
+    n_layers, n_tok, n_slots = 4, 10, 64
+    stack = DeviceStack(1337, dims, n_layers, zipf_s=1.1)
+    hidden = synth.markov_hidden(1337, n_tok, dims.d_model)
+    ring, keep = make_ring(dims, stack, n_slots, pageable_layers={1, 3})
+    routing, got = ring_decode(dims, stack, ring, hidden)
+    assert np.array_equal(got, resident_decode(dims, stack, hidden))
+    chunk = random_residual(np.random.default_rng(9), 24, dims.d_model, scale=1.5)
+    pg, unions = prefill_layers(dims, stack, chunk, ring)
+    pr, _ = prefill_layers(dims, stack, chunk)
+    for L in range(n_layers):
+        assert np.array_equal(pg[L], pr[L]), f"prefill layer {L}"
+    log = ring.log(1 << 20)
+    ring.release()
+    ring.destroy()
+    ref = oracle.LruRing(n_slots)
+    ref_events = []
+    for layers in routing:
+        for L, experts in enumerate(layers):
+            ref.release()
+            ref_events.extend(ref.acquire(L, experts))
+    for L in range(n_layers):
+        ref.release()
+        ref_events.extend(ref.acquire(L, unions[L]))
+    assert log == ref_events
