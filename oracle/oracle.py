@@ -229,7 +229,7 @@ def prefill_chunk(residuals, w_router_bits, experts, dims, bias=None):
 # ---------------------------------------------------------------------------
 # The LRU expert ring
 # ---------------------------------------------------------------------------
-HIT, MISS = 0, 1
+HIT, MISS, PREFETCH = 0, 1, 2
 
 
 class LruRing:
@@ -256,6 +256,7 @@ class LruRing:
         self.now = 0
         self.where = {}
         self.hits = self.misses = self.evictions = 0
+        self.prefetches = 0
 
     def release(self):
         self.pinned[:] = False
@@ -289,6 +290,42 @@ class LruRing:
             self.pinned[s] = True
             self.now += 1
             events.append((key[0], r, key[1], kind, s, evicted))
+        return events
+
+    def _victim(self):
+        """Lowest-index empty slot, else the unpinned slot with the oldest
+        tick; None when every slot is pinned."""
+        for i in range(self.n):
+            if self.keys[i] is None:
+                return i
+        cand = np.where(~self.pinned, self.tick, np.iinfo(np.int64).max)
+        s = int(np.argmin(cand))
+        return None if self.pinned[s] else s
+
+    def prefetch(self, layer: int, experts):
+        """Speculative loads (not demand): each expert not resident is loaded
+        into the victim slot the same policy picks, with a fresh tick and no
+        pin; a resident expert is left untouched (no tick).  Stops when every
+        slot is pinned (a bet never displaces the current acquisition).
+        Returns one PREFETCH event per load."""
+        events = []
+        for r, e in enumerate(experts):
+            key = (int(layer), int(e))
+            if key in self.where:
+                continue
+            s = self._victim()
+            if s is None:
+                break
+            evicted = self.keys[s]
+            if evicted is not None:
+                del self.where[evicted]
+                self.evictions += 1
+            self.keys[s] = key
+            self.where[key] = s
+            self.tick[s] = self.now
+            self.now += 1
+            self.prefetches += 1
+            events.append((key[0], r, key[1], PREFETCH, s, evicted))
         return events
 
 

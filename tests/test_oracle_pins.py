@@ -452,6 +452,24 @@ class _LruOrderedDict:
             self.pins.add(key)
         return out
 
+    def prefetch(self, L, experts):
+        out = []
+        for r, e in enumerate(experts):
+            key = (L, int(e))
+            if key in self.od:
+                continue
+            if self.next_empty < self.n:
+                s, ev = self.next_empty, None
+                self.next_empty += 1
+            else:
+                ev = next((k for k in self.od if k not in self.pins), None)
+                if ev is None:
+                    break
+                s = self.od.pop(ev)
+            self.od[key] = s
+            out.append((L, r, int(e), 2, s, ev))
+        return out
+
 
 def _routing_trace(rng, T, L, E, k, reuse=0.5):
     trace, prev = [], None
@@ -520,3 +538,59 @@ def test_lru_never_evicts_current_layer():
     for (t, l, r, e, kind, s, evicted) in events:
         if evicted is not None:
             assert evicted[0] != l or evicted[1] not in trace[t][l][:r]
+
+
+@pytest.mark.parametrize("n_slots", [4, 9, 30, 200])
+def test_lru_prefetch_two_independent_simulators_agree(n_slots):
+    """Speculative loads after every layer (ranks past k, drawn at random):
+    the oracle's prefetch and an OrderedDict model give the same events."""
+    rng = np.random.default_rng(40 + n_slots)
+    T, L, E, k, N = 10, 4, 16, 4, 5
+    trace = _routing_trace(rng, T, L, E, k)
+    a, b = oracle.LruRing(n_slots), _LruOrderedDict(n_slots)
+    ev_a, ev_b = [], []
+    for layers in trace:
+        for l, experts in enumerate(layers):
+            a.release()
+            ev_a.extend(a.acquire(l, experts))
+            ev_b.extend(b.layer(l, experts))
+            bets = [int(e) for e in rng.permutation(E) if e not in experts][:N]
+            ev_a.extend(a.prefetch(l, bets))
+            ev_b.extend(b.prefetch(l, bets))
+    assert ev_a == ev_b
+    assert a.prefetches == sum(1 for e in ev_a if e[3] == oracle.PREFETCH)
+
+
+def test_prefetch_then_request_is_a_hit_and_a_resident_bet_is_free():
+    ring = oracle.LruRing(8)
+    ring.acquire(0, [1, 2])
+    ev = ring.prefetch(0, [3, 1, 4])              # 1 is resident: no event, no tick
+    assert [(e[2], e[3], e[4]) for e in ev] == [(3, oracle.PREFETCH, 2), (4, oracle.PREFETCH, 3)]
+    ring.release()
+    got = ring.acquire(1, [3])                     # another layer's expert 3: a miss
+    assert got[0][3] == oracle.MISS
+    ring.release()
+    got = ring.acquire(0, [3, 4])                  # the bets pay off
+    assert [e[3] for e in got] == [oracle.HIT, oracle.HIT]
+    assert ring.hits == 2 and ring.misses == 3 and ring.prefetches == 2
+
+
+def test_prefetch_never_displaces_the_current_acquisition():
+    ring = oracle.LruRing(4)
+    ring.acquire(0, [0, 1, 2, 3])                  # every slot pinned
+    assert ring.prefetch(0, [4, 5]) == []
+    ring.release()
+    ev = ring.prefetch(0, [4])                     # now the oldest slot goes
+    assert ev == [(0, 0, 4, oracle.PREFETCH, 0, (0, 0))]
+
+
+def test_prefetch_evicts_in_lru_order_after_bets():
+    # a bet gets a fresh tick, so older demand entries go first
+    ring = oracle.LruRing(3)
+    ring.acquire(0, [0])
+    ring.release()
+    ring.acquire(1, [0])
+    ring.release()
+    ring.prefetch(2, [0])                          # fills the last empty slot
+    ev = ring.prefetch(3, [0])                     # evicts (0, 0), the oldest
+    assert ev[0][5] == (0, 0)
