@@ -118,6 +118,16 @@ int smoe_route(const smoe_dims* dims, int32_t n_tok, const float* residual, uint
                const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* smoe_route, plus the gate ranking past the top k (the speculative-prefetch
+ * bets of the Optimizations page, "ranks 9-16"):
+ *   next_idx  device int32 [n_tok][n_next] (written) the experts at exact ranks
+ *             k .. k + n_next - 1, from the same ranking as topk_idx
+ * 0 <= n_next <= E - k; n_next == 0 is smoe_route. */
+int smoe_route_ext(const smoe_dims* dims, int32_t n_tok, const float* residual, uint16_t* x_out,
+                   const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w,
+                   int32_t n_next, int32_t* next_idx, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
 /* Decode MoE FFN for one token ("Coalesced GPU Kernels"; step table,
  * Metal-kernel row): for r = 0..k-1, expert e = topk_idx[r]:
  *   h_r = silu(G_e x) * (U_e x),   y = sum_r topk_w[r] * (D_e h_r)  (rank order)
@@ -229,7 +239,7 @@ typedef struct {
 /* One ring decision. */
 typedef struct {
   int32_t layer, rank, expert;
-  int32_t kind;           /* 0 = hit, 1 = miss                              */
+  int32_t kind;           /* 0 = hit, 1 = miss, 2 = speculative load       */
   int32_t slot;
   int32_t evicted_layer;  /* -1 if no eviction                              */
   int32_t evicted_expert;
@@ -259,6 +269,26 @@ int smoe_ring_acquire(smoe_ring* ring, int32_t layer, const int32_t* experts_hos
  * smoe_ring_acquire, plus SMOE_EINVAL for a NULL or unaligned table_dev. */
 int smoe_ring_acquire_table(smoe_ring* ring, int32_t layer, const int32_t* experts_host, int32_t k,
                             void* table_dev, void* compute_stream);
+
+/* Speculative loads ("Speculative prefetch"; "Idle-time popularity
+ * prewarm"): each of the n experts of `layer` (host array) that is not
+ * resident is loaded into the slot a miss would take (the lowest empty slot,
+ * else the unpinned slot with the oldest tick), with a fresh tick and no hold;
+ * a resident expert is left as it is.  Stops at the first expert for which
+ * every slot is held: a bet never displaces the current acquisition.  Fills
+ * go on copy_stream after the work already enqueued on compute_stream (the
+ * same FIFO as demand fills, at the default priority).  Each load is logged
+ * with kind 2.  *n_loaded (may be NULL) = loads issued. */
+int smoe_ring_prefetch(smoe_ring* ring, int32_t layer, const int32_t* experts_host, int32_t n,
+                       int32_t* n_loaded, void* compute_stream);
+
+/* The claim histogram the ring keeps: every demand request of
+ * smoe_ring_acquire(_table) counts one claim of its (layer, expert).  Writes
+ * the n most claimed pairs (most claims first, ties to the lower layer, then
+ * the lower expert) to host arrays; counts_out may be NULL; *n_out = pairs
+ * written (only pairs with at least one claim). */
+int smoe_ring_hottest(const smoe_ring* ring, int32_t n, int32_t* layers_out, int32_t* experts_out,
+                      uint64_t* counts_out, int32_t* n_out);
 
 /* Drop the current holds (the slots stay resident for later hits). */
 int smoe_ring_release(smoe_ring* ring);

@@ -21,6 +21,7 @@ EXPORTED = [
     "smoe_workspace_bytes", "smoe_route", "smoe_moe_decode", "smoe_moe_decode_slots",
     "smoe_decode_layers", "smoe_moe_prefill_chunk", "smoe_ring_create", "smoe_ring_acquire",
     "smoe_ring_release", "smoe_ring_stats", "smoe_ring_log", "smoe_ring_destroy", "smoe_ring_acquire_table",
+    "smoe_ring_prefetch", "smoe_ring_hottest", "smoe_route_ext",
 ]
 
 
@@ -70,6 +71,7 @@ def lib():
             "smoe_q4_blob_stride": (S, [D]),
             "smoe_workspace_bytes": (I, [D, ctypes.c_int32, P(S)]),
             "smoe_route": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, S, VP]),
+            "smoe_route_ext": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, ctypes.c_int32, VP, VP, S, VP]),
             "smoe_moe_decode": (I, [D, VP, VP, VP, VP, VP, VP, S, VP]),
             "smoe_moe_decode_slots": (I, [D, VP, VP, P(VP), VP, VP, S, VP]),
             "smoe_decode_layers": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, P(VP), VP, S, VP]),
@@ -78,6 +80,9 @@ def lib():
             "smoe_ring_acquire": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, P(VP), VP]),
             "smoe_ring_release": (I, [VP]),
             "smoe_ring_acquire_table": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, VP, VP]),
+            "smoe_ring_prefetch": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, P(ctypes.c_int32), VP]),
+            "smoe_ring_hottest": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_uint64),
+                                      P(ctypes.c_int32)]),
             "smoe_ring_stats": (I, [VP, P(ctypes.c_uint64), P(ctypes.c_uint64), P(ctypes.c_uint64),
                                     P(ctypes.c_uint64)]),
             "smoe_ring_log": (I, [VP, P(SmoeRingEvent), S, P(S)]),
@@ -143,6 +148,15 @@ def route(dims, residual, x_out, w_router, bias, topk_idx, topk_w, ws, stream=No
                             ws.numel() if ws is not None else 0, _stream(stream)))
 
 
+def route_ext(dims, residual, x_out, w_router, bias, topk_idx, topk_w, next_idx, ws, stream=None):
+    """route(), plus next_idx [n_tok][n_next]: the experts at ranks k .. k + n_next - 1."""
+    n_tok = residual.shape[0] if residual.dim() == 2 else 1
+    n_next = next_idx.shape[-1] if next_idx is not None else 0
+    _check(lib().smoe_route_ext(ctypes.byref(dims_struct(dims)), int(n_tok), _ptr(residual), _ptr(x_out),
+                                _ptr(w_router), _ptr(bias), _ptr(topk_idx), _ptr(topk_w), int(n_next),
+                                _ptr(next_idx), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
 def moe_decode(dims, x, topk_idx, topk_w, expert_table, residual, ws, stream=None):
     _check(lib().smoe_moe_decode(ctypes.byref(dims_struct(dims)), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
                                  _ptr(expert_table), _ptr(residual), _ptr(ws), ws.numel(), _stream(stream)))
@@ -202,6 +216,22 @@ class Ring:
         table of blob pointers (NULL for the experts not requested)."""
         ex = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
         _check(lib().smoe_ring_acquire_table(self.h, int(layer), ex, len(experts), _ptr(table), _stream(stream)))
+
+    def prefetch(self, layer, experts, stream=None):
+        """Speculative loads of the experts not resident; returns loads issued."""
+        ex = (ctypes.c_int32 * max(1, len(experts)))(*[int(e) for e in experts])
+        n = ctypes.c_int32(0)
+        _check(lib().smoe_ring_prefetch(self.h, int(layer), ex, len(experts), ctypes.byref(n), _stream(stream)))
+        return int(n.value)
+
+    def hottest(self, n):
+        """[(layer, expert, claims)] of the n most claimed pairs."""
+        L = (ctypes.c_int32 * max(1, n))()
+        E = (ctypes.c_int32 * max(1, n))()
+        C = (ctypes.c_uint64 * max(1, n))()
+        m = ctypes.c_int32(0)
+        _check(lib().smoe_ring_hottest(self.h, int(n), L, E, C, ctypes.byref(m)))
+        return [(int(L[i]), int(E[i]), int(C[i])) for i in range(m.value)]
 
     def release(self):
         _check(lib().smoe_ring_release(self.h))

@@ -128,11 +128,20 @@ int smoe_workspace_bytes(const smoe_dims* d, int32_t max_tokens, size_t* bytes) 
 int smoe_route(const smoe_dims* d, int32_t n_tok, const float* residual, uint16_t* x_out,
                const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w, void* ws,
                size_t ws_bytes, void* stream) {
+  return smoe_route_ext(d, n_tok, residual, x_out, w_router, bias, topk_idx, topk_w, 0, nullptr, ws, ws_bytes,
+                        stream);
+}
+
+int smoe_route_ext(const smoe_dims* d, int32_t n_tok, const float* residual, uint16_t* x_out,
+                   const uint16_t* w_router, const float* bias, int32_t* topk_idx, float* topk_w, int32_t n_next,
+                   int32_t* next_idx, void* ws, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (int e = check_dims(d)) return e;
   if (n_tok < 0 || n_tok > kMaxPrefillTokens)
     return fail(SMOE_EINVAL, "n_tok=%d must be in [0, %d]", n_tok, kMaxPrefillTokens);
   if (n_tok == 0) return SMOE_OK;  // nothing to route; the buffers may be NULL
+  if (n_next < 0 || n_next > d->n_experts - d->top_k || (n_next > 0 && !next_idx))
+    return fail(SMOE_EINVAL, "n_next=%d must be in [0, E - k] with next_idx given", n_next);
   if (!residual || !x_out || !w_router || !topk_idx || !topk_w)
     return fail(SMOE_EINVAL, "NULL tensor argument");
   if (!aligned16(residual) || !aligned16(x_out) || !aligned16(w_router))
@@ -154,6 +163,8 @@ int smoe_route(const smoe_dims* d, int32_t n_tok, const float* residual, uint16_
   ta.groups = groups;
   ta.bias = bias;
   ta.n_tok = n_tok;
+  ta.next_idx = n_next > 0 ? next_idx : nullptr;
+  ta.n_next = n_next;
   ta.idx = topk_idx;
   ta.w = topk_w;
   ta.E = d->n_experts;

@@ -23,6 +23,7 @@ struct alignas(16) TopkShared {
   alignas(16) float logf[kMaxExperts];  // the logits rounded to float (topk_select_fast*)
   int part[kTopkMaxSlices][kMaxExperts];
   int idx[kMaxTopK];
+  int rank[kMaxExperts];     // exact rank of every expert (topk_select)
   double val[kMaxTopK];
   double ex[kMaxExperts];
   float w[kMaxTopK];
@@ -51,6 +52,7 @@ __device__ inline void topk_select(TopkShared& s, int E, int k) {
   if (t < E) {
     int rank = 0;
     for (int q = 0; q < slices; ++q) rank += s.part[q][t];
+    s.rank[t] = rank;
     if (rank < k) {
       s.idx[rank] = t;
       s.val[rank] = s.log[t];
@@ -224,6 +226,8 @@ struct TopkArgs {
   const void** ptr_out;      // [n_tok][k] selected blob pointers, or null
   int32_t* idx_rec;          // optional copies
   float* w_rec;
+  int32_t* next_idx;         // [n_tok][n_next] experts at ranks k .. k + n_next - 1, or null
+  int n_next;
   int E, k, norm;
 };
 hipError_t launch_route_topk(const TopkArgs& a, int n_tok, hipStream_t s);

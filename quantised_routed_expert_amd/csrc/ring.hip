@@ -22,6 +22,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <condition_variable>
 #include <mutex>
 #include <new>
@@ -129,6 +130,7 @@ struct smoe_ring {
   std::vector<unsigned char> fill_recorded;
   std::vector<hipEvent_t> fill_done;  // per slot, recorded after its latest fill
   std::vector<int> where;          // (layer * E + expert) -> slot, or -1
+  std::vector<unsigned long long> claims;  // (layer * E + expert) -> demand requests
   std::vector<int> held;           // slots of the current acquisition
   std::vector<const char*> vault;  // per layer: host base of its blobs
   std::vector<unsigned char> pageable;  // per layer: not page-locked (staged)
@@ -140,12 +142,70 @@ struct smoe_ring {
   hipEvent_t compute_mark;
   unsigned long long now = 0;
   int n_filled = 0;                // empty slots are exactly [n_filled, n_slots)
-  unsigned long long hits = 0, misses = 0, evictions = 0, h2d_bytes = 0;
+  unsigned long long hits = 0, misses = 0, evictions = 0, h2d_bytes = 0, prefetches = 0;
   std::vector<smoe_ring_event> log;
 };
 
 static int hip_err(hipError_t e, const char* what) {
   return fail(SMOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The slot a load takes: the lowest-index empty slot, else the unpinned slot
+// with the oldest tick; -1 when every slot is pinned.
+static int victim(const smoe_ring* r) {
+  if (r->n_filled < r->desc.n_slots) return r->n_filled;
+  unsigned long long best = ~0ull;
+  int s = -1;
+  for (int i = 0; i < r->desc.n_slots; ++i)
+    if (!r->pinned[i] && r->tick[i] < best) {
+      best = r->tick[i];
+      s = i;
+    }
+  return s;
+}
+
+// Gives slot s to (layer, expert): drops its previous key (recorded in ev as
+// the eviction) and copies the blob on the copy stream -- directly from a
+// page-locked layer, through a staging buffer from a pageable one -- then
+// records the slot's fill event.
+static hipError_t load_slot(smoe_ring* r, int layer, int expert, int s, smoe_ring_event& ev) {
+  const smoe_ring_desc& d = r->desc;
+  hipStream_t ps = (hipStream_t)d.copy_stream;
+  if (s == r->n_filled) {
+    ++r->n_filled;
+  } else {
+    const long long old = r->key[s];
+    r->where[old] = -1;
+    ev.evicted_layer = (int)(old / d.n_experts);
+    ev.evicted_expert = (int)(old % d.n_experts);
+    ++r->evictions;
+  }
+  const long long kk = (long long)layer * d.n_experts + expert;
+  r->key[s] = kk;
+  r->where[kk] = s;
+  const char* src = r->vault[layer] + (size_t)expert * d.vault_stride;
+  char* dst = (char*)d.slab_dev + (size_t)s * d.slot_stride;
+  hipError_t he;
+  if (r->pageable[layer]) {
+    // host copy into a free staging buffer while earlier DMAs run
+    const int q = r->next_stage;
+    r->next_stage = (q + 1) % kStages;
+    he = r->stage_used[q] ? hipEventSynchronize(r->stage_done[q]) : hipSuccess;
+    if (he == hipSuccess) {
+      r->pool->copy(r->stage[q], src, d.slot_bytes);
+      he = hipMemcpyAsync(dst, r->stage[q], d.slot_bytes, hipMemcpyHostToDevice, ps);
+    }
+    if (he == hipSuccess) he = hipEventRecord(r->stage_done[q], ps);
+    r->stage_used[q] = 1;
+  } else {
+    he = hipMemcpyAsync(dst, src, d.slot_bytes, hipMemcpyHostToDevice, ps);
+  }
+  if (he == hipSuccess) he = hipEventRecord(r->fill_done[s], ps);
+  if (he == hipSuccess) {
+    r->fill_recorded[s] = 1;
+    r->h2d_bytes += d.slot_bytes;
+  }
+  return he;
 }
 
 extern "C" {
@@ -189,6 +249,7 @@ int smoe_ring_create(const smoe_ring_desc* d, smoe_ring** out) {
   r->fill_recorded.assign(n, 0);
   r->fill_done.assign(n, nullptr);
   r->where.assign((size_t)d->n_layers * d->n_experts, -1);
+  r->claims.assign((size_t)d->n_layers * d->n_experts, 0);
   r->log.reserve(d->log_capacity);
   hipError_t e = hipEventCreateWithFlags(&r->compute_mark, hipEventDisableTiming);
   for (size_t i = 0; e == hipSuccess && i < n; ++i) e = hipEventCreateWithFlags(&r->fill_done[i], hipEventDisableTiming);
@@ -252,48 +313,15 @@ int smoe_ring_acquire(smoe_ring* r, int32_t layer, const int32_t* experts, int32
     ev.evicted_layer = -1;
     ev.evicted_expert = -1;
     ev.pad = 0;
+    ++r->claims[kk];
     if (s >= 0) {
       ev.kind = 0;
       ++r->hits;
     } else {
-      if (r->n_filled < d.n_slots) {
-        s = r->n_filled++;
-      } else {
-        unsigned long long best = ~0ull;
-        for (int i = 0; i < d.n_slots; ++i)
-          if (!r->pinned[i] && r->tick[i] < best) {
-            best = r->tick[i];
-            s = i;
-          }
-        if (s < 0) return fail(SMOE_ENOSLOT, "every slot is held by the current layer");
-        const long long old = r->key[s];
-        r->where[old] = -1;
-        ev.evicted_layer = (int)(old / d.n_experts);
-        ev.evicted_expert = (int)(old % d.n_experts);
-        ++r->evictions;
-      }
-      r->key[s] = kk;
-      r->where[kk] = s;
-      const char* src = r->vault[layer] + (size_t)experts[rank] * d.vault_stride;
-      char* dst = (char*)d.slab_dev + (size_t)s * d.slot_stride;
-      if (r->pageable[layer]) {
-        // host copy into a free staging buffer while earlier DMAs run
-        const int q = r->next_stage;
-        r->next_stage = (q + 1) % kStages;
-        he = r->stage_used[q] ? hipEventSynchronize(r->stage_done[q]) : hipSuccess;
-        if (he == hipSuccess) {
-          r->pool->copy(r->stage[q], src, d.slot_bytes);
-          he = hipMemcpyAsync(dst, r->stage[q], d.slot_bytes, hipMemcpyHostToDevice, ps);
-        }
-        if (he == hipSuccess) he = hipEventRecord(r->stage_done[q], ps);
-        r->stage_used[q] = 1;
-      } else {
-        he = hipMemcpyAsync(dst, src, d.slot_bytes, hipMemcpyHostToDevice, ps);
-      }
-      if (he == hipSuccess) he = hipEventRecord(r->fill_done[s], ps);
+      s = victim(r);
+      if (s < 0) return fail(SMOE_ENOSLOT, "every slot is held by the current layer");
+      he = load_slot(r, layer, experts[rank], s, ev);
       if (he != hipSuccess) return hip_err(he, "fill");
-      r->fill_recorded[s] = 1;
-      r->h2d_bytes += d.slot_bytes;
       ev.kind = 1;
       ++r->misses;
     }
@@ -310,6 +338,68 @@ int smoe_ring_acquire(smoe_ring* r, int32_t layer, const int32_t* experts, int32
     he = hipStreamWaitEvent(cs, r->fill_done[s], 0);
     if (he != hipSuccess) return hip_err(he, "hipStreamWaitEvent");
   }
+  return SMOE_OK;
+}
+
+int smoe_ring_prefetch(smoe_ring* r, int32_t layer, const int32_t* experts, int32_t n, int32_t* n_loaded,
+                       void* compute_stream) {
+  if (!r || (n > 0 && !experts)) return fail(SMOE_EINVAL, "NULL argument");
+  const smoe_ring_desc& d = r->desc;
+  if (n_loaded) *n_loaded = 0;
+  if (layer < 0 || layer >= d.n_layers) return fail(SMOE_EINVAL, "layer=%d out of range", layer);
+  if (n < 0 || n > d.n_experts) return fail(SMOE_EINVAL, "n=%d must be in [0, %d]", n, d.n_experts);
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= d.n_experts) return fail(SMOE_EINVAL, "expert %d out of range", experts[i]);
+  bool ordered = false;
+  int loaded = 0;
+  for (int i = 0; i < n; ++i) {
+    const long long kk = (long long)layer * d.n_experts + experts[i];
+    if (r->where[kk] >= 0) continue;  // resident: a bet that costs nothing
+    const int s = victim(r);
+    if (s < 0) break;                 // never displaces the current acquisition
+    if (!ordered) {                   // loads must not overtake earlier compute
+      hipError_t he = hipEventRecord(r->compute_mark, (hipStream_t)compute_stream);
+      if (he == hipSuccess) he = hipStreamWaitEvent((hipStream_t)d.copy_stream, r->compute_mark, 0);
+      if (he != hipSuccess) return hip_err(he, "ordering the copy stream after the compute stream");
+      ordered = true;
+    }
+    smoe_ring_event ev;
+    ev.layer = layer;
+    ev.rank = i;
+    ev.expert = experts[i];
+    ev.kind = 2;
+    ev.slot = s;
+    ev.evicted_layer = -1;
+    ev.evicted_expert = -1;
+    ev.pad = 0;
+    const hipError_t he = load_slot(r, layer, experts[i], s, ev);
+    if (he != hipSuccess) return hip_err(he, "prefetch fill");
+    r->tick[s] = r->now++;
+    ++r->prefetches;
+    ++loaded;
+    if (r->log.size() < d.log_capacity) r->log.push_back(ev);
+  }
+  if (n_loaded) *n_loaded = loaded;
+  return SMOE_OK;
+}
+
+int smoe_ring_hottest(const smoe_ring* r, int32_t n, int32_t* layers_out, int32_t* experts_out,
+                      uint64_t* counts_out, int32_t* n_out) {
+  if (!r || !n_out || (n > 0 && (!layers_out || !experts_out))) return fail(SMOE_EINVAL, "NULL argument");
+  if (n < 0) return fail(SMOE_EINVAL, "n=%d < 0", n);
+  std::vector<int> order;
+  for (size_t i = 0; i < r->claims.size(); ++i)
+    if (r->claims[i]) order.push_back((int)i);
+  const size_t m = order.size() < (size_t)n ? order.size() : (size_t)n;
+  std::partial_sort(order.begin(), order.begin() + m, order.end(), [r](int a, int b) {
+    return r->claims[a] != r->claims[b] ? r->claims[a] > r->claims[b] : a < b;
+  });
+  for (size_t i = 0; i < m; ++i) {
+    layers_out[i] = order[i] / r->desc.n_experts;
+    experts_out[i] = order[i] % r->desc.n_experts;
+    if (counts_out) counts_out[i] = r->claims[order[i]];
+  }
+  *n_out = (int32_t)m;
   return SMOE_OK;
 }
 

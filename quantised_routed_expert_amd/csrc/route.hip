@@ -359,6 +359,10 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(TopkArgs a) {
     if (a.idx_rec) a.idx_rec[o] = e;
     if (a.w_rec) a.w_rec[o] = tk.w[tid];
   }
+  if (a.next_idx && tid < a.E) {  // the ranking past k, from the same exact ranks
+    const int rk = tk.rank[tid] - a.k;
+    if (rk >= 0 && rk < a.n_next) a.next_idx[(size_t)t * a.n_next + rk] = tid;
+  }
 }
 
 hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s, int* groups) {
