@@ -476,27 +476,49 @@ def bench_ring(args):
     x = torch.empty((1, dims.d_model), dtype=torch.int16, device="cuda")
     idx = torch.empty((1, dims.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((1, dims.top_k), dtype=torch.float32, device="cuda")
-    idx_host = torch.empty((1, dims.top_k), dtype=torch.int32, pin_memory=True)
+    S = args.spec
+    sel = torch.empty((1, dims.top_k + S), dtype=torch.int32, device="cuda")   # ranks 0 .. k + S - 1
+    sel_host = torch.empty((1, dims.top_k + S), dtype=torch.int32, pin_memory=True)
     r = torch.empty((1, dims.d_model), dtype=torch.float32, device="cuda")
     prev = [None] * NL
     repeats = []
+    bets_loaded = [0]
 
     def token(t, count):
         for L in range(NL):
             r.copy_(hidden[L, t:t + 1])
-            smoe.route(dims, r, x, router[L], None, idx, w, ws)
-            idx_host.copy_(idx)
+            if S:
+                smoe.route_ext(dims, r, x, router[L], None, sel[:, :dims.top_k], w, sel[:, dims.top_k:], ws)
+            else:
+                smoe.route(dims, r, x, router[L], None, sel, w, ws)
+            sel_host.copy_(sel)
             torch.cuda.current_stream().synchronize()
-            experts = idx_host.numpy()[0].tolist()
+            ranked = sel_host.numpy()[0].tolist()
+            experts = ranked[:dims.top_k]
             if count and prev[L] is not None:
                 repeats.append(len(set(experts) & set(prev[L])) / dims.top_k)
             prev[L] = experts
             ptrs = ring.acquire(L, experts)
             smoe.moe_decode_slots(dims, x, w, ptrs, r, ws)
+            if S:  # bets on the next token at this layer: this token's ranks k .. k + S - 1
+                n = ring.prefetch(L, ranked[dims.top_k:])
+                if count:
+                    bets_loaded[0] += n
 
     for t in range(W):
         token(t, False)
     torch.cuda.synchronize()
+    prewarm_loads = 0
+    if args.prewarm:  # idle time between turns: the historically hottest experts into the ring
+        ring.release()
+        hot = ring.hottest(n_slots)
+        by_layer = {}
+        for L, e, _ in hot:
+            by_layer.setdefault(L, []).append(e)
+        for L in sorted(by_layer):
+            prewarm_loads += ring.prefetch(L, by_layer[L])
+        torch.cuda.synchronize()
+        log(f"prewarm: {prewarm_loads} loads from {len(hot)} hottest (layer, expert) pairs")
     s0 = ring.stats()
     t1 = time.time()
     for t in range(K):
@@ -517,8 +539,10 @@ def bench_ring(args):
         "ms_per_step": dt * 1000.0 / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "q4-affine weights, f16 dot products with fp32 accumulation; float64 router",
         "data": "synthetic (per-layer Markov router inputs h_t = 0.7 h_{t-1} + 0.3 z_t)",
-        "config": {"workload": wl.name, "layers": NL, "ring_slots": n_slots, "parallelism": "single GPU"},
+        "config": {"workload": wl.name, "layers": NL, "ring_slots": n_slots, "spec": S, "prewarm": bool(args.prewarm),
+                   "parallelism": "single GPU"},
         "hit_rate": hits / max(1, hits + misses), "misses_per_token": misses / K,
+        "bets_loaded_per_token": bets_loaded[0] / K, "prewarm_loads": prewarm_loads,
         "h2d_gbps": h2d / dt / 1e9, "expert_repeat_fraction": float(np.mean(repeats)),
         "vault_layers_page_locked": n_pinned,
         "host_link": dict(link, h2d_frac_of_pinned=h2d / dt / 1e9 / link["pinned_h2d_gbps"]),
@@ -708,7 +732,10 @@ def main():
     ap.add_argument("--instrument-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--pinned-gib", type=float, default=56.0, help="ring workload: page-locked vault budget")
+    ap.add_argument("--pinned-gib", type=float, default=56.0, help="ring workloads: page-locked vault budget")
+    ap.add_argument("--spec", type=int, default=0, help="ring workload: bet on gate ranks k .. k + spec - 1")
+    ap.add_argument("--prewarm", action="store_true",
+                    help="ring workload: after the warm-up tokens, load the most claimed experts (idle time)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
