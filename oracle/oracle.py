@@ -22,7 +22,10 @@ Overview" (docs.s-moe.com, v1) and the S-MoE diary feed.
 * Fused SMOE-Q4 expert FFN: per-chunk affine dequant, gate and up on the same
   input, SwiGLU, down projection, and the gate-weighted sum of the k expert
   outputs added into the residual (Optimizations, "Coalesced GPU Kernels";
-  System Overview, step table, "Metal Kernel" row).
+  System Overview, step table, "Metal Kernel" row).  The SMOE-Q2 vault of
+  the Optimizations page ("Q2 Vaults -- the Next 2x") uses the same affine
+  dequant with 2-bit codes; the oracle reads logical codes, so only their
+  range (0..3 instead of 0..15) differs.
 * Layer-major prefill: the distinct experts of a chunk form a union that is
   streamed once (Optimizations, "Prefill Reads Each Expert Once"); the union
   is listed in first-touch order because that section has each expert
@@ -126,10 +129,11 @@ def select_topk(logits, k: int, norm_topk_prob: bool = True):
 
 
 # ---------------------------------------------------------------------------
-# SMOE-Q4 expert
+# SMOE-Q4 / SMOE-Q2 expert
 # ---------------------------------------------------------------------------
 def dequant(q, scale_bits, min_bits, chunk: int) -> np.ndarray:
-    """W[n][k] = scale[n][k // chunk] * q[n][k] + min[n][k // chunk] (float64)."""
+    """W[n][k] = scale[n][k // chunk] * q[n][k] + min[n][k // chunk] (float64),
+    for codes of any width (Q4: 0..15, Q2: 0..3)."""
     q = np.asarray(q, dtype=np.float64)
     s = np.repeat(bf16_to_f64(scale_bits), chunk, axis=1)
     m = np.repeat(bf16_to_f64(min_bits), chunk, axis=1)

@@ -59,3 +59,19 @@ QWEN235B_RING = Workload(
     n_layers=94, steps=256, mode="ring", ring_slots=1536, markov=(0.7, 0.3))
 
 CONFIGS = [TINY, QWEN30B_DECODE, QWEN235B_DECODE, QWEN235B_PREFILL, QWEN235B_RING]
+
+# SMOE-Q2 variants ("Q2 Vaults -- the Next 2x, Twice Over", Optimizations page:
+# a 2-bit vault halves every blob and doubles the ring's slots).  Same shapes,
+# seeds and distributions as the Q4 workloads; the ring keeps the Q4 ring's HBM
+# budget (1536 Q4 slots = 16.31 GB), which holds 2764 Q2 blobs.
+QWEN235B_DECODE_Q2 = Workload(
+    name="qwen3-235b-a22b-shape-decode-94L-d4096-f1536-e128-k8-q2c64",
+    dims=Dims(4096, 1536, 128, 8, 64, bits=2),
+    n_layers=94, steps=64, mode="decode")
+
+QWEN235B_RING_Q2 = Workload(
+    name="qwen3-235b-a22b-shape-ring-decode-256tok-2764slots-markov0.7-q2c64",
+    dims=Dims(4096, 1536, 128, 8, 64, bits=2),
+    n_layers=94, steps=256, mode="ring", ring_slots=2764, markov=(0.7, 0.3))
+
+Q2_WORKLOADS = [QWEN235B_DECODE_Q2, QWEN235B_RING_Q2]

@@ -36,6 +36,7 @@ KIND_SCALES = 2
 KIND_ROUTER = 3
 KIND_HIDDEN = 4
 KIND_BIASPERM = 5
+KIND_CODES_Q2 = 6
 
 MAT_GATE, MAT_UP, MAT_DOWN = 0, 1, 2
 
@@ -122,10 +123,12 @@ def normal_box_muller(words: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 class Dims:
     """Geometry of one routed-expert MoE layer.  ``rms_eps`` is a float32 value
-    (the library takes it as float), 1e-6 rounded to float32 by default."""
+    (the library takes it as float), 1e-6 rounded to float32 by default.
+    ``bits`` is the code width of the expert blobs: 4 (SMOE-Q4) or 2
+    (SMOE-Q2, the halved vault of the Optimizations page, "Q2 Vaults")."""
 
     def __init__(self, d_model, d_ff, n_experts, top_k, chunk, norm_topk_prob=True,
-                 rms_eps=float(np.float32(1e-6))):
+                 rms_eps=float(np.float32(1e-6)), bits=4):
         self.d_model = int(d_model)
         self.d_ff = int(d_ff)
         self.n_experts = int(n_experts)
@@ -133,6 +136,8 @@ class Dims:
         self.chunk = int(chunk)
         self.norm_topk_prob = bool(norm_topk_prob)
         self.rms_eps = float(rms_eps)
+        self.bits = int(bits)
+        assert self.bits in (2, 4)
 
     def replace(self, **kw):
         d = dict(self.__dict__)
@@ -141,7 +146,8 @@ class Dims:
 
     def __repr__(self):
         return (f"Dims(d_model={self.d_model}, d_ff={self.d_ff}, n_experts={self.n_experts}, "
-                f"top_k={self.top_k}, chunk={self.chunk}, norm_topk_prob={self.norm_topk_prob})")
+                f"top_k={self.top_k}, chunk={self.chunk}, norm_topk_prob={self.norm_topk_prob}, "
+                f"bits={self.bits})")
 
 
 def blob_sections(dims: Dims) -> dict:
@@ -149,7 +155,9 @@ def blob_sections(dims: Dims) -> dict:
 
     Matrices: gate G[d_ff][d_model], up U[d_ff][d_model], down D[d_model][d_ff].
     Element W[n][k] = scale[n][k // chunk] * q[n][k] + min[n][k // chunk].
-    Codes are row-major, two per byte, the even element in the low nibble.
+    Codes are row-major, 8 / bits per byte, element k of a byte's group in
+    bits [bits * k, bits * k + bits) (Q4: the even element in the low nibble;
+    Q2: four codes per byte, the first in bits 0..1).
     Per-chunk parameters are (scale, min) bf16 pairs, row-major, scale first.
     Section order: G codes, U codes, D codes, G params, U params, D params.
     """
@@ -158,7 +166,7 @@ def blob_sections(dims: Dims) -> dict:
     pos = 0
     for name, rows, cols in (("gate", f, d), ("up", f, d), ("down", d, f)):
         off[name + "_codes"] = pos
-        pos += rows * cols // 2
+        pos += rows * cols * dims.bits // 8
     for name, rows, cols in (("gate", f, d), ("up", f, d), ("down", d, f)):
         off[name + "_params"] = pos
         pos += rows * (cols // c) * 4
@@ -174,26 +182,49 @@ def _mat_shape(dims: Dims, mat: int):
 
 
 def code_words(seed: int, dims: Dims, layer: int, expert: int, mat: int) -> np.ndarray:
+    """The matrix's packed code section as stream words: Q4 codes come from
+    stream kind 1, Q2 codes from kind 6 (64 / bits codes per word)."""
     rows, cols = _mat_shape(dims, mat)
-    assert (rows * cols) % 16 == 0
-    key = stream_key(seed, KIND_CODES, layer, expert, mat)
-    return stream_words(key, 0, rows * cols // 16)
+    per_word = 64 // dims.bits
+    assert (rows * cols) % per_word == 0
+    kind = KIND_CODES if dims.bits == 4 else KIND_CODES_Q2
+    key = stream_key(seed, kind, layer, expert, mat)
+    return stream_words(key, 0, rows * cols // per_word)
+
+
+def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
+    """Codes of a packed byte array, element order as in ``blob_sections``."""
+    b = np.asarray(packed, dtype=np.uint8)
+    per = 8 // bits
+    q = np.empty(b.size * per, dtype=np.uint8)
+    for j in range(per):
+        q[j::per] = (b >> (bits * j)) & ((1 << bits) - 1)
+    return q
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of ``unpack_codes``."""
+    q = np.asarray(q, dtype=np.uint8).reshape(-1)
+    per = 8 // bits
+    assert q.size % per == 0 and q.max(initial=0) < (1 << bits)
+    b = np.zeros(q.size // per, dtype=np.uint8)
+    for j in range(per):
+        b |= (q[j::per] << (bits * j)).astype(np.uint8)
+    return b
 
 
 def expert_codes(seed: int, dims: Dims, layer: int, expert: int, mat: int) -> np.ndarray:
-    """Logical 4-bit codes q[n][k] (uint8, 0..15) of one matrix."""
+    """Logical codes q[n][k] (uint8, 0 .. 2^bits - 1) of one matrix."""
     rows, cols = _mat_shape(dims, mat)
     b = code_words(seed, dims, layer, expert, mat).view(np.uint8)
-    q = np.empty(b.size * 2, dtype=np.uint8)
-    q[0::2] = b & 15
-    q[1::2] = b >> 4
-    return q.reshape(rows, cols)
+    return unpack_codes(b, dims.bits).reshape(rows, cols)
 
 
 def expert_params_bits(seed: int, dims: Dims, layer: int, expert: int, mat: int):
     """Per-chunk (scale, min) of one matrix as bf16 bit patterns [rows][cols/chunk].
 
-    scale ~ U(0.002, 0.01) rounded to bf16; min = -8 * scale (exact)."""
+    scale ~ U(0.002, 0.01) rounded to bf16; min = -2^(bits-1) * scale (exact):
+    -8 * scale for Q4, -2 * scale for Q2, so that the mid code is zero."""
     rows, cols = _mat_shape(dims, mat)
     nc = cols // dims.chunk
     key = stream_key(seed, KIND_SCALES, layer, expert, mat)
@@ -201,7 +232,7 @@ def expert_params_bits(seed: int, dims: Dims, layer: int, expert: int, mat: int)
     t = 0.008 * u            # two separately rounded double operations
     s = 0.002 + t
     sbits = bf16_bits_from_f64(s)
-    mbits = bf16_bits_from_f64(-8.0 * bf16_bits_to_f64(sbits))
+    mbits = bf16_bits_from_f64(-float(1 << (dims.bits - 1)) * bf16_bits_to_f64(sbits))
     return sbits.reshape(rows, nc), mbits.reshape(rows, nc)
 
 
@@ -236,9 +267,7 @@ def pack_logical(dims: Dims, logical: dict) -> np.ndarray:
     off = blob_sections(dims)
     blob = np.zeros(off["stride"], dtype=np.uint8)
     for name in ("gate", "up", "down"):
-        q = np.asarray(logical[name]["q"], dtype=np.uint8).reshape(-1)
-        assert q.max(initial=0) < 16
-        b = (q[0::2] | (q[1::2] << 4)).astype(np.uint8)
+        b = pack_codes(logical[name]["q"], dims.bits)
         blob[off[name + "_codes"]: off[name + "_codes"] + b.size] = b
         s = np.asarray(logical[name]["scale_bits"], dtype=np.uint16).reshape(-1)
         m = np.asarray(logical[name]["min_bits"], dtype=np.uint16).reshape(-1)

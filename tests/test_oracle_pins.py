@@ -377,6 +377,83 @@ def test_expert_order_permutation_gives_same_mix():
 
 
 # ---------------------------------------------------------------------------
+# SMOE-Q2 (2-bit codes, the same per-chunk affine dequant)
+# ---------------------------------------------------------------------------
+def _hand_expert_q2():
+    """d_model 4, d_ff 2, chunk 2, codes 0..3.  Dequantised matrices by hand."""
+    b = lambda v: synth.bf16_bits_from_f64(np.asarray(v, dtype=np.float64))
+    return {
+        # G row0: [0.5*2-1, 0.5*3-1, 1*0-2, 1*3-2] = [0, 0.5, -2, 1]
+        # G row1: [2*1-4, 2*2-4, 0.25*2-0.5, 0.25*0-0.5] = [-2, 0, 0, -0.5]
+        "gate": {"q": np.array([[2, 3, 0, 3], [1, 2, 2, 0]], dtype=np.uint8),
+                 "scale_bits": b([[0.5, 1.0], [2.0, 0.25]]),
+                 "min_bits": b([[-1.0, -2.0], [-4.0, -0.5]])},
+        # U row0: [1, 0, 0, 0]; U row1: [0, 0, -4, 0]
+        "up": {"q": np.array([[3, 2, 2, 2], [2, 2, 0, 2]], dtype=np.uint8),
+               "scale_bits": b([[1.0, 1.0], [1.0, 2.0]]),
+               "min_bits": b([[-2.0, -2.0], [-2.0, -4.0]])},
+        # D rows: [1, 0], [0, 1], [0.5, 0.5], [0.5, -0.5]
+        "down": {"q": np.array([[3, 2], [2, 3], [2, 2], [3, 1]], dtype=np.uint8),
+                 "scale_bits": b([[1.0], [1.0], [0.25], [0.5]]),
+                 "min_bits": b([[-2.0], [-2.0], [0.0], [-1.0]])},
+    }
+
+
+def test_q2_dequant_and_expert_hand_example():
+    ex = _hand_expert_q2()
+    G = oracle.dequant(ex["gate"]["q"], ex["gate"]["scale_bits"], ex["gate"]["min_bits"], 2)
+    assert G.tolist() == [[0, 0.5, -2, 1], [-2, 0, 0, -0.5]]
+    D = oracle.dequant(ex["down"]["q"], ex["down"]["scale_bits"], ex["down"]["min_bits"], 2)
+    assert D.tolist() == [[1, 0], [0, 1], [0.5, 0.5], [0.5, -0.5]]
+    x = np.array([1.0, 2.0, 0.5, -1.0])
+    # g = [-1, -1.5]; u = [1, -2]; h = silu(g) * u
+    h0 = -1.0 / (1 + math.exp(1.0))
+    h1 = -1.5 / (1 + math.exp(1.5)) * -2.0
+    y = oracle.expert_ffn(ex, x, 2)
+    assert np.allclose(y, [h0, h1, 0.5 * (h0 + h1), 0.5 * (h0 - h1)], rtol=1e-15, atol=1e-17)
+
+
+def test_q2_dequant_mid_code_zero_round_trip_and_float32_exact():
+    dims = synth.Dims(128, 64, 4, 2, 64, bits=2)
+    for mat in (synth.MAT_UP, synth.MAT_DOWN):
+        q = synth.expert_codes(1337, dims, 0, 2, mat)
+        assert q.max() <= 3 and set(np.unique(q).tolist()) == {0, 1, 2, 3}
+        sb, mb = synth.expert_params_bits(1337, dims, 0, 2, mat)
+        W = oracle.dequant(q, sb, mb, dims.chunk)
+        s = np.repeat(oracle.bf16_to_f64(sb), dims.chunk, 1)
+        m = np.repeat(oracle.bf16_to_f64(mb), dims.chunk, 1)
+        assert np.all(W[q == 2] == 0.0)                         # min = -2 * scale
+        assert np.array_equal(np.rint((W - m) / s).astype(np.uint8), q)
+        w32 = (s.astype(np.float32) * q.astype(np.float32)) + m.astype(np.float32)
+        assert np.array_equal(w32.astype(np.float64), W)
+
+
+def test_q2_quantisation_error_bound():
+    # A 4-level affine grid spanning each chunk: dequant(quant(v)) is within
+    # half a step of v.
+    rng = np.random.default_rng(13)
+    v = rng.uniform(-0.05, 0.05, (8, 64))
+    sb = synth.bf16_bits_from_f64((v.max(1) - v.min(1)) / 3.0)[:, None]
+    mb = synth.bf16_bits_from_f64(v.min(1))[:, None]
+    sv, mv = oracle.bf16_to_f64(sb), oracle.bf16_to_f64(mb)
+    q = np.clip(np.rint((v - mv) / sv), 0, 3).astype(np.uint8)
+    W = oracle.dequant(q, sb, mb, 64)
+    inside = (v >= mv) & (v <= mv + 3 * sv)
+    bound = np.broadcast_to(sv / 2 + 1e-15, v.shape)
+    assert np.all(np.abs(W - v)[inside] <= bound[inside])
+
+
+def test_q2_single_expert_weight_one_is_dense_swiglu():
+    dims = synth.Dims(256, 128, 16, 1, 64, bits=2)
+    dims, experts, wr = _tiny_stack(dims=dims)
+    r = synth.hidden_bf16(1337, 1, dims.d_model).astype(np.float64)
+    out = oracle.moe_layer(r, wr, experts, dims)
+    assert out["w"].tolist() == [1.0]
+    dense = _dense_swiglu_torch(experts[out["idx"][0]], out["x"], dims.chunk)
+    assert np.allclose(out["y"], dense, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
 # Prefill union
 # ---------------------------------------------------------------------------
 def _random_idx(rng, T, E, k):

@@ -111,3 +111,60 @@ def test_golden_tiny_decode_reproduces():
     assert [int(b) for b in out["x_bits"]] == g["x_bits"]
     assert np.allclose(out["w"], g["w"], rtol=1e-14)
     assert np.allclose(out["y"], g["y"], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# SMOE-Q2 blobs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wl, blob", [(synth.Q2_WORKLOADS[0], 5898240), (synth.Q2_WORKLOADS[1], 5898240)])
+def test_q2_blob_sizes_exact(wl, blob):
+    off = synth.blob_sections(wl.dims)
+    # codes: 3 * d * f / 4 bytes; params as Q4: 12 * d * f / chunk
+    assert off["bytes"] == blob == 3 * 4096 * 1536 // 4 + 12 * 4096 * 1536 // 64
+    assert off["stride"] == 360 * 16384
+    assert wl.ring_slots in (0, 2764)
+    for k, v in off.items():
+        assert v % 16 == 0, k
+    # the Q4 ring's HBM budget holds 2764 Q2 blobs
+    assert 2764 * blob <= 1536 * 10616832 < 2765 * blob
+
+
+def test_q2_code_and_param_layout():
+    dims = synth.Dims(512, 128, 16, 4, 64, bits=2)
+    off = synth.blob_sections(dims)
+    blob = synth.pack_blob(1337, dims, 0, 3)
+    for name, mat, rows, cols in (("gate", 0, 128, 512), ("up", 1, 128, 512), ("down", 2, 512, 128)):
+        q = synth.expert_codes(1337, dims, 0, 3, mat)
+        sb, mb = synth.expert_params_bits(1337, dims, 0, 3, mat)
+        for n, j in ((0, 0), (5, 17), (rows - 1, cols // 4 - 1)):
+            byte = int(blob[off[name + "_codes"] + n * cols // 4 + j])
+            assert [(byte >> (2 * i)) & 3 for i in range(4)] == q[n, 4 * j:4 * j + 4].tolist()
+        nc = cols // dims.chunk
+        for n, c in ((0, 0), (7, nc - 1), (rows - 1, 1)):
+            p = off[name + "_params"] + (n * nc + c) * 4
+            assert int(blob[p]) | int(blob[p + 1]) << 8 == sb[n, c]
+            assert int(blob[p + 2]) | int(blob[p + 3]) << 8 == mb[n, c]
+    assert np.all(blob[off["bytes"]:] == 0)
+
+
+def test_q2_packers_agree_and_streams_differ_from_q4():
+    dims = synth.Dims(512, 192, 8, 2, 64, bits=2)
+    a = synth.pack_blob(7, dims, 2, 5)
+    b = synth.pack_logical(dims, synth.expert_logical(7, dims, 2, 5))
+    assert np.array_equal(a, b)
+    q = np.arange(64, dtype=np.uint8) % 4
+    assert np.array_equal(synth.unpack_codes(synth.pack_codes(q, 2), 2), q)
+    q4 = synth.expert_codes(7, dims.replace(bits=4), 2, 5, synth.MAT_GATE)
+    q2 = synth.expert_codes(7, dims, 2, 5, synth.MAT_GATE)
+    assert not np.array_equal(q4 & 3, q2)
+
+
+def test_q2_distributions():
+    dims = synth.Dims(2048, 768, 128, 8, 64, bits=2)
+    q = synth.expert_codes(1337, dims, 1, 2, synth.MAT_UP)
+    freq = np.bincount(q.reshape(-1), minlength=4) / q.size
+    assert np.all(np.abs(freq - 0.25) < 0.002)
+    sb, mb = synth.expert_params_bits(1337, dims, 1, 2, synth.MAT_DOWN)
+    s, m = oracle.bf16_to_f64(sb), oracle.bf16_to_f64(mb)
+    assert s.min() >= 0.002 - 1e-5 and s.max() <= 0.01 + 1e-4
+    assert np.array_equal(m, -2 * s)
