@@ -48,6 +48,16 @@
  *   D params (per row and chunk: bf16 scale, then bf16 min);
  *   blob bytes = 1.5*d_model*d_ff + 12*d_model*d_ff/chunk; blobs sit at a
  *   stride rounded up to 16384 bytes; a blob must be 16-byte aligned.
+ *
+ * SMOE-Q2 expert blob (the 2-bit vault the Optimizations page announces in
+ * "Q2 Vaults -- the Next 2x, Twice Over": same affine dequant, every blob
+ * about half the size; the layout is again the library's): as SMOE-Q4 with
+ * q in 0..3 and four codes per byte, element 4j + i of a row in bits
+ * [2i, 2i + 2) of the row's byte j; parameters unchanged.  Chunk 64 only.
+ *   blob bytes = 0.75*d_model*d_ff + 12*d_model*d_ff/chunk.
+ * SMOE-Q2 is supported by the decode calls (smoe_moe_decode,
+ * smoe_moe_decode_slots, smoe_decode_layers) and by the ring, which moves
+ * blobs of any size; smoe_moe_prefill_chunk takes SMOE-Q4 only.
  */
 #ifndef SMOE_H
 #define SMOE_H
@@ -77,15 +87,22 @@ typedef struct {
   int32_t chunk;          /* Q4 affine chunk along the reduction dim: 32, 64 */
   int32_t norm_topk_prob; /* 1: divide the k weights by their sum (Qwen3)    */
   float rms_eps;          /* RMSNorm epsilon (1e-6 for the Qwen3 shapes)     */
+  int32_t quant_bits;     /* code width of the expert blobs: 4 (SMOE-Q4; 0 is
+                             read as 4) or 2 (SMOE-Q2, chunk 64, d_model a
+                             multiple of 512)                                */
 } smoe_dims;
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char* smoe_last_error(void);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2; 2 added smoe_dims.quant_bits). */
 int32_t smoe_version(void);
 
-/* Exact byte size of one expert blob and its 16 KiB-aligned stride. */
+/* Exact byte size of one expert blob (in the format dims->quant_bits
+ * selects) and its 16 KiB-aligned stride; 0 for invalid dims. */
+size_t smoe_blob_bytes(const smoe_dims* dims);
+size_t smoe_blob_stride(const smoe_dims* dims);
+/* The same two functions under their SMOE-Q4-era names. */
 size_t smoe_q4_blob_bytes(const smoe_dims* dims);
 size_t smoe_q4_blob_stride(const smoe_dims* dims);
 
@@ -189,7 +206,8 @@ int smoe_decode_layers(const smoe_dims* dims, int32_t n_layers, float* residual,
  *   residual     device fp32 [n_tok][d_model], += the MoE output per token
  * Each union expert's blob is streamed once per chunk; the grouped FFN runs on
  * MFMA with weights dequantised to fp16 (exact for min = -8*scale).  The
- * per-token mix is summed in rank order; no atomics. */
+ * per-token mix is summed in rank order; no atomics.  SMOE-Q4 blobs only
+ * (dims->quant_bits 2 returns SMOE_EINVAL). */
 int smoe_moe_prefill_chunk(const smoe_dims* dims, int32_t n_tok, const uint16_t* x,
                            const int32_t* topk_idx, const float* topk_w,
                            const void* const* expert_table, float* residual, int32_t* union_ids,

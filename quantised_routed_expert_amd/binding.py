@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libsmoe.so")
 SMOE_OK, SMOE_EINVAL, SMOE_EHIP, SMOE_ENOSLOT, SMOE_EBUSY, SMOE_ENOMEM = 0, -1, -2, -3, -4, -5
 
 EXPORTED = [
-    "smoe_last_error", "smoe_version", "smoe_q4_blob_bytes", "smoe_q4_blob_stride",
+    "smoe_last_error", "smoe_version", "smoe_blob_bytes", "smoe_blob_stride", "smoe_q4_blob_bytes",
+    "smoe_q4_blob_stride",
     "smoe_workspace_bytes", "smoe_route", "smoe_moe_decode", "smoe_moe_decode_slots",
     "smoe_decode_layers", "smoe_moe_prefill_chunk", "smoe_ring_create", "smoe_ring_acquire",
     "smoe_ring_release", "smoe_ring_stats", "smoe_ring_log", "smoe_ring_destroy", "smoe_ring_acquire_table",
@@ -34,7 +35,7 @@ class SmoeError(RuntimeError):
 class SmoeDims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("chunk", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("quant_bits", ctypes.c_int32)]
 
 
 class SmoeRingDesc(ctypes.Structure):
@@ -67,6 +68,8 @@ def lib():
         sig = {
             "smoe_last_error": (ctypes.c_char_p, []),
             "smoe_version": (ctypes.c_int32, []),
+            "smoe_blob_bytes": (S, [D]),
+            "smoe_blob_stride": (S, [D]),
             "smoe_q4_blob_bytes": (S, [D]),
             "smoe_q4_blob_stride": (S, [D]),
             "smoe_workspace_bytes": (I, [D, ctypes.c_int32, P(S)]),
@@ -103,7 +106,7 @@ def _check(code: int):
 
 def dims_struct(dims) -> SmoeDims:
     return SmoeDims(int(dims.d_model), int(dims.d_ff), int(dims.n_experts), int(dims.top_k), int(dims.chunk),
-                    1 if dims.norm_topk_prob else 0, float(dims.rms_eps))
+                    1 if dims.norm_topk_prob else 0, float(dims.rms_eps), int(getattr(dims, "bits", 4)))
 
 
 def _ptr(t):
@@ -123,11 +126,11 @@ def _stream(stream):
 
 
 def blob_bytes(dims) -> int:
-    return int(lib().smoe_q4_blob_bytes(ctypes.byref(dims_struct(dims))))
+    return int(lib().smoe_blob_bytes(ctypes.byref(dims_struct(dims))))
 
 
 def blob_stride(dims) -> int:
-    return int(lib().smoe_q4_blob_stride(ctypes.byref(dims_struct(dims))))
+    return int(lib().smoe_blob_stride(ctypes.byref(dims_struct(dims))))
 
 
 def workspace_bytes(dims, max_tokens: int) -> int:

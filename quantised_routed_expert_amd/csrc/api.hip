@@ -27,6 +27,9 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Code width of the dims' blobs (0 is read as 4).
+static int quant_bits(const smoe_dims* d) { return d->quant_bits == 0 ? 4 : d->quant_bits; }
+
 int check_dims(const smoe_dims* d) {
   if (!d) return fail(SMOE_EINVAL, "dims is NULL");
   if (d->d_model <= 0 || d->d_model > 8192 || d->d_model % 256)
@@ -41,7 +44,12 @@ int check_dims(const smoe_dims* d) {
   if (!(d->rms_eps >= 0.0f) || d->rms_eps > 1.0f) return fail(SMOE_EINVAL, "rms_eps out of range");
   if (d->d_model % 128 || d->d_ff % 128)
     return fail(SMOE_EINVAL, "d_model=%d and d_ff=%d must be multiples of 128", d->d_model, d->d_ff);
-  if (!decode_shape_supported(d->d_model, d->d_ff, d->chunk))
+  const int bits = quant_bits(d);
+  if (bits != 4 && bits != 2) return fail(SMOE_EINVAL, "quant_bits=%d must be 4 (or 0) or 2", d->quant_bits);
+  if (bits == 2 && (d->chunk != 64 || d->d_model % 512))
+    return fail(SMOE_EINVAL, "SMOE-Q2 needs chunk 64 and d_model a multiple of 512 (chunk=%d d_model=%d)",
+                d->chunk, d->d_model);
+  if (!decode_shape_supported(d->d_model, d->d_ff, d->chunk, bits))
     return fail(SMOE_EINVAL, "unsupported row split for d_model=%d d_ff=%d", d->d_model, d->d_ff);
   return SMOE_OK;
 }
@@ -90,7 +98,8 @@ static DecodeArgs decode_args(const smoe_dims* d, char* ws, const Workspace& L) 
   a.k = d->top_k;
   a.chunk = d->chunk;
   a.norm = d->norm_topk_prob ? 1 : 0;
-  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk);
+  a.bits = quant_bits(d);
+  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk, a.bits);
   a.h = reinterpret_cast<_Float16*>(ws + L.h);
   return a;
 }
@@ -103,17 +112,21 @@ extern "C" {
 
 const char* smoe_last_error(void) { return g_err; }
 
-int32_t smoe_version(void) { return 1; }
+int32_t smoe_version(void) { return 2; }
 
-size_t smoe_q4_blob_bytes(const smoe_dims* d) {
+size_t smoe_blob_bytes(const smoe_dims* d) {
   if (check_dims(d) != SMOE_OK) return 0;
-  return blob_layout(d->d_model, d->d_ff, d->chunk).bytes;
+  return blob_layout(d->d_model, d->d_ff, d->chunk, quant_bits(d)).bytes;
 }
 
-size_t smoe_q4_blob_stride(const smoe_dims* d) {
-  const size_t b = smoe_q4_blob_bytes(d);
+size_t smoe_blob_stride(const smoe_dims* d) {
+  const size_t b = smoe_blob_bytes(d);
   return (b + 16383) / 16384 * 16384;
 }
+
+size_t smoe_q4_blob_bytes(const smoe_dims* d) { return smoe_blob_bytes(d); }
+
+size_t smoe_q4_blob_stride(const smoe_dims* d) { return smoe_blob_stride(d); }
 
 int smoe_workspace_bytes(const smoe_dims* d, int32_t max_tokens, size_t* bytes) {
   g_err[0] = 0;
@@ -281,6 +294,7 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
                            size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (int e = check_dims(d)) return e;
+  if (quant_bits(d) != 4) return fail(SMOE_EINVAL, "prefill takes SMOE-Q4 blobs only (quant_bits=%d)", d->quant_bits);
   if (n_tok < 1 || n_tok > kMaxPrefillTokens)
     return fail(SMOE_EINVAL, "n_tok=%d must be in [1, %d]", n_tok, kMaxPrefillTokens);
   if (!x || !topk_idx || !topk_w || !expert_table || !residual || !union_ids || !union_count || !offsets || !perm)
@@ -311,7 +325,7 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
   a.E = d->n_experts;
   a.k = d->top_k;
   a.chunk = d->chunk;
-  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk);
+  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk, 4);
   hipError_t he = launch_prefill(a, (hipStream_t)stream);
   if (he != hipSuccess) return hip_fail(he, "prefill launch");
   return SMOE_OK;

@@ -14,9 +14,12 @@
 // run (each lane NSEG adjacent segments) makes every instruction touch each
 // line of the row at half width, which measured markedly slower.
 //
-// Affine folding: a 16-byte segment (32 codes) lies inside one chunk, so its
-// contribution is scale * sum(q x) + min * sum(x); sum(x) over the segment is
-// computed once per wave because every row of a wave uses the same columns.
+// Affine folding: a 16-byte segment (32 Q4 or 64 Q2 codes) lies inside one
+// chunk, so its contribution is scale * sum(q x) + min * sum(x); sum(x) over
+// the segment is computed once per wave because every row of a wave uses the
+// same columns.  The code width BITS (4: SMOE-Q4, 2: SMOE-Q2, the halved blobs
+// of the Optimizations page's "Q2 Vaults") is a template parameter: a Q2
+// segment holds twice the values, read in 16-value pair groups.
 #include <hip/hip_ext.h>
 
 #include "kernels.h"
@@ -41,37 +44,42 @@ namespace smoe {
 
 // Per-lane layout of one row: lane li owns the NSEG 16-byte code segments at
 // row bytes s * STRIDE + li * 16 (s < NSEG) and the (scale, min) record of the
-// chunk each falls in.  A segment (32 codes) never straddles a chunk, and two
-// segments of a lane are STRIDE >= 32 bytes apart, so each has its own record.
-template <int LR, int CHUNK>
+// chunk each falls in.  A segment (SEGV codes) never straddles a chunk (a chunk
+// holds >= 16 code bytes), and two segments of a lane are STRIDE >= 32 bytes
+// apart, so each has its own record.
+template <int LR, int CHUNK, int BITS>
 struct LaneRun {
-  static constexpr int STRIDE = LR * 16;  // bytes between a lane's segments
-  static constexpr int CB = CHUNK / 2;    // code bytes per chunk
+  static constexpr int STRIDE = LR * 16;      // bytes between a lane's segments
+  static constexpr int CB = CHUNK * BITS / 8; // code bytes per chunk
+  static constexpr int SEGV = 128 / BITS;     // values per segment
+  static constexpr int NQ = SEGV / 8;         // 16-byte pieces of a segment's 16-bit inputs
+  static constexpr int NDW = SEGV / 2;        // f16-pair dwords per segment
+  static_assert(CB >= 16 && CB % 16 == 0, "a segment must lie inside one chunk");
   __device__ static int chunk_of(int li, int s) { return (s * STRIDE + li * 16) / CB; }
 };
 
-// Pair-ordered f16 input of a lane's NSEG segments (32 values each, the
-// columns of its code segments: 32 * (s * LR + li) onwards) and the
+// Pair-ordered f16 input of a lane's NSEG segments (SEGV values each, the
+// columns of its code segments: SEGV * (s * LR + li) onwards) and the
 // per-segment sums, from bf16 (x) or pair-ordered f16 (h) storage.  The raw
 // loads are separate from the conversion so that the weight loads can be
 // issued in between.  `base` points at the lane's first segment; segments are
-// LR * 64 bytes apart (32 two-byte values per lane).
-template <int LR, int NSEG>
-__device__ __forceinline__ void load_raw(const void* base, uint4 (*raw)[4]) {
+// LR * NQ * 16 bytes apart (SEGV two-byte values per lane).
+template <int LR, int NSEG, int NQ>
+__device__ __forceinline__ void load_raw(const void* base, uint4 (*raw)[NQ]) {
 #pragma unroll
   for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      raw[s][q] = gload16(reinterpret_cast<const uint8_t*>(base) + (size_t)s * LR * 64 + q * 16);
+    for (int q = 0; q < NQ; ++q)
+      raw[s][q] = gload16(reinterpret_cast<const uint8_t*>(base) + (size_t)s * LR * NQ * 16 + q * 16);
 }
 
-template <int NSEG>
-__device__ __forceinline__ void pack_bf16_run(const uint4 (*raw)[4], uint32_t (*xp)[16], float* xseg) {
+template <int NSEG, int NQ>
+__device__ __forceinline__ void pack_bf16_run(const uint4 (*raw)[NQ], uint32_t (*xp)[NQ * 4], float* xseg) {
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
-    float v[32];
+    float v[NQ * 8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const uint32_t w4[4] = {raw[s][q].x, raw[s][q].y, raw[s][q].z, raw[s][q].w};
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -79,23 +87,31 @@ __device__ __forceinline__ void pack_bf16_run(const uint4 (*raw)[4], uint32_t (*
         v[8 * q + 2 * p + 1] = bf16_to_f32(w4[p] >> 16);
       }
     }
-    pack_segment(v, xp[s]);
-    xseg[s] = seg_sum(xp[s]);
+    if constexpr (NQ == 4) pack_segment(v, xp[s]);
+    else pack_segment_q2(v, xp[s]);
+    xseg[s] = seg_sum<NQ * 4>(xp[s]);
   }
 }
 
 // Pair-ordered f16 storage (the router's prepared x, or h) is used as is.
-template <int NSEG>
-__device__ __forceinline__ void pack_f16_run(const uint4 (*raw)[4], uint32_t (*hp)[16], float* xseg) {
+template <int NSEG, int NQ>
+__device__ __forceinline__ void pack_f16_run(const uint4 (*raw)[NQ], uint32_t (*hp)[NQ * 4], float* xseg) {
 #pragma unroll
   for (int s = 0; s < NSEG; ++s) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       hp[s][4 * q + 0] = raw[s][q].x; hp[s][4 * q + 1] = raw[s][q].y;
       hp[s][4 * q + 2] = raw[s][q].z; hp[s][4 * q + 3] = raw[s][q].w;
     }
-    xseg[s] = seg_sum(hp[s]);
+    xseg[s] = seg_sum<NQ * 4>(hp[s]);
   }
+}
+
+// One 16-byte code segment's contribution for code width BITS.
+template <int BITS>
+__device__ __forceinline__ float seg_contrib_b(const uint4& c, const uint32_t* xp, float xseg, uint32_t params) {
+  if constexpr (BITS == 4) return seg_contrib(c, xp, xseg, params);
+  else return seg_contrib_q2(c, xp, xseg, params);
 }
 
 // Blob of rank r: passed by value, published by the router, or looked up in the
@@ -110,12 +126,12 @@ __device__ __forceinline__ const void* expert_pointer(const DecodeArgs& a, int r
 
 // The NP * (64 / LR) rows of one wave (all in expert r, starting at row
 // n_begin): every weight load is issued before any is consumed.
-template <int LR, int NSEG, int NP, int CHUNK>
+template <int LR, int NSEG, int NP, int CHUNK, int BITS>
 __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t* blob, int r, int n_begin, int li,
-                                             int grp, const uint4 (*xraw)[4]) {
-  using Run = LaneRun<LR, CHUNK>;
+                                             int grp, const uint4 (*xraw)[LaneRun<LR, CHUNK, BITS>::NQ]) {
+  using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;
-  const size_t row_bytes = (size_t)a.d / 2;
+  const size_t row_bytes = (size_t)a.d * BITS / 8;
   const size_t prow_bytes = (size_t)(a.d / CHUNK) * 4;
   const size_t first = (size_t)(n_begin + grp);
   const uint8_t* gcodes = blob + first * row_bytes + li * 16;
@@ -142,24 +158,24 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
   __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
 
   // this lane's input columns as f16 pairs, converted while the weights stream
-  uint32_t xp[NSEG][16];
+  uint32_t xp[NSEG][Run::NDW];
   float xseg[NSEG];
-  if (a.px) pack_f16_run<NSEG>(xraw, xp, xseg);
-  else pack_bf16_run<NSEG>(xraw, xp, xseg);
+  if (BITS == 4 && a.px) pack_f16_run<NSEG, Run::NQ>(xraw, xp, xseg);
+  else pack_bf16_run<NSEG, Run::NQ>(xraw, xp, xseg);
 
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int s = 0; s < NSEG; ++s) {
-      g += seg_contrib(cg[p][s], xp[s], xseg[s], pg[p][s]);
-      u += seg_contrib(cu[p][s], xp[s], xseg[s], pu[p][s]);
+      g += seg_contrib_b<BITS>(cg[p][s], xp[s], xseg[s], pg[p][s]);
+      u += seg_contrib_b<BITS>(cu[p][s], xp[s], xseg[s], pu[p][s]);
     }
     g = group_sum<LR>(g);
     u = group_sum<LR>(u);
     if (li == 0) {
       const int n = n_begin + p * P + grp;
-      a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)(silu_f32(g) * u);
+      a.h[(size_t)r * a.f + pair_index<BITS>(n)] = (_Float16)(silu_f32(g) * u);
     }
   }
 }
@@ -172,8 +188,9 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
 // and finds the blobs in src.table; workgroup 0 also publishes ids, weights and
 // pointers.  grid = ceil(k * d_ff / (4 * rows per wave)) workgroups of 4 waves.
 // ---------------------------------------------------------------------------
-template <int LR, int NSEG, int NP, int CHUNK>
+template <int LR, int NSEG, int NP, int CHUNK, int BITS>
 __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(DecodeArgs a) {
+  using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;  // rows per pass
   constexpr int RPW = NP * P;    // rows per wave
   __shared__ const void* s_ptr[kMaxTopK];
@@ -193,9 +210,10 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
   } else if (tid < a.k) {
     s_ptr[tid] = expert_pointer(a, tid);
   }
-  uint4 xraw[NSEG][4];
-  if (a.px) load_raw<LR, NSEG>(a.px + li * 32, xraw);
-  else load_raw<LR, NSEG>(a.x + li * 32, xraw);
+  // (the router's pair-ordered f16 copy of x is in Q4's pair order)
+  uint4 xraw[NSEG][Run::NQ];
+  if (BITS == 4 && a.px) load_raw<LR, NSEG, Run::NQ>(a.px + li * Run::SEGV, xraw);
+  else load_raw<LR, NSEG, Run::NQ>(a.x + li * Run::SEGV, xraw);
   if (fused && tid < kMaxExperts) {  // stored after the input loads are issued
     // padding, and a NaN logit (from a non-finite residual), rank as -inf
     const double l = (tid < a.E && lv == lv) ? lv : -__builtin_inf();
@@ -217,11 +235,11 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
     const int n_begin = row0 - r * a.f;
     const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
     if (blob) {
-      gate_up_rows<LR, NSEG, NP, CHUNK>(a, blob, r, n_begin, li, grp, xraw);
+      gate_up_rows<LR, NSEG, NP, CHUNK, BITS>(a, blob, r, n_begin, li, grp, xraw);
     } else {  // an index outside [0, E) or a null table entry: the rank contributes nothing
       for (int it = lane; it < RPW; it += kWave) {
         const int n = n_begin + it;
-        a.h[(size_t)r * a.f + (n & ~7) + pair_slot(n & 7)] = (_Float16)0.0f;
+        a.h[(size_t)r * a.f + pair_index<BITS>(n)] = (_Float16)0.0f;
       }
     }
   }
@@ -249,9 +267,9 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
 // weight loads of its rows before it computes.
 // grid = ceil(d / rows per workgroup), block = 64 * min(k, 8).
 // ---------------------------------------------------------------------------
-template <int LR, int NSEG, int NPASS, int CHUNK>
+template <int LR, int NSEG, int NPASS, int CHUNK, int BITS>
 __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
-  using Run = LaneRun<LR, CHUNK>;
+  using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;
   constexpr int ROWS = NPASS * P;
   __shared__ float ylds[kMaxTopK][ROWS];
@@ -296,7 +314,7 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
 
   const int li = lane % LR, grp = lane / LR;
   const int n0 = blockIdx.x * ROWS;
-  const size_t row_bytes = (size_t)a.f / 2;
+  const size_t row_bytes = (size_t)a.f * BITS / 8;
   const size_t prow_bytes = (size_t)(a.f / CHUNK) * 4;
 
   for (int r = wave, it = 0; r < a.k; r += nw, ++it) {
@@ -307,8 +325,8 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     }
     const uint8_t* codes = blob + a.lay.down_codes + li * 16;
     const uint8_t* par = blob + a.lay.down_params;
-    uint4 hraw[NSEG][4];
-    load_raw<LR, NSEG>(a.h + (size_t)r * a.f + li * 32, hraw);
+    uint4 hraw[NSEG][Run::NQ];
+    load_raw<LR, NSEG, Run::NQ>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
     __builtin_amdgcn_sched_barrier(0);  // h first: the math can start when it lands
     uint4 c[NPASS][NSEG];
     uint32_t pr[NPASS][NSEG];
@@ -326,15 +344,15 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
     // h_r for this lane's columns (already pair-ordered) and its segment sums
-    uint32_t hp[NSEG][16];
+    uint32_t hp[NSEG][Run::NDW];
     float xseg[NSEG];
-    pack_f16_run<NSEG>(hraw, hp, xseg);
+    pack_f16_run<NSEG, Run::NQ>(hraw, hp, xseg);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       float y = 0.f;
 #pragma unroll
       for (int s = 0; s < NSEG; ++s)
-        y += seg_contrib(c[p][s], hp[s], xseg[s], pr[p][s]);
+        y += seg_contrib_b<BITS>(c[p][s], hp[s], xseg[s], pr[p][s]);
       y = group_sum<LR>(y);
       if (li == 0) ylds[r][p * P + grp] = y;
     }
@@ -362,17 +380,24 @@ struct RowSplit {
 };
 
 // LR = the largest power of two <= 64 dividing the row's segment count.
-static RowSplit split_row(int cols) {
-  const int segs = cols / 32;  // 16-byte segments per row
+static RowSplit split_row(int cols, int bits) {
+  const int segs = cols * bits / 128;  // 16-byte segments per row
   int lr = pow2_part(segs);
   if (lr > 64) lr = 64;
   return {lr, segs / lr};
 }
 
-bool decode_shape_supported(int d, int f, int chunk) {
-  if (chunk != 32 && chunk != 64) return false;
-  if (d % 256 || f % 64) return false;
-  const RowSplit g = split_row(d), dn = split_row(f);
+bool decode_shape_supported(int d, int f, int chunk, int bits) {
+  if (bits == 4) {
+    if (chunk != 32 && chunk != 64) return false;
+    if (d % 256 || f % 64) return false;
+  } else if (bits == 2) {
+    if (chunk != 64) return false;  // a Q2 segment (64 codes) is one chunk of 64
+    if (d % 512 || f % 128) return false;
+  } else {
+    return false;
+  }
+  const RowSplit g = split_row(d, bits), dn = split_row(f, bits);
   return g.lr >= 8 && g.nseg <= 4 && dn.lr >= 2 && dn.nseg <= 4;
 }
 
@@ -390,9 +415,12 @@ bool decode_shape_supported(int d, int f, int chunk) {
   switch (V) { SMOE_CASE(1, NAME, __VA_ARGS__) SMOE_CASE(2, NAME, __VA_ARGS__)             \
                SMOE_CASE(4, NAME, __VA_ARGS__)                                             \
                default: return hipErrorInvalidValue; }
-#define SMOE_CHUNK_SWITCH(V, ...)                                                           \
-  switch (V) { SMOE_CASE(32, CHUNK, __VA_ARGS__) SMOE_CASE(64, CHUNK, __VA_ARGS__)         \
-               default: return hipErrorInvalidValue; }
+// (code width, chunk): SMOE-Q4 with chunks of 32 or 64, SMOE-Q2 with chunks of 64
+#define SMOE_FORMAT_SWITCH(B, C, ...)                                                      \
+  if ((B) == 4 && (C) == 32) { constexpr int BITS = 4, CHUNK = 32; __VA_ARGS__; }          \
+  else if ((B) == 4 && (C) == 64) { constexpr int BITS = 4, CHUNK = 64; __VA_ARGS__; }     \
+  else if ((B) == 2 && (C) == 64) { constexpr int BITS = 2, CHUNK = 64; __VA_ARGS__; }     \
+  else return hipErrorInvalidValue;
 
 // Rows per wave of the gate/up kernel: NP passes of 64/LR rows, the largest
 // NP <= SMOE_GU_ROWS_MAX that divides d_ff and leaves >= SMOE_GU_MIN_WAVES waves.
@@ -405,25 +433,25 @@ static int gate_up_np(int lr, int total, int f) {
 }
 
 hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-  const RowSplit sp = split_row(a.d);
+  const RowSplit sp = split_row(a.d, a.bits);
   const int total = a.k * a.f;
   const int np = gate_up_np(sp.lr, total, a.f);
   const int waves = total / (np * (64 / sp.lr));
   // the launch bounds and the selection's thread count are SMOE_GU_WAVES waves
   constexpr int nw = SMOE_GU_WAVES;
   const dim3 grid((waves + nw - 1) / nw);
-  SMOE_CHUNK_SWITCH(a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
+  SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
       if (start || stop) {
-        hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(64 * nw), 0, s, start,
-                              stop, 0, a);
+        hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS>), grid, dim3(64 * nw), 0, s,
+                              start, stop, 0, a);
       } else {
-        hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK>), grid, dim3(64 * nw), 0, s, a);
+        hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS>), grid, dim3(64 * nw), 0, s, a);
       }))));
   return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
-  const RowSplit sp = split_row(a.f);
+  const RowSplit sp = split_row(a.f, a.bits);
   const int P = 64 / sp.lr;
   int np = 1;
   while (np * 2 <= SMOE_DN_PASSES_MAX && a.d / (P * np * 2) >= SMOE_DN_MIN_WG) np *= 2;
@@ -431,8 +459,8 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   if (a.d % rows) return hipErrorInvalidValue;  // every workgroup owns full rows
   const int nw = a.k < 8 ? a.k : 8;
   const dim3 grid(a.d / rows);
-  SMOE_CHUNK_SWITCH(a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NPASS,
-      hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK>), grid, dim3(64 * nw), 0, s, a)))));
+  SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NPASS,
+      hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS>), grid, dim3(64 * nw), 0, s, a)))));
   return hipGetLastError();
 }
 

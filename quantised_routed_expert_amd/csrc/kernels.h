@@ -270,16 +270,17 @@ struct DecodeArgs {
   FusedTopk sel;
   const float* w;           // [k] mixing weights (device), read by the down kernel
   const void* const* ptrs;   // [k] device blob pointers from the router, or null
-  _Float16* h;              // [k][d_ff], pair-ordered within groups of 8
+  _Float16* h;              // [k][d_ff], pair-ordered within groups of 8 (Q4) or 16 (Q2)
   float* residual;          // [d]
   const uint8_t* pf_base;   // next layer's router [E][d] bf16 to pull into cache, or null
   int d, f, E, k, chunk, norm;
+  int bits;                 // code width: 4 (SMOE-Q4) or 2 (SMOE-Q2)
   BlobLayout lay;
 };
 
 hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t start = nullptr,
                                  hipEvent_t stop = nullptr);
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s);
-bool decode_shape_supported(int d, int f, int chunk);
+bool decode_shape_supported(int d, int f, int chunk, int bits);
 
 }  // namespace smoe

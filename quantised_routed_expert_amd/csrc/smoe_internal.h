@@ -14,17 +14,19 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxPrefillTokens = 64;
 
-// Byte offsets of the sections of one SMOE-Q4 expert blob (layout in smoe.h).
+// Byte offsets of the sections of one SMOE-Q4 / SMOE-Q2 expert blob (layout
+// in smoe.h); `bits` is the code width.
 struct BlobLayout {
   size_t up_codes, down_codes, gate_params, up_params, down_params, bytes;
 };
 
-inline BlobLayout blob_layout(int d, int f, int chunk) {
+inline BlobLayout blob_layout(int d, int f, int chunk, int bits) {
   BlobLayout b;
   const size_t df = (size_t)d * (size_t)f;
-  b.up_codes = df / 2;
-  b.down_codes = df;
-  b.gate_params = df + df / 2;
+  const size_t mat = df * (size_t)bits / 8;  // code bytes of one matrix
+  b.up_codes = mat;
+  b.down_codes = 2 * mat;
+  b.gate_params = 3 * mat;
   b.up_params = b.gate_params + df / chunk * 4;
   b.down_params = b.up_params + df / chunk * 4;
   b.bytes = b.down_params + df / chunk * 4;
@@ -82,6 +84,17 @@ __device__ __forceinline__ uint32_t f16_bits(float v) {
 // products: stored slot i holds element kPairSlot^-1(i); element j goes to
 // slot (j < 4 ? 2j : 2(j-4)+1), so dword p of the group holds (e_p, e_{p+4}).
 __device__ __forceinline__ int pair_slot(int j) { return j < 4 ? 2 * j : 2 * (j - 4) + 1; }
+
+// The same for SMOE-Q2's groups of 16: dword p of a group holds (e_p, e_{p+8}).
+__device__ __forceinline__ int pair_slot16(int j) { return j < 8 ? 2 * j : 2 * (j - 8) + 1; }
+
+// Pair order of code width BITS (groups of 8 for Q4, 16 for Q2): the storage
+// index of element n of a vector.
+template <int BITS>
+__device__ __forceinline__ int pair_index(int n) {
+  if (BITS == 4) return (n & ~7) + pair_slot(n & 7);
+  return (n & ~15) + pair_slot16(n & 15);
+}
 
 // ---------------------------------------------------------------------------
 // Wave reductions.  Within a row of 16 lanes the partial sums move with DPP
@@ -185,11 +198,44 @@ __device__ __forceinline__ float seg_contrib(const uint4& c, const uint32_t* xp,
   return fmaf(s, sq, m * xseg);
 }
 
-// Sum of the 32 values of one pair-ordered f16 segment (dot2 against ones).
+// 2-bit pairs.  A dword w of SMOE-Q2 codes holds elements e0..e15 (e_j in
+// bits 2j..2j+1).  Masking a 2-bit field at bit 2i of each half gives the fp16
+// subnormals (e_i, e_{i+8}) * 4^i * 2^-24 exactly, and w >> 8 brings
+// (e_{i+4}, e_{i+12}) to the same positions.  With the input in 16-group pair
+// order (dword p holds (x_p, x_{p+8})), four accumulators a_i collect the
+// products of field i, and sum q x = 2^24 * (a0 + a1/4 + a2/16 + a3/64).
+__device__ __forceinline__ void crumb16_dot(uint32_t w, const uint32_t* xp, float* acc) {
+  const uint32_t w8 = w >> 8;
+  acc[0] = dot2(w & 0x00030003u, xp[0], acc[0]);
+  acc[1] = dot2(w & 0x000C000Cu, xp[1], acc[1]);
+  acc[2] = dot2(w & 0x00300030u, xp[2], acc[2]);
+  acc[3] = dot2(w & 0x00C000C0u, xp[3], acc[3]);
+  acc[0] = dot2(w8 & 0x00030003u, xp[4], acc[0]);
+  acc[1] = dot2(w8 & 0x000C000Cu, xp[5], acc[1]);
+  acc[2] = dot2(w8 & 0x00300030u, xp[6], acc[2]);
+  acc[3] = dot2(w8 & 0x00C000C0u, xp[7], acc[3]);
+}
+
+// Contribution of one 16-byte SMOE-Q2 segment (64 codes = one chunk of 64):
+// scale * sum(q x) + min * sum(x); xp: 32 pair-ordered input dwords.
+__device__ __forceinline__ float seg_contrib_q2(const uint4& c, const uint32_t* xp, float xseg, uint32_t params) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  crumb16_dot(c.x, xp + 0, acc);
+  crumb16_dot(c.y, xp + 8, acc);
+  crumb16_dot(c.z, xp + 16, acc);
+  crumb16_dot(c.w, xp + 24, acc);
+  const float sq = fmaf(fmaf(acc[3], 0.25f, acc[2]), 0.0625f, fmaf(acc[1], 0.25f, acc[0])) * 16777216.0f;
+  const float s = __uint_as_float(params << 16);
+  const float m = __uint_as_float(params & 0xFFFF0000u);
+  return fmaf(s, sq, m * xseg);
+}
+
+// Sum of the 2 * NDW values of NDW pair-ordered f16 dwords (dot2 against ones).
+template <int NDW = 16>
 __device__ __forceinline__ float seg_sum(const uint32_t* xp) {
   float a = 0.f, b = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; i += 2) {
+  for (int i = 0; i < NDW; i += 2) {
     a = dot2(xp[i], 0x3C003C00u, a);
     b = dot2(xp[i + 1], 0x3C003C00u, b);
   }
@@ -204,6 +250,16 @@ __device__ __forceinline__ void pack_segment(const float* v, uint32_t* xp) {
     const float* e = v + 8 * g;
 #pragma unroll
     for (int p = 0; p < 4; ++p) xp[4 * g + p] = f16_bits(e[p]) | (f16_bits(e[p + 4]) << 16);
+  }
+}
+
+// The same for a 64-value SMOE-Q2 segment in 16-group pair order.
+__device__ __forceinline__ void pack_segment_q2(const float* v, uint32_t* xp) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float* e = v + 16 * g;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) xp[8 * g + p] = f16_bits(e[p]) | (f16_bits(e[p + 8]) << 16);
   }
 }
 

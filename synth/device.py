@@ -1,4 +1,4 @@
-"""Device-side synthetic stacks: draws SMOE-Q4 vaults in HBM with
+"""Device-side synthetic stacks: draws SMOE-Q4 / SMOE-Q2 vaults in HBM with
 libsmoe_synth.so (the device twin of synth.gen's code and scale streams) and
 uploads host-drawn router weights, biases and hidden states."""
 from __future__ import annotations
@@ -25,8 +25,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.synth_fill_experts.restype = ctypes.c_int
         L.synth_fill_experts.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
-                                         ctypes.c_void_p]
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]
         L.synth_stream_read.restype = ctypes.c_int
         L.synth_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -36,7 +36,7 @@ def lib():
 
 def fill_experts(seed, dims, layer, e_begin, n_exp, dst_ptr, stride, stream=None):
     s = torch.cuda.current_stream().cuda_stream if stream is None else stream.cuda_stream
-    rc = lib().synth_fill_experts(int(seed), dims.d_model, dims.d_ff, dims.chunk, int(layer), int(e_begin),
+    rc = lib().synth_fill_experts(int(seed), dims.d_model, dims.d_ff, dims.chunk, dims.bits, int(layer), int(e_begin),
                                   int(n_exp), int(dst_ptr), int(stride), s)
     if rc != 0:
         raise RuntimeError(f"synth_fill_experts failed: {rc}")

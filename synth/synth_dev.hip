@@ -1,14 +1,15 @@
-// Device twin of synth/gen.py's expert streams: fills SMOE-Q4 blobs with the
+// Device twin of synth/gen.py's expert streams: fills SMOE-Q4 or SMOE-Q2 blobs with the
 // seeded codes and per-chunk (scale, min) pairs, bit for bit as the numpy
 // generator draws them, so that a whole vault can be drawn in HBM.
 //
 // SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): word i of the stream with
 // key K is mix64(K + (i + 1) * GAMMA).  Keys: mix64(mix64(seed + GAMMA) ^ tag),
 // tag = kind << 56 | mat << 48 | layer << 24 | expert.
-// Codes: the little-endian bytes of the words of stream (kind 1, mat).
+// Codes: the little-endian bytes of the words of stream (kind 1 for Q4, kind 6
+// for Q2, mat).
 // Scales: s = bf16(0.002 + 0.008 * U), U = (word >> 11) * 2^-53, two separately
 // rounded double operations (this file is built with -ffp-contract=off);
-// min = -8 * s.  Holds no arithmetic of the MoE layer.
+// min = -8 * s (Q4) or -2 * s (Q2).  Holds no arithmetic of the MoE layer.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,7 +56,7 @@ struct Geo {
 
 // One thread per 8-byte unit of a blob: code words first, then 8-byte pairs of
 // (scale, min) records (two chunks), then zero padding.
-__global__ void fill_kernel(uint64_t seed, int layer, int e_begin, int chunk, Geo g, uint8_t* dst) {
+__global__ void fill_kernel(uint64_t seed, int layer, int e_begin, int bits, Geo g, uint8_t* dst) {
   const int eo = blockIdx.y;
   const int expert = e_begin + eo;
   uint8_t* blob = dst + (size_t)eo * g.stride;
@@ -67,7 +68,7 @@ __global__ void fill_kernel(uint64_t seed, int layer, int e_begin, int chunk, Ge
     bool done = false;
     for (int m = 0; m < 3 && !done; ++m) {
       if (byte >= g.code_off[m] && byte < g.code_off[m] + g.code_words[m] * 8) {
-        const uint64_t key = stream_key(seed, 1, layer, expert, m);
+        const uint64_t key = stream_key(seed, bits == 4 ? 1 : 6, layer, expert, m);
         out = stream_word(key, (byte - g.code_off[m]) / 8);
         done = true;
       } else if (byte >= g.par_off[m] && byte < g.par_off[m] + g.par_count[m] * 4) {
@@ -81,7 +82,8 @@ __global__ void fill_kernel(uint64_t seed, int layer, int e_begin, int chunk, Ge
           const double s = 0.002 + t;
           const uint16_t sb = bf16_bits(s);
           const float sv = __uint_as_float((uint32_t)sb << 16);
-          const uint16_t mb = (uint16_t)(__float_as_uint(-8.0f * sv) >> 16);
+          const float mul = bits == 4 ? -8.0f : -2.0f;
+          const uint16_t mb = (uint16_t)(__float_as_uint(mul * sv) >> 16);
           out |= ((uint64_t)sb | ((uint64_t)mb << 16)) << (32 * h);
         }
         done = true;
@@ -95,12 +97,14 @@ __global__ void fill_kernel(uint64_t seed, int layer, int e_begin, int chunk, Ge
 
 extern "C" {
 
-// Fills n_exp blobs of `layer`, experts e_begin.., at dst + i * stride.
+// Fills n_exp blobs of `layer`, experts e_begin.., at dst + i * stride, with
+// codes of `bits` (4 or 2) bits.
 // Returns 0, or -1 for bad arguments, -2 for a HIP launch error.
-int synth_fill_experts(uint64_t seed, int d_model, int d_ff, int chunk, int layer, int e_begin, int n_exp,
-                       void* dst, size_t stride, void* stream) {
+int synth_fill_experts(uint64_t seed, int d_model, int d_ff, int chunk, int bits, int layer, int e_begin,
+                       int n_exp, void* dst, size_t stride, void* stream) {
   if (d_model <= 0 || d_ff <= 0 || (chunk != 32 && chunk != 64) || n_exp < 0 || !dst) return -1;
-  if ((int64_t)d_model * d_ff % 32 != 0 || d_model % chunk || d_ff % chunk) return -1;
+  if (bits != 4 && bits != 2) return -1;
+  if ((int64_t)d_model * d_ff % 64 != 0 || d_model % chunk || d_ff % chunk) return -1;
   if (n_exp == 0) return 0;
   Geo g;
   const int64_t d = d_model, f = d_ff;
@@ -110,8 +114,8 @@ int synth_fill_experts(uint64_t seed, int d_model, int d_ff, int chunk, int laye
   int64_t pos = 0;
   for (int m = 0; m < 3; ++m) {
     g.code_off[m] = pos;
-    g.code_words[m] = g.rows[m] * g.cols[m] / 16;
-    pos += g.rows[m] * g.cols[m] / 2;
+    g.code_words[m] = g.rows[m] * g.cols[m] * bits / 64;
+    pos += g.rows[m] * g.cols[m] * bits / 8;
   }
   for (int m = 0; m < 3; ++m) {
     g.par_off[m] = pos;
@@ -128,7 +132,7 @@ int synth_fill_experts(uint64_t seed, int d_model, int d_ff, int chunk, int laye
   int bx = (int)((units + 255) / 256);
   if (bx > 4096) bx = 4096;
   hipLaunchKernelGGL(fill_kernel, dim3(bx, n_exp), dim3(256), 0, (hipStream_t)stream, (uint64_t)seed, layer,
-                     e_begin, chunk, g, reinterpret_cast<uint8_t*>(dst));
+                     e_begin, bits, g, reinterpret_cast<uint8_t*>(dst));
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

@@ -32,11 +32,19 @@ def test_library_exports_every_declared_symbol():
 def test_host_only_queries():
     import synth
     lib = smoe.lib()
-    assert lib.smoe_version() == 1
-    for wl, blob, stride in ((synth.CONFIGS[0], 61440, 65536), (synth.CONFIGS[2], 10616832, 10616832)):
-        assert smoe.blob_bytes(wl.dims) == blob
-        assert smoe.blob_stride(wl.dims) == stride
+    assert lib.smoe_version() == 2
+    for wl, blob, stride in ((synth.CONFIGS[0], 61440, 65536), (synth.CONFIGS[2], 10616832, 10616832),
+                             (synth.Q2_WORKLOADS[0], 5898240, 5898240)):
+        assert smoe.blob_bytes(wl.dims) == blob == synth.blob_sections(wl.dims)["bytes"]
+        assert smoe.blob_stride(wl.dims) == stride == synth.blob_sections(wl.dims)["stride"]
         assert smoe.workspace_bytes(wl.dims, 1) > 0
+    # SMOE-Q2 needs chunk 64 and d_model % 512 == 0; quant_bits must be 2 or 4
+    for bad_q2 in (synth.Q2_WORKLOADS[0].dims.replace(chunk=32), synth.Dims(768, 256, 16, 4, 64, bits=2)):
+        try:
+            smoe.workspace_bytes(bad_q2, 1)
+            raise AssertionError("expected SmoeError")
+        except smoe.SmoeError as e:
+            assert e.code == -1 and "Q2" in str(e)
     bad = synth.CONFIGS[0].dims.replace(chunk=48)
     try:
         smoe.workspace_bytes(bad, 1)

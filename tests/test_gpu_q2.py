@@ -1,0 +1,165 @@
+"""SMOE-Q2 decode on the GPU (the 2-bit vault of the Optimizations page, "Q2
+Vaults -- the Next 2x, Twice Over"): the device generator, per-layer and
+chained decode against the CPU oracle, ring-backed decode against resident
+decode and the oracle's LRU run, and the argument checks, all through the C
+ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantised_routed_expert_amd as smoe
+import synth
+from synth.device import DeviceStack, fill_experts
+from tests.gpu_common import (LazyExperts, bits_u16, check_moe_output, need_gpu, random_residual, say,
+                              topk_gap_ok)
+from tests.test_gpu_decode import _decode_one_layer
+from tests.test_gpu_ring import make_ring, resident_decode, ring_decode
+
+pytestmark = pytest.mark.gpu
+
+Q2 = {
+    "small": synth.Dims(512, 256, 16, 4, 64, bits=2),
+    "ragged": synth.Dims(1536, 384, 24, 3, 64, bits=2),
+    "q30b": synth.Dims(2048, 768, 128, 8, 64, bits=2),
+    "q235b": synth.Dims(4096, 1536, 128, 8, 64, bits=2),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    torch.cuda.init()
+
+
+def test_q2_device_generator_matches_host():
+    for name, dims, layer, experts in (("small", Q2["small"], 0, range(16)),
+                                      ("q235b", Q2["q235b"], 93, (0, 127))):
+        say(f"[q2-synth] {name} layer {layer}")
+        stride = synth.blob_sections(dims)["stride"]
+        buf = torch.empty(len(experts) * stride, dtype=torch.uint8, device="cuda")
+        for i, e in enumerate(experts):
+            fill_experts(1337, dims, layer, e, 1, buf.data_ptr() + i * stride, stride)
+        got = buf.cpu().numpy()
+        for i, e in enumerate(experts):
+            assert np.array_equal(got[i * stride:(i + 1) * stride], synth.pack_blob(1337, dims, layer, e)), (name, e)
+
+
+@pytest.mark.parametrize("shape,layers,tokens", [("small", 1, 4), ("ragged", 2, 3), ("q30b", 2, 2),
+                                                 ("q235b", 1, 2)])
+def test_q2_decode_layer_parity(shape, layers, tokens):
+    dims = Q2[shape]
+    say(f"[q2-decode] {shape} layers={layers} tokens={tokens}")
+    stack = DeviceStack(1337, dims, layers)
+    rng = np.random.default_rng(17)
+    worst = 0.0
+    for L in range(layers):
+        experts = LazyExperts(1337, dims, L)
+        for t in range(tokens):
+            res = random_residual(rng, 1, dims.d_model, scale=2.0)[0]
+            xb, ig, wg, r_out = _decode_one_layer(dims, stack, L, res, slots=(t % 2 == 1))
+            ref = oracle.moe_layer(res.astype(np.float64), stack.router_bits[L], experts, dims)
+            assert np.array_equal(xb, ref["x_bits"])
+            assert list(ig) == ref["idx"]
+            assert np.allclose(wg, ref["w"], rtol=2e-6, atol=1e-7)
+            y = r_out.astype(np.float64) - res.astype(np.float64)
+            worst = max(worst, check_moe_output(y, ref["y"], f"q2 {shape} L{L} t{t}"))
+    say(f"[q2-decode] {shape}: worst rel-L2 {worst:.2e}")
+
+
+def test_q2_special_routings_and_size_bounds():
+    base = Q2["small"]
+    rng = np.random.default_rng(18)
+    for dims in (base.replace(top_k=1), base.replace(top_k=16), base.replace(norm_topk_prob=False),
+                 base.replace(d_model=8192, d_ff=128), base.replace(d_ff=8192)):
+        say(f"[q2-special] {dims}")
+        stack = DeviceStack(1337, dims, 1)
+        experts = LazyExperts(1337, dims, 0)
+        res = random_residual(rng, 1, dims.d_model)[0]
+        xb, ig, wg, r_out = _decode_one_layer(dims, stack, 0, res)
+        ref = oracle.moe_layer(res.astype(np.float64), stack.router_bits[0], experts, dims)
+        assert list(ig) == ref["idx"]
+        check_moe_output(r_out.astype(np.float64) - res, ref["y"], str(dims))
+
+
+def test_q2_decode_layers_chain_matches_per_layer_calls_and_oracle():
+    dims = Q2["q30b"]
+    n_layers = 5
+    stack = DeviceStack(1337, dims, n_layers)
+    h0 = synth.hidden_bf16(1337, 2, dims.d_model)
+    r = torch.from_numpy(h0.copy()).cuda()
+    x_rec = torch.empty((n_layers, dims.d_model), dtype=torch.int16, device="cuda")
+    i_rec = torch.empty((n_layers, dims.top_k), dtype=torch.int32, device="cuda")
+    w_rec = torch.empty((n_layers, dims.top_k), dtype=torch.float32, device="cuda")
+    smoe.decode_layers(dims, n_layers, r, stack.router, None, stack.tables, smoe.workspace(dims, 1), x_rec,
+                       i_rec, w_rec)
+    torch.cuda.synchronize()
+    chain = r.cpu().numpy()
+    res = h0.copy()
+    for L in range(n_layers):
+        xb, ig, wg, res = _decode_one_layer(dims, stack, L, res)
+        assert np.array_equal(xb, bits_u16(x_rec)[L])
+        assert np.array_equal(ig, i_rec.cpu().numpy()[L])
+        assert np.array_equal(wg, w_rec.cpu().numpy()[L])
+    assert np.array_equal(res, chain)
+    ro = h0.astype(np.float64)
+    for L in range(n_layers):
+        ref = oracle.moe_layer(ro, stack.router_bits[L], LazyExperts(1337, dims, L), dims)
+        gi = i_rec.cpu().numpy()[L].tolist()
+        if gi != ref["idx"]:
+            assert topk_gap_ok(ref["logits"], gi, ref["idx"], dims.top_k, 1e-4), f"layer {L}"
+            say(f"[q2-chain] near-tie flip at layer {L}; stopping comparison")
+            return
+        ro = ref["r_out"]
+    rel = np.linalg.norm(chain - ro) / np.linalg.norm(ro - h0)
+    say(f"[q2-chain] final residual rel error (vs MoE delta) {rel:.2e}")
+    assert rel <= 2e-3
+
+
+def test_q2_decode_is_deterministic():
+    dims = Q2["q235b"]
+    stack = DeviceStack(1337, dims, 2)
+    h0 = synth.hidden_bf16(1337, 3, dims.d_model)
+    outs = []
+    for _ in range(3):
+        r = torch.from_numpy(h0.copy()).cuda()
+        smoe.decode_layers(dims, 2, r, stack.router, None, stack.tables, smoe.workspace(dims, 1))
+        torch.cuda.synchronize()
+        outs.append(r.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("n_slots", [64, 120])
+def test_q2_ring_log_matches_oracle_lru_and_output_matches_resident(n_slots):
+    dims = synth.Dims(512, 128, 128, 8, 64, bits=2)
+    n_layers, n_tok = 5, 10
+    stack = DeviceStack(1337, dims, n_layers)
+    hidden = synth.markov_hidden(1337, n_tok, dims.d_model)
+    ring, keep = make_ring(dims, stack, n_slots)
+    routing, got = ring_decode(dims, stack, ring, hidden)
+    log = ring.log(1 << 20)
+    stats = ring.stats()
+    ring.destroy()
+    ref_events, (h, m, ev) = oracle.ring_trace(routing, n_slots)
+    assert [e[1:] for e in ref_events] == log
+    assert (stats["hits"], stats["misses"], stats["evictions"]) == (h, m, ev)
+    assert stats["h2d_bytes"] == m * stack.blob_bytes == m * synth.blob_sections(dims)["bytes"]
+    say(f"[q2-ring] slots={n_slots}: hits {h} misses {m} evictions {ev}")
+    assert np.array_equal(got, resident_decode(dims, stack, hidden))
+
+
+def test_q2_argument_checks():
+    dims = Q2["small"]
+    ws = smoe.workspace(dims, 4)
+    x = torch.zeros((4, dims.d_model), dtype=torch.int16, device="cuda")
+    idx = torch.zeros((4, dims.top_k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((4, dims.top_k), dtype=torch.float32, device="cuda")
+    table = torch.zeros(dims.n_experts, dtype=torch.int64, device="cuda")
+    r = torch.zeros((4, dims.d_model), dtype=torch.float32, device="cuda")
+    u = torch.zeros(dims.n_experts + 1, dtype=torch.int32, device="cuda")
+    # layer-major prefill takes SMOE-Q4 blobs only: rejected before any launch
+    with pytest.raises(smoe.SmoeError, match="Q4"):
+        smoe.moe_prefill_chunk(dims, x, idx, w, table, r, u, u, u, idx, ws)
+    for bad in (dims.replace(chunk=32), synth.Dims(256, 128, 16, 4, 64, bits=2)):
+        with pytest.raises(smoe.SmoeError, match="Q2"):
+            smoe.moe_decode(bad, x[0], idx[0], w[0], table, r[0], ws)
