@@ -41,7 +41,8 @@ HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 # while they are unchanged since its counters were read
 GATE_UP_SOURCES = ("quantised_routed_expert_amd/csrc/decode.hip", "quantised_routed_expert_amd/csrc/kernels.h",
                    "quantised_routed_expert_amd/csrc/smoe_internal.h")
-TRAFFIC_FILE = "profiles/hbm_traffic_decode_gate_up_235b.txt"
+TRAFFIC_FILES = {4: "profiles/hbm_traffic_decode_gate_up_235b.txt",
+                 2: "profiles/hbm_traffic_decode_gate_up_235b_q2.txt"}
 
 
 def sources_digest(paths):
@@ -53,11 +54,12 @@ def sources_digest(paths):
     return h.hexdigest()
 
 
-def stored_traffic():
+def stored_traffic(bits=4):
     """HBM bytes per gate/up launch from the committed counter summary (FETCH_SIZE
-    + WRITE_SIZE, each scaled by the copy-kernel calibration), or None if there
-    is none or the kernel's sources changed since it was taken."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+    + WRITE_SIZE, each scaled by the copy-kernel calibration) for the code width
+    ``bits``, or None if there is none or the kernel's sources changed since it
+    was taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILES[bits])
     if not os.path.exists(path):
         return None
     kv = {}
@@ -189,8 +191,9 @@ def cpu_baseline(stack, wl, budget_s=15.0):
 
 
 def bench_decode(args):
-    wl = synth.CONFIGS[2]
+    wl = synth.CONFIGS[2] if args.quant == "q4" else synth.Q2_WORKLOADS[0]
     dims = wl.dims
+    qname = args.quant.upper()
     torch.cuda.set_device(0)
     t0 = time.time()
     stack = DeviceStack(wl.seed, dims, wl.n_layers)
@@ -261,7 +264,7 @@ def bench_decode(args):
 
     bytes_per_token = wl.n_layers * (dims.top_k * off["bytes"] + dims.n_experts * dims.d_model * 2)
     out = {
-        "metric": "MoE decode tokens/s + achieved HBM GB/s on Q4 expert bytes (235B-shape)",
+        "metric": f"MoE decode tokens/s + achieved HBM GB/s on {qname} expert bytes (235B-shape)",
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -271,14 +274,15 @@ def bench_decode(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4-affine weights, f16 dot products with fp32 accumulation; float64 router",
+        "dtype": f"{args.quant}-affine weights, f16 dot products with fp32 accumulation; float64 router",
         "data": "synthetic (seeded SplitMix64 codes/scales, N(0,0.02) router, N(0,1) bf16 hidden states)",
         "config": {"workload": wl.name, "layers": wl.n_layers, "d_model": dims.d_model, "d_ff": dims.d_ff,
-                   "experts": dims.n_experts, "top_k": dims.top_k, "chunk": dims.chunk, "batch": 1,
+                   "experts": dims.n_experts, "top_k": dims.top_k, "chunk": dims.chunk, "code_bits": dims.bits,
+                   "batch": 1,
                    "vault_bytes": stack.vault.numel(), "parallelism": "single GPU"},
-        "gbps_q4_expert_and_router_bytes": tok_s * bytes_per_token / 1e9,
+        f"gbps_{args.quant}_expert_and_router_bytes": tok_s * bytes_per_token / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(dims.bits),
                      "kernel": "decode_gate_up_kernel", "bytes_per_launch": per_launch,
                      "avg_launch_us": gu_ms * 1000.0, "launches_timed": len(durs),
                      "timing": "hipExtLaunchKernel start/stop events, eager token with the queue pre-filled",
@@ -450,7 +454,7 @@ def bench_ring(args):
     Each layer's router input follows its own Markov chain over tokens
     (h_t = 0.7 h_{t-1} + 0.3 z_t), so consecutive tokens share part of their
     experts; the residual update of each layer is computed and discarded."""
-    wl = synth.CONFIGS[4]
+    wl = synth.CONFIGS[4] if args.quant == "q4" else synth.Q2_WORKLOADS[1]
     dims = wl.dims
     E, NL = dims.n_experts, wl.n_layers
     torch.cuda.set_device(0)
@@ -534,12 +538,13 @@ def bench_ring(args):
     log(f"ring: {tok_s:.2f} tokens/s, hit rate {hits / max(1, hits + misses):.3f}, "
         f"H2D {h2d / dt / 1e9:.1f} GB/s, repeat {np.mean(repeats):.3f}")
     out = {
-        "metric": "ring-backed MoE decode tokens/s (235B-shape, 1536-slot HBM ring over a pinned-host vault)",
+        "metric": f"ring-backed MoE decode tokens/s (235B-shape, {n_slots}-slot HBM ring over a pinned-host vault)",
         "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": dt * 1000.0 / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q4-affine weights, f16 dot products with fp32 accumulation; float64 router",
+        "dtype": f"{args.quant}-affine weights, f16 dot products with fp32 accumulation; float64 router",
         "data": "synthetic (per-layer Markov router inputs h_t = 0.7 h_{t-1} + 0.3 z_t)",
-        "config": {"workload": wl.name, "layers": NL, "ring_slots": n_slots, "spec": S, "prewarm": bool(args.prewarm),
+        "config": {"workload": wl.name, "layers": NL, "ring_slots": n_slots, "code_bits": dims.bits,
+                   "slot_bytes": off["bytes"], "spec": S, "prewarm": bool(args.prewarm),
                    "parallelism": "single GPU"},
         "hit_rate": hits / max(1, hits + misses), "misses_per_token": misses / K,
         "bets_loaded_per_token": bets_loaded[0] / K, "prewarm_loads": prewarm_loads,
@@ -734,12 +739,18 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--pinned-gib", type=float, default=56.0, help="ring workloads: page-locked vault budget")
     ap.add_argument("--spec", type=int, default=0, help="ring workload: bet on gate ranks k .. k + spec - 1")
+    ap.add_argument("--quant", choices=["q4", "q2"], default="q4",
+                    help="decode and ring workloads: SMOE-Q4 blobs, or the SMOE-Q2 variant (2-bit codes)")
     ap.add_argument("--prewarm", action="store_true",
                     help="ring workload: after the warm-up tokens, load the most claimed experts (idle time)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
               "MI355X (the layer has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if args.quant == "q2" and args.workload not in ("decode", "ring"):
+        print("--quant q2 applies to the decode and ring workloads: layer-major prefill takes SMOE-Q4 blobs only",
+              file=sys.stderr)
         sys.exit(2)
     defaults = {"decode": (64, 8), "prefill": (3, 1), "ring": (256, 8), "ring-prefill": (1, 1),
                 "copy": (10, 2)}[args.workload]
