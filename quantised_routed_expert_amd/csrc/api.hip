@@ -259,7 +259,7 @@ int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, co
     uint16_t* xl = x_rec ? x_rec + (size_t)layer * D : xbuf;
     _Float16* px = reinterpret_cast<_Float16*>(base + L.px);
     const RouteArgs ra{residual, xl, px, w_router + (size_t)layer * E * D, bias ? bias + (size_t)layer * E : nullptr,
-                       logits, 1, d->d_model, d->n_experts, d->rms_eps, nullptr};
+                       logits, 1, d->d_model, d->n_experts, d->rms_eps, nullptr, quant_bits(d) == 2 ? 1 : 0};
     int groups = 0;  // one token: the logits are written directly
     hipError_t he = launch_route_logits(ra, s, &groups);
     if (he != hipSuccess) return hip_fail(he, "route_logits launch");

@@ -160,7 +160,7 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
   // this lane's input columns as f16 pairs, converted while the weights stream
   uint32_t xp[NSEG][Run::NDW];
   float xseg[NSEG];
-  if (BITS == 4 && a.px) pack_f16_run<NSEG, Run::NQ>(xraw, xp, xseg);
+  if (a.px) pack_f16_run<NSEG, Run::NQ>(xraw, xp, xseg);
   else pack_bf16_run<NSEG, Run::NQ>(xraw, xp, xseg);
 
 #pragma unroll
@@ -210,9 +210,9 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
   } else if (tid < a.k) {
     s_ptr[tid] = expert_pointer(a, tid);
   }
-  // (the router's pair-ordered f16 copy of x is in Q4's pair order)
+  // (the router writes its pair-ordered f16 copy of x in the order of BITS)
   uint4 xraw[NSEG][Run::NQ];
-  if (BITS == 4 && a.px) load_raw<LR, NSEG, Run::NQ>(a.px + li * Run::SEGV, xraw);
+  if (a.px) load_raw<LR, NSEG, Run::NQ>(a.px + li * Run::SEGV, xraw);
   else load_raw<LR, NSEG, Run::NQ>(a.x + li * Run::SEGV, xraw);
   if (fused && tid < kMaxExperts) {  // stored after the input loads are issued
     // padding, and a NaN logit (from a non-finite residual), rank as -inf
@@ -264,10 +264,13 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
 // NPASS * (64 / LR) output rows; its wave w handles ranks w, w + nw, ... so
 // that each wave keeps one expert's h in registers; per-row partial results
 // meet in LDS and are mixed in rank order (no atomics).  Each wave issues all
-// weight loads of its rows before it computes.
+// weight loads of its rows before it computes.  Only the first LA lanes of
+// each LR-lane group hold segments (LA < LR when a row's segment count is not
+// a power of two: one segment per active lane, so that the LR-lane groups
+// share one expert's h as few times as possible); the others contribute 0.
 // grid = ceil(d / rows per workgroup), block = 64 * min(k, 8).
 // ---------------------------------------------------------------------------
-template <int LR, int NSEG, int NPASS, int CHUNK, int BITS>
+template <int LR, int NSEG, int NPASS, int CHUNK, int BITS, int LA>
 __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;
@@ -313,6 +316,7 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int li = lane % LR, grp = lane / LR;
+  const bool act = LA == LR || li < LA;
   const int n0 = blockIdx.x * ROWS;
   const size_t row_bytes = (size_t)a.f * BITS / 8;
   const size_t prow_bytes = (size_t)(a.f / CHUNK) * 4;
@@ -325,8 +329,17 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     }
     const uint8_t* codes = blob + a.lay.down_codes + li * 16;
     const uint8_t* par = blob + a.lay.down_params;
+    // an idle lane (li >= LA) keeps zero codes, parameters and inputs, so its
+    // contribution is exactly 0
     uint4 hraw[NSEG][Run::NQ];
-    load_raw<LR, NSEG, Run::NQ>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
+    if (act) {
+      load_raw<LR, NSEG, Run::NQ>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+#pragma unroll
+        for (int q = 0; q < Run::NQ; ++q) hraw[s][q] = make_uint4(0, 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);  // h first: the math can start when it lands
     uint4 c[NPASS][NSEG];
     uint32_t pr[NPASS][NSEG];
@@ -334,9 +347,11 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     for (int p = 0; p < NPASS; ++p) {
       const int n = n0 + p * P + grp;  // < d: the launcher checks d % ROWS == 0
 #pragma unroll
-      for (int s = 0; s < NSEG; ++s) c[p][s] = gload16(codes + (size_t)n * row_bytes + s * Run::STRIDE);
+      for (int s = 0; s < NSEG; ++s)
+        c[p][s] = act ? gload16(codes + (size_t)n * row_bytes + s * Run::STRIDE) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int s = 0; s < NSEG; ++s) pr[p][s] = gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, s) * 4);
+      for (int s = 0; s < NSEG; ++s)
+        pr[p][s] = act ? gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, s) * 4) : 0u;
     }
     if (it == 0 && a.pf_base) {
 #pragma unroll
@@ -450,8 +465,26 @@ hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t 
   return hipGetLastError();
 }
 
+// The down rows' split.  SMOE-Q2 rows of 3 * 2^m segments (3 <= segs <= 48)
+// take one segment per lane over the next power of two (LR lanes, LA = segs
+// active): with split_row's LR = segs / 3 lanes, each lane would hold three
+// 64-value h segments and the 64 / LR row groups of a wave would each re-read
+// h (235B shape: 24 KB of h per wave against 6 KB of codes), which measured
+// slower than the idle quarter of lanes.  For SMOE-Q4 (32-value segments) the
+// power-of-two split measured faster.  Otherwise split_row's split.
+struct DownSplit {
+  int lr, nseg, la;
+};
+static DownSplit split_down(int f, int bits) {
+  const int segs = f * bits / 128;
+  if (bits == 2 && segs >= 3 && segs <= 48 && segs % 3 == 0 && pow2_part(segs / 3) == segs / 3)
+    return {segs / 3 * 4, 1, segs};
+  const RowSplit sp = split_row(f, bits);
+  return {sp.lr, sp.nseg, sp.lr};
+}
+
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
-  const RowSplit sp = split_row(a.f, a.bits);
+  const DownSplit sp = split_down(a.f, a.bits);
   const int P = 64 / sp.lr;
   int np = 1;
   while (np * 2 <= SMOE_DN_PASSES_MAX && a.d / (P * np * 2) >= SMOE_DN_MIN_WG) np *= 2;
@@ -459,8 +492,16 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   if (a.d % rows) return hipErrorInvalidValue;  // every workgroup owns full rows
   const int nw = a.k < 8 ? a.k : 8;
   const dim3 grid(a.d / rows);
+  if (sp.la != sp.lr) {  // one segment per active lane: LA = 3 LR / 4
+    if (a.bits != 2 || a.chunk != 64) return hipErrorInvalidValue;
+    constexpr int BITS = 2, CHUNK = 64;
+    SMOE_LR_SWITCH(sp.lr, SMOE_NP_SWITCH(np, NPASS,
+        hipLaunchKernelGGL((decode_down_kernel<LR, 1, NPASS, CHUNK, BITS, LR * 3 / 4>), grid, dim3(64 * nw), 0, s,
+                           a)));
+    return hipGetLastError();
+  }
   SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NPASS,
-      hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS>), grid, dim3(64 * nw), 0, s, a)))));
+      hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS, LR>), grid, dim3(64 * nw), 0, s, a)))));
   return hipGetLastError();
 }
 

@@ -204,6 +204,7 @@ struct RouteArgs {
   int n_tok, d, E;
   float eps;
   double* partial;          // [d / kRouteGroupCols][n_tok][E] workspace for the MFMA path, or null
+  int px16;                 // px_out pair order: 0 = groups of 8 (SMOE-Q4), 1 = groups of 16 (SMOE-Q2)
 };
 
 // Columns per workgroup of the multi-token MFMA router: its partial logits

@@ -82,11 +82,11 @@ __global__ __launch_bounds__(256) void route_logits_kernel(RouteArgs a) {
         *reinterpret_cast<uint2*>(xs + (size_t)t * d + j) = packed;
         if (blockIdx.x == 0 && a.x_out) *reinterpret_cast<uint2*>(a.x_out + (size_t)(t0 + t) * d + j) = packed;
         if (TB == 1 && blockIdx.x == 0 && a.px_out) {
-          // the same values as f16, in pair order within each group of 8
+          // the same values as f16, in the pair order of the blobs' code width
           const uint32_t bb[4] = {b0, b1, b2, b3};
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            a.px_out[(j & ~7) + pair_slot((j & 7) + i)] = (_Float16)bf16_to_f32(bb[i]);
+            a.px_out[a.px16 ? pair_index<2>(j + i) : pair_index<4>(j + i)] = (_Float16)bf16_to_f32(bb[i]);
         }
       }
     }
@@ -195,8 +195,8 @@ __global__ __launch_bounds__(256) void route_logits_decode_kernel(RouteArgs a) {
       if (m < M) {
         const int j = half * hd + m * 512 + lane * 8;
         if (a.x_out) *reinterpret_cast<uint4*>(a.x_out + j) = make_uint4(xb[m][0], xb[m][1], xb[m][2], xb[m][3]);
-        if (a.px_out) {
-          // dword p of the group holds (e_p, e_{p+4}) as f16
+        if (a.px_out && !a.px16) {
+          // dword p of the group of 8 holds (e_p, e_{p+4}) as f16
           uint32_t pw[4];
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
@@ -204,6 +204,25 @@ __global__ __launch_bounds__(256) void route_logits_decode_kernel(RouteArgs a) {
             const uint32_t hi = (xb[m][2 + (p >> 1)] >> (16 * (p & 1))) & 0xFFFFu;
             pw[p] = f16_bits(bf16_to_f32(lo)) | (f16_bits(bf16_to_f32(hi)) << 16);
           }
+          *reinterpret_cast<uint4*>(a.px_out + j) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        } else if (a.px_out) {
+          // groups of 16 (SMOE-Q2): dword p holds (e_p, e_{p+8}).  A group spans
+          // lanes 2i (e_0..e_7) and 2i+1 (e_8..e_15): the even lane writes
+          // dwords 0..3 and needs e_8..e_11, the odd lane dwords 4..7 and needs
+          // e_4..e_7, so each hands its partner two of its four bf16 pairs.
+          const bool odd = lane & 1;
+          const uint32_t r0 = __shfl_xor(odd ? xb[m][0] : xb[m][2], 1, kWave);
+          const uint32_t r1 = __shfl_xor(odd ? xb[m][1] : xb[m][3], 1, kWave);
+          const uint32_t A[2] = {odd ? r0 : xb[m][0], odd ? r1 : xb[m][1]};        // e_p
+          const uint32_t B[2] = {odd ? xb[m][2] : r0, odd ? xb[m][3] : r1};        // e_{p+8}
+          uint32_t pw[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = (A[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+            const uint32_t hi = (B[p >> 1] >> (16 * (p & 1))) & 0xFFFFu;
+            pw[p] = f16_bits(bf16_to_f32(lo)) | (f16_bits(bf16_to_f32(hi)) << 16);
+          }
+          // the even lane's dwords start the group, the odd lane's follow: px + j
           *reinterpret_cast<uint4*>(a.px_out + j) = make_uint4(pw[0], pw[1], pw[2], pw[3]);
         }
       }
