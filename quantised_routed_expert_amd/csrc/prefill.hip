@@ -279,8 +279,14 @@ __device__ __forceinline__ bool slice_info(const PrefillArgs& a, SliceInfo& si) 
   return si.n_rows > 0;
 }
 
+#ifdef SMOE_PF_WAVES_PER_EU
+#define SMOE_PF_OCC __attribute__((amdgpu_waves_per_eu(SMOE_PF_WAVES_PER_EU)))
+#else
+#define SMOE_PF_OCC
+#endif
+
 template <int CHUNK, int KT>
-__global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) SMOE_PF_OCC void prefill_gate_up_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ int rows[16];
   SliceInfo si;
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
 }
 
 template <int CHUNK, int KT>
-__global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) SMOE_PF_OCC void prefill_down_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ int rows[16];
   SliceInfo si;
@@ -370,6 +376,262 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 2-3 (chunk 64).  The same grouped GEMMs with the affine dequant folded per
+// chunk instead of applied to every weight: sum_k W x = sum_c (s_c P_c +
+// m_c X_c), P_c = sum_{k in c} q x on MFMA over the raw codes, X_c = sum_{k in
+// c} x.  A weight then costs two VALU ops per pair of codes less than the
+// dequant above (a profile of the kernels above showed them VALU-bound: taking
+// the affine step out of their dequant alone cut the prompt time by a fifth).
+//
+// Raw codes as MFMA inputs: masking a nibble into the low mantissa bits of an
+// fp16 half gives the subnormal q * 2^-24 exactly, a nibble at bits 4..7 gives
+// 16 q * 2^-24; the odd elements' inputs are staged divided by 16, so every
+// product is q x 2^-24 exactly (subnormal fp16 MFMA inputs are kept), and
+// s_c 2^24 scales the chunk's fp32 result.
+//
+// K order: MFMA step t of a K block takes the block's codes 32 t .. 32 t + 31,
+// lane group g the eight at 32 t + 8 g, so that two consecutive steps cover one
+// chunk.  Lane group g loads 16-byte pieces 4 q + g of its row (whole pieces,
+// as before), and a 4x4 dword transpose across the four lane groups hands each
+// group its dword of every piece.
+// ---------------------------------------------------------------------------
+
+// 4x4 transpose of dwords across the wave's four 16-lane rows: lane n of row
+// g holds v[j] = T[g][j] on entry and v[j] = T[j][g] on return.  Rows g = 2a +
+// b: v_permlane32_swap exchanges the row pairs (a) on the high bit of j, then
+// v_permlane16_swap exchanges odd and even rows (b) on its low bit.
+__device__ __forceinline__ void xpose4(uint32_t (&v)[4]) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+  v[0] = s0[0]; v[2] = s0[1]; v[1] = s1[0]; v[3] = s1[1];
+  const auto t0 = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+  const auto t1 = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+  v[0] = t0[0]; v[1] = t0[1]; v[2] = t1[0]; v[3] = t1[1];
+}
+
+// Eight codes (one dword, e_j in bits 4j..4j+3) as the B fragment of one MFMA
+// step, pair order (e0, e4, 16 e1, 16 e5, e2, e6, 16 e3, 16 e7) * 2^-24.
+__device__ __forceinline__ half8_t codes8(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  const uint4 r = make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u);
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// A slice's 16 token rows for one K block as fp16 in pair order, the odd
+// elements divided by 16, and the sum of each row's fp16 values over each
+// chunk of 64 (xsum[chunk of the block][row]).  Thread (r = tid / 16, c =
+// tid % 16) moves KT / 16 consecutive values of row r; load() and store() are
+// separate so that the loads run a block ahead.
+template <bool FROM_BF16, int KT>
+struct FoldStage {
+  static constexpr int PER = KT / 16;   // values per thread
+  static constexpr int V = PER / 8;     // uint4 per thread
+  static constexpr int TPC = 64 / PER;  // threads per chunk
+  uint4 v[V];
+
+  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
+    const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * PER;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      v[j] = make_uint4(0, 0, 0, 0);
+      if (r < n_rows) v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + c + 8 * j);
+    }
+  }
+
+  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16]) const {
+    const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * PER;
+    const uint32_t k16 = 0x2C002C00u;  // (1/16, 1/16) in fp16
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      uint4 o;
+      if (FROM_BF16) {  // bf16 in natural order -> fp16 pairs (e_p, e_{p+4})
+        const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float f[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          f[2 * p] = (float)(_Float16)bf16_to_f32(w4[p] & 0xFFFF);
+          f[2 * p + 1] = (float)(_Float16)bf16_to_f32(w4[p] >> 16);
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) part += f[p];
+        o.x = f16_bits(f[0]) | (f16_bits(f[4]) << 16);
+        o.y = f16_bits(f[1] * 0.0625f) | (f16_bits(f[5] * 0.0625f) << 16);
+        o.z = f16_bits(f[2]) | (f16_bits(f[6]) << 16);
+        o.w = f16_bits(f[3] * 0.0625f) | (f16_bits(f[7] * 0.0625f) << 16);
+      } else {  // fp16 already in pair order (H): divide dwords 1 and 3 by 16
+        const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const h2_t hv = as_h2(w4[p]);
+          part += (float)hv[0] + (float)hv[1];
+        }
+        o.x = v[j].x;
+        o.y = __builtin_bit_cast(uint32_t, as_h2(v[j].y) * as_h2(k16));
+        o.z = v[j].z;
+        o.w = __builtin_bit_cast(uint32_t, as_h2(v[j].w) * as_h2(k16));
+      }
+      *reinterpret_cast<uint4*>(&xs[r][c + 8 * j]) = o;
+    }
+    part = group_sum<TPC>(part);  // the TPC threads of a chunk are adjacent lanes
+    if ((tid & (TPC - 1)) == 0) xsum[c / 64][r] = part;
+  }
+};
+
+// One K block of one weight row per lane: pieces 4 q + g of the row's codes in
+// the block and the (scale, min) words of the block's KT / 64 chunks.
+template <int KT>
+struct FoldW {
+  static constexpr int NL = KT / 128;  // 16-byte code loads per lane
+  static constexpr int NPW = KT / 64;  // chunks per block
+  static_assert(NPW % 4 == 0, "K blocks of a multiple of 256 codes");
+  uint4 c[NL];
+  uint4 p[NPW / 4];
+
+  __device__ __forceinline__ void load(const uint8_t* codes_row, const uint8_t* par_row, int kb, int g) {
+#pragma unroll
+    for (int q = 0; q < NL; ++q) c[q] = gload16(codes_row + kb / 2 + 16 * (4 * q + g));
+#pragma unroll
+    for (int q = 0; q < NPW / 4; ++q) p[q] = gload16(par_row + (kb / 64) * 4 + 16 * q);
+  }
+};
+
+// acc += sum over the block's chunks of s_c P_c + m_c X_c for this lane's
+// column (feature) and its four rows 4 (lane / 16) + i; chunks in order.  All
+// of the block's MFMA chains are issued before the first result is folded, so
+// the VALU epilogue of one chunk overlaps the MFMAs of the next.
+template <int KT>
+__device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _Float16 (*xs)[KT + 8],
+                                            float (*xsum)[16], int lane) {
+  constexpr int NC = FoldW<KT>::NPW;
+  const int g = lane >> 4, ml = lane & 15, r4 = 4 * (lane >> 4);
+  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+  float4_t P[NC];
+#pragma unroll
+  for (int q = 0; q < FoldW<KT>::NL; ++q) {
+    uint32_t u[4] = {w.c[q].x, w.c[q].y, w.c[q].z, w.c[q].w};
+    xpose4(u);  // u[j] = dword g of piece 4 q + j: the codes of step 4 q + j
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t0 = 4 * q + 2 * h, cl = 2 * q + h;  // steps t0, t0 + 1 = chunk cl of the block
+      const half8_t a0 = *reinterpret_cast<const half8_t*>(&xs[ml][32 * t0 + 8 * g]);
+      const half8_t a1 = *reinterpret_cast<const half8_t*>(&xs[ml][32 * t0 + 32 + 8 * g]);
+      P[cl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, codes8(u[2 * h]), zero, 0, 0, 0);
+      P[cl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, codes8(u[2 * h + 1]), P[cl], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int cl = 0; cl < NC; ++cl) {
+    const uint4 pw = w.p[cl >> 2];
+    const uint32_t prm = (cl & 3) == 0 ? pw.x : (cl & 3) == 1 ? pw.y : (cl & 3) == 2 ? pw.z : pw.w;
+    const float S = __uint_as_float(prm << 16) * 16777216.0f;  // scale * 2^24
+    const float M = __uint_as_float(prm & 0xFFFF0000u);
+    const float4 X = *reinterpret_cast<const float4*>(&xsum[cl][r4]);
+    acc[0] = fmaf(S, P[cl][0], fmaf(M, X.x, acc[0]));
+    acc[1] = fmaf(S, P[cl][1], fmaf(M, X.y, acc[1]));
+    acc[2] = fmaf(S, P[cl][2], fmaf(M, X.z, acc[2]));
+    acc[3] = fmaf(S, P[cl][3], fmaf(M, X.w, acc[3]));
+  }
+}
+
+#ifdef SMOE_PF_FOLD_WAVES_PER_EU
+#define SMOE_PF_FOLD_OCC __attribute__((amdgpu_waves_per_eu(SMOE_PF_FOLD_WAVES_PER_EU)))
+#else
+#define SMOE_PF_FOLD_OCC
+#endif
+
+template <int KT>
+__global__ __launch_bounds__(256) SMOE_PF_FOLD_OCC void prefill_gate_up_fold_kernel(PrefillArgs a) {
+  __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
+  __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
+  __shared__ int rows[16];
+  SliceInfo si;
+  if (!slice_info(a, si)) return;
+  const int e = a.union_ids[si.u];
+  if (e < 0 || e >= a.E) return;
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.table[e]);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
+  __syncthreads();
+  const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const size_t row_bytes = (size_t)a.d / 2, prow = (size_t)(a.d / 64) * 4;
+  const uint8_t* gc = blob + (size_t)n0 * row_bytes;
+  const uint8_t* uc = blob + a.lay.up_codes + (size_t)n0 * row_bytes;
+  const uint8_t* gp = blob + a.lay.gate_params + (size_t)n0 * prow;
+  const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
+  float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
+  const int nk = a.d / KT;
+  FoldStage<true, KT> xr;
+  FoldW<KT> g0, u0, g1, u1;
+  xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
+  g0.load(gc, gp, 0, g);
+  u0.load(uc, up, 0, g);
+  xr.store(xs[0], xsum[0]);
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) {  // rows first, then weights, of block i + 1
+      xr.load(a.x, (size_t)a.d, rows, si.n_rows, (i + 1) * KT);
+      g1.load(gc, gp, (i + 1) * KT, g);
+      u1.load(uc, up, (i + 1) * KT, g);
+    }
+    fold_kblock<KT>(ag, g0, xs[i & 1], xsum[i & 1], lane);
+    fold_kblock<KT>(au, u0, xs[i & 1], xsum[i & 1], lane);
+    if (i + 1 < nk) xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+    g0 = g1;
+    u0 = u1;
+    __syncthreads();
+  }
+  const int hcol = (n0 & ~7) + pair_slot(n0 & 7);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    if (row < si.n_rows) a.H[(size_t)(si.o + row) * a.f + hcol] = (_Float16)(silu_f32(ag[i]) * au[i]);
+  }
+}
+
+template <int KT>
+__global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
+  __shared__ _Float16 xs[2][16][KT + 8];
+  __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
+  __shared__ int rows[16];
+  SliceInfo si;
+  if (!slice_info(a, si)) return;
+  const int e = a.union_ids[si.u];
+  if (e < 0 || e >= a.E) return;
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.table[e]);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
+  __syncthreads();
+  const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const size_t row_bytes = (size_t)a.f / 2, prow = (size_t)(a.f / 64) * 4;
+  const uint8_t* dc = blob + a.lay.down_codes + (size_t)n0 * row_bytes;
+  const uint8_t* dp = blob + a.lay.down_params + (size_t)n0 * prow;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int nk = a.f / KT;
+  FoldStage<false, KT> hr;
+  FoldW<KT> w0, w1;
+  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
+  w0.load(dc, dp, 0, g);
+  hr.store(xs[0], xsum[0]);
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) {
+      hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT);
+      w1.load(dc, dp, (i + 1) * KT, g);
+    }
+    fold_kblock<KT>(acc, w0, xs[i & 1], xsum[i & 1], lane);
+    if (i + 1 < nk) hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+    w0 = w1;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    if (row < si.n_rows) a.Y[(size_t)(si.o + row) * a.d + n0] = acc[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 4. Combine.  grid = (ceil(d / 256), T), 256 threads: residual[t][n] +=
 // sum_r w[t][r] * Y[invperm[t*k + r]][n], r ascending.
 // ---------------------------------------------------------------------------
@@ -385,6 +647,16 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
   a.residual[(size_t)t * a.d + n] += acc;
 }
 
+#ifndef SMOE_PF_GU_KT
+#define SMOE_PF_GU_KT 256  // K block of the gate/up GEMM (codes per row per block)
+#endif
+#ifndef SMOE_PF_FOLD_DN_KT
+#define SMOE_PF_FOLD_DN_KT 256  // K block of the chunk-folded down GEMM (256 or 512)
+#endif
+#ifndef SMOE_PF_DN_KT
+#define SMOE_PF_DN_KT 512  // K block of the down GEMM
+#endif
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const int max_union = a.E < a.T * a.k ? a.E : a.T * a.k;
   hipLaunchKernelGGL(prefill_union_kernel, dim3(1), dim3(1024), 0, s, a);
@@ -393,15 +665,22 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const dim3 gu(a.f / 64, ms), dn(a.d / 64, ms);
   // K blocks of 256 codes for gate/up (two matrices in registers), 512 for
   // down, when K allows (runs of 128 / 256 bytes per row); else 128
-  if (a.chunk == 64) {
-    if (a.d % 256 == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<64, 256>), gu, dim3(256), 0, s, a);
+  constexpr int GKT = SMOE_PF_GU_KT, DKT = SMOE_PF_DN_KT;
+  if (a.chunk == 64 && a.d % 256 == 0 && a.f % 256 == 0) {  // affine folded per chunk
+    hipLaunchKernelGGL((prefill_gate_up_fold_kernel<256>), gu, dim3(256), 0, s, a);
+    if (SMOE_PF_FOLD_DN_KT == 512 && a.f % 512 == 0)
+      hipLaunchKernelGGL((prefill_down_fold_kernel<512>), dn, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_down_fold_kernel<256>), dn, dim3(256), 0, s, a);
+  } else if (a.chunk == 64) {
+    if (a.d % GKT == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<64, GKT>), gu, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((prefill_gate_up_kernel<64, 128>), gu, dim3(256), 0, s, a);
-    if (a.f % 512 == 0) hipLaunchKernelGGL((prefill_down_kernel<64, 512>), dn, dim3(256), 0, s, a);
+    if (a.f % DKT == 0) hipLaunchKernelGGL((prefill_down_kernel<64, DKT>), dn, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((prefill_down_kernel<64, 128>), dn, dim3(256), 0, s, a);
   } else {
-    if (a.d % 256 == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<32, 256>), gu, dim3(256), 0, s, a);
+    if (a.d % GKT == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<32, GKT>), gu, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((prefill_gate_up_kernel<32, 128>), gu, dim3(256), 0, s, a);
-    if (a.f % 512 == 0) hipLaunchKernelGGL((prefill_down_kernel<32, 512>), dn, dim3(256), 0, s, a);
+    if (a.f % DKT == 0) hipLaunchKernelGGL((prefill_down_kernel<32, DKT>), dn, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((prefill_down_kernel<32, 128>), dn, dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((a.d + 255) / 256, a.T), dim3(256), 0, s, a);
