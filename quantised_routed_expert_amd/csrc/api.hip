@@ -56,7 +56,7 @@ int check_dims(const smoe_dims* d) {
 
 // Workspace carve-up (offsets from the workspace base, 256-byte aligned).
 struct Workspace {
-  size_t logits, plog, idx, w, ptr, x, px, h, ph, py, pinv, slices, end;
+  size_t logits, plog, idx, w, ptr, x, px, h, ph, py, pinv, slices, recs, end;
 };
 
 Workspace ws_layout(const smoe_dims* d, int max_tokens) {
@@ -76,6 +76,7 @@ Workspace ws_layout(const smoe_dims* d, int max_tokens) {
   w.py = o;     o = align_up(o + T * k * D * 4, 256);
   w.pinv = o;   o = align_up(o + T * k * 4, 256);
   w.slices = o; o = align_up(o + ((T * k + 15) / 16 + (E < T * k ? E : T * k) + 1) * 4, 256);
+  w.recs = o;   o = align_up(o + ((T * k + 15) / 16 + (E < T * k ? E : T * k)) * 16, 256);
   w.end = o;
   return w;
 }
@@ -317,6 +318,7 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
   a.invperm = reinterpret_cast<int32_t*>(base + L.pinv);
   a.slices = reinterpret_cast<int32_t*>(base + L.slices);
   a.n_slices = a.slices + prefill_max_slices(n_tok, d->top_k, d->n_experts);
+  a.recs = reinterpret_cast<PrefillArgs::SliceRec*>(base + L.recs);
   a.H = reinterpret_cast<_Float16*>(base + L.ph);
   a.Y = reinterpret_cast<float*>(base + L.py);
   a.T = n_tok;

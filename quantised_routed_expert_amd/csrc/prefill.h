@@ -19,6 +19,10 @@ struct PrefillArgs {
   int32_t* slices;            // [T*k/16 + min(E, T*k)] (u << 8 | s): slice s = entries
                               // 16 s .. 16 s + 15 of union expert u (workspace)
   int32_t* n_slices;          // [1] (workspace)
+  struct SliceRec {           // one slice, ready for a GEMM workgroup: its blob,
+    const void* blob;         // first entry (in perm order) and entry count
+    int32_t o, n_rows;
+  }* recs;                    // [prefill max slices] (workspace, 16-byte aligned)
   _Float16* H;                // [T*k][f] SwiGLU activations, fp16 pair order
   float* Y;                   // [T*k][d] per-entry expert outputs
   int T, d, f, E, k, chunk;

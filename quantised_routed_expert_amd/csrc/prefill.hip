@@ -102,8 +102,18 @@ __global__ __launch_bounds__(1024) void prefill_union_kernel(PrefillArgs a) {
     ssrc ^= 1;
   }
   if (tid < nu) {
-    const int end = sscan[ssrc][tid], ns = (cnt[uid[tid]] + 15) / 16;
-    for (int q = 0; q < ns; ++q) a.slices[end - ns + q] = (tid << 8) | q;
+    const int e = uid[tid], n_u = cnt[e];
+    const int end = sscan[ssrc][tid], ns = (n_u + 15) / 16;
+    const int base = tid == 0 ? 0 : scan[src][tid - 1];
+    const void* blob = a.table[e];
+    for (int q = 0; q < ns; ++q) {
+      a.slices[end - ns + q] = (tid << 8) | q;
+      PrefillArgs::SliceRec r;
+      r.blob = blob;
+      r.o = base + 16 * q;
+      r.n_rows = n_u - 16 * q < 16 ? n_u - 16 * q : 16;
+      a.recs[end - ns + q] = r;
+    }
     if (tid == nu - 1) *a.n_slices = end;
   }
   if (tid == 0 && nu == 0) *a.n_slices = 0;
@@ -545,14 +555,16 @@ __global__ __launch_bounds__(256) SMOE_PF_FOLD_OCC void prefill_gate_up_fold_ker
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
+  // the slice's record (written by the union kernel) and the slice count are
+  // independent loads: one round trip before the weights stream
+  const int n_slices = *a.n_slices;
+  const PrefillArgs::SliceRec rec = a.recs[blockIdx.y];
+  if ((int)blockIdx.y >= n_slices || !rec.blob) return;
   SliceInfo si;
-  if (!slice_info(a, si)) return;
-  const int e = a.union_ids[si.u];
-  if (e < 0 || e >= a.E) return;
-  const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.table[e]);
+  si.o = rec.o;
+  si.n_rows = rec.n_rows;
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(rec.blob);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
-  __syncthreads();
   const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
   const size_t row_bytes = (size_t)a.d / 2, prow = (size_t)(a.d / 64) * 4;
   const uint8_t* gc = blob + (size_t)n0 * row_bytes;
@@ -563,9 +575,11 @@ __global__ __launch_bounds__(256) SMOE_PF_FOLD_OCC void prefill_gate_up_fold_ker
   const int nk = a.d / KT;
   FoldStage<true, KT> xr;
   FoldW<KT> g0, u0, g1, u1;
-  xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
-  g0.load(gc, gp, 0, g);
+  g0.load(gc, gp, 0, g);  // the first weights go out before the token lookup
   u0.load(uc, up, 0, g);
+  if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
+  __syncthreads();
+  xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
   xr.store(xs[0], xsum[0]);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
@@ -594,14 +608,14 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
+  const int n_slices = *a.n_slices;
+  const PrefillArgs::SliceRec rec = a.recs[blockIdx.y];
+  if ((int)blockIdx.y >= n_slices || !rec.blob) return;
   SliceInfo si;
-  if (!slice_info(a, si)) return;
-  const int e = a.union_ids[si.u];
-  if (e < 0 || e >= a.E) return;
-  const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.table[e]);
+  si.o = rec.o;
+  si.n_rows = rec.n_rows;
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(rec.blob);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
-  __syncthreads();
   const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
   const size_t row_bytes = (size_t)a.f / 2, prow = (size_t)(a.f / 64) * 4;
   const uint8_t* dc = blob + a.lay.down_codes + (size_t)n0 * row_bytes;
@@ -610,8 +624,10 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   const int nk = a.f / KT;
   FoldStage<false, KT> hr;
   FoldW<KT> w0, w1;
-  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
   w0.load(dc, dp, 0, g);
+  if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
+  __syncthreads();
+  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
   hr.store(xs[0], xsum[0]);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
