@@ -344,7 +344,7 @@ def bench_prefill(args):
     dims = wl.dims
     T, C = wl.steps, wl.prefill_chunk
     n_chunks = T // C
-    NL = wl.n_layers
+    NL = wl.n_layers if args.layers is None else max(1, min(args.layers, wl.n_layers))
     torch.cuda.set_device(0)
     stack = DeviceStack(wl.seed, dims, NL, zipf_s=wl.zipf_s)
     torch.cuda.synchronize()
@@ -739,6 +739,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--pinned-gib", type=float, default=56.0, help="ring workloads: page-locked vault budget")
     ap.add_argument("--spec", type=int, default=0, help="ring workload: bet on gate ranks k .. k + spec - 1")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="prefill workload: run only the first N layers (for counter passes; the default line "
+                         "runs all 94)")
     ap.add_argument("--quant", choices=["q4", "q2"], default="q4",
                     help="decode and ring workloads: SMOE-Q4 blobs, or the SMOE-Q2 variant (2-bit codes)")
     ap.add_argument("--prewarm", action="store_true",
