@@ -45,6 +45,14 @@ def test_host_only_queries():
             raise AssertionError("expected SmoeError")
         except smoe.SmoeError as e:
             assert e.code == -1 and "Q2" in str(e)
+    # a code width other than 4 (or 0) and 2 is rejected; 0 reads as SMOE-Q4
+    from quantised_routed_expert_amd.binding import SmoeDims
+    d = SmoeDims(4096, 1536, 128, 8, 64, 1, 1e-6, 3)
+    assert lib.smoe_blob_bytes(ctypes.byref(d)) == 0
+    d.quant_bits = 0
+    assert lib.smoe_blob_bytes(ctypes.byref(d)) == 10616832
+    d.quant_bits = 2
+    assert lib.smoe_blob_bytes(ctypes.byref(d)) == 5898240
     bad = synth.CONFIGS[0].dims.replace(chunk=48)
     try:
         smoe.workspace_bytes(bad, 1)

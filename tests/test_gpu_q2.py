@@ -163,3 +163,29 @@ def test_q2_argument_checks():
     for bad in (dims.replace(chunk=32), synth.Dims(256, 128, 16, 4, 64, bits=2)):
         with pytest.raises(smoe.SmoeError, match="Q2"):
             smoe.moe_decode(bad, x[0], idx[0], w[0], table, r[0], ws)
+
+
+@pytest.mark.parametrize("E,k", [(256, 8), (24, 3)])
+def test_q2_decode_layers_selection_other_expert_counts(E, k):
+    """The in-kernel top-k of the chained entry point (general path above 128
+    experts) on SMOE-Q2 blobs: equal to the per-layer calls and the oracle."""
+    dims = synth.Dims(512, 128, E, k, 64, bits=2)
+    n_layers = 2
+    stack = DeviceStack(1337, dims, n_layers)
+    h0 = random_residual(np.random.default_rng(E + k + 2), 1, dims.d_model)[0]
+    r = torch.from_numpy(h0.copy()).cuda()
+    i_rec = torch.empty((n_layers, k), dtype=torch.int32, device="cuda")
+    w_rec = torch.empty((n_layers, k), dtype=torch.float32, device="cuda")
+    smoe.decode_layers(dims, n_layers, r, stack.router, None, stack.tables, smoe.workspace(dims, 1), None,
+                       i_rec, w_rec)
+    torch.cuda.synchronize()
+    res = h0.copy()
+    for L in range(n_layers):
+        xb, ig, wg, res_next = _decode_one_layer(dims, stack, L, res)
+        ref = oracle.moe_layer(res.astype(np.float64), stack.router_bits[L], LazyExperts(1337, dims, L), dims)
+        assert list(ig) == ref["idx"]
+        assert np.array_equal(ig, i_rec.cpu().numpy()[L])
+        assert np.array_equal(wg, w_rec.cpu().numpy()[L])
+        check_moe_output(res_next.astype(np.float64) - res.astype(np.float64), ref["y"], f"q2 E{E} k{k} L{L}")
+        res = res_next
+    assert np.array_equal(res, r.cpu().numpy())
