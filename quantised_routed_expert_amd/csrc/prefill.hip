@@ -506,6 +506,30 @@ struct FoldW {
   }
 };
 
+// Line-wise loads of one K block of 256 codes for the 16 weight rows of a
+// wave: 8 lanes cover one row's 128-byte line, so an instruction reads 8
+// whole lines (lane l: row 8 q + l / 8, bytes 16 (l % 8) of the block) rather
+// than half lines of 16 rows; relayout() then moves the pieces through the
+// wave's LDS stage into the FoldW register layout (lane (n, g): pieces
+// 4 q + g of row n).  Rows are 144 bytes apart in the stage (2-way read
+// conflicts at most).
+constexpr int kLineStageRow = 144;
+__device__ __forceinline__ void load_lines256(FoldW<256>& w, const uint8_t* codes_row0, size_t row_bytes,
+                                              const uint8_t* par_row, int kb, int lane) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    w.c[q] = gload16(codes_row0 + (size_t)(8 * q + (lane >> 3)) * row_bytes + kb / 2 + 16 * (lane & 7));
+  w.p[0] = gload16(par_row + (kb / 64) * 4);
+}
+__device__ __forceinline__ void relayout256(FoldW<256>& w, uint8_t* stage, int lane) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    *reinterpret_cast<uint4*>(stage + (8 * q + (lane >> 3)) * kLineStageRow + 16 * (lane & 7)) = w.c[q];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    w.c[q] = *reinterpret_cast<const uint4*>(stage + (lane & 15) * kLineStageRow + 16 * (4 * q + (lane >> 4)));
+}
+
 // acc += sum over the block's chunks of s_c P_c + m_c X_c for this lane's
 // column (feature) and its four rows 4 (lane / 16) + i; chunks in order.  All
 // of the block's MFMA chains are issued before the first result is folded, so
@@ -555,6 +579,7 @@ __global__ __launch_bounds__(256) SMOE_PF_FOLD_OCC void prefill_gate_up_fold_ker
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
+  __shared__ __attribute__((aligned(16))) uint8_t wst[4][2][16 * kLineStageRow];
   // the slice's record (written by the union kernel) and the slice count are
   // independent loads: one round trip before the weights stream
   const int n_slices = *a.n_slices;
@@ -567,30 +592,39 @@ __global__ __launch_bounds__(256) SMOE_PF_FOLD_OCC void prefill_gate_up_fold_ker
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
   const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
   const size_t row_bytes = (size_t)a.d / 2, prow = (size_t)(a.d / 64) * 4;
-  const uint8_t* gc = blob + (size_t)n0 * row_bytes;
-  const uint8_t* uc = blob + a.lay.up_codes + (size_t)n0 * row_bytes;
   const uint8_t* gp = blob + a.lay.gate_params + (size_t)n0 * prow;
   const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
   const int nk = a.d / KT;
   FoldStage<true, KT> xr;
   FoldW<KT> g0, u0, g1, u1;
-  g0.load(gc, gp, 0, g);  // the first weights go out before the token lookup
-  u0.load(uc, up, 0, g);
+  const size_t nw0 = (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;  // the wave's first row
+  const uint8_t* gc0 = blob + nw0;
+  const uint8_t* uc0 = blob + a.lay.up_codes + nw0;
+  uint8_t* gst = wst[wave][0];
+  uint8_t* ust = wst[wave][1];
+  load_lines256(g0, gc0, row_bytes, gp, 0, lane);  // the first weights go out before the token lookup
+  load_lines256(u0, uc0, row_bytes, up, 0, lane);
   if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
   __syncthreads();
   xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
   xr.store(xs[0], xsum[0]);
+  relayout256(g0, gst, lane);
+  relayout256(u0, ust, lane);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {  // rows first, then weights, of block i + 1
       xr.load(a.x, (size_t)a.d, rows, si.n_rows, (i + 1) * KT);
-      g1.load(gc, gp, (i + 1) * KT, g);
-      u1.load(uc, up, (i + 1) * KT, g);
+      load_lines256(g1, gc0, row_bytes, gp, (i + 1) * KT, lane);
+      load_lines256(u1, uc0, row_bytes, up, (i + 1) * KT, lane);
     }
     fold_kblock<KT>(ag, g0, xs[i & 1], xsum[i & 1], lane);
     fold_kblock<KT>(au, u0, xs[i & 1], xsum[i & 1], lane);
-    if (i + 1 < nk) xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+    if (i + 1 < nk) {
+      xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+      relayout256(g1, gst, lane);
+      relayout256(u1, ust, lane);
+    }
     g0 = g1;
     u0 = u1;
     __syncthreads();
@@ -608,6 +642,7 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
+  __shared__ __attribute__((aligned(16))) uint8_t wst[4][KT == 256 ? 16 * kLineStageRow : 16];
   const int n_slices = *a.n_slices;
   const PrefillArgs::SliceRec rec = a.recs[blockIdx.y];
   if ((int)blockIdx.y >= n_slices || !rec.blob) return;
@@ -624,19 +659,33 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   const int nk = a.f / KT;
   FoldStage<false, KT> hr;
   FoldW<KT> w0, w1;
-  w0.load(dc, dp, 0, g);
+  // KT == 256: line-wise weight loads re-laid through the wave's LDS stage
+  const uint8_t* dc0 = blob + a.lay.down_codes + (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;
+  uint8_t* dst = wst[wave];
+  auto wload = [&](FoldW<KT>& w, int kb) {
+    if constexpr (KT == 256) load_lines256(w, dc0, row_bytes, dp, kb, lane);
+    else w.load(dc, dp, kb, g);
+  };
+  auto wlay = [&](FoldW<KT>& w) {
+    if constexpr (KT == 256) relayout256(w, dst, lane);
+  };
+  wload(w0, 0);
   if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
   __syncthreads();
   hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
   hr.store(xs[0], xsum[0]);
+  wlay(w0);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
       hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT);
-      w1.load(dc, dp, (i + 1) * KT, g);
+      wload(w1, (i + 1) * KT);
     }
     fold_kblock<KT>(acc, w0, xs[i & 1], xsum[i & 1], lane);
-    if (i + 1 < nk) hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+    if (i + 1 < nk) {
+      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+      wlay(w1);
+    }
     w0 = w1;
     __syncthreads();
   }
