@@ -434,27 +434,28 @@ __device__ __forceinline__ half8_t codes8(uint32_t w) {
 // separate so that the loads run a block ahead.
 template <bool FROM_BF16, int KT>
 struct FoldStage {
-  static constexpr int PER = KT / 16;   // values per thread
-  static constexpr int V = PER / 8;     // uint4 per thread
-  static constexpr int TPC = 64 / PER;  // threads per chunk
+  static constexpr int V = KT / 128;  // 16-byte pieces (8 values) per thread
   uint4 v[V];
 
+  // thread (r, k) takes pieces 16 j + k of row r: the 16 threads of a row
+  // read 256 contiguous bytes per load instruction
   __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
-    const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * PER;
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       v[j] = make_uint4(0, 0, 0, 0);
-      if (r < n_rows) v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + c + 8 * j);
+      if (r < n_rows)
+        v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + 8 * (16 * j + k));
     }
   }
 
   __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16]) const {
-    const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * PER;
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
     const uint32_t k16 = 0x2C002C00u;  // (1/16, 1/16) in fp16
-    float part = 0.f;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       uint4 o;
+      float part = 0.f;
       if (FROM_BF16) {  // bf16 in natural order -> fp16 pairs (e_p, e_{p+4})
         const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         float f[8];
@@ -481,10 +482,11 @@ struct FoldStage {
         o.z = v[j].z;
         o.w = __builtin_bit_cast(uint32_t, as_h2(v[j].w) * as_h2(k16));
       }
-      *reinterpret_cast<uint4*>(&xs[r][c + 8 * j]) = o;
+      *reinterpret_cast<uint4*>(&xs[r][8 * (16 * j + k)]) = o;
+      // a chunk is 8 pieces: threads 8h .. 8h + 7 of the row (adjacent lanes)
+      part = group_sum<8>(part);
+      if ((k & 7) == 0) xsum[2 * j + (k >> 3)][r] = part;
     }
-    part = group_sum<TPC>(part);  // the TPC threads of a chunk are adjacent lanes
-    if ((tid & (TPC - 1)) == 0) xsum[c / 64][r] = part;
   }
 };
 
