@@ -8,11 +8,15 @@
 //               rank), per-expert token counts and offsets, and the token
 //               permutation (t ascending within an expert) -- integers only,
 //               deterministic (LDS min/add/or atomics on integers).
-//   2. gate_up: grouped GEMM per union expert on MFMA (v_mfma_f32_16x16x32_f16):
-//               Q4 codes dequantised to fp16 in registers (exact when
-//               min = -8 * scale), the chunk's token rows staged in LDS as
-//               fp16, SwiGLU in the epilogue -> H [T*k][d_ff] fp16.
-//   3. down:    grouped GEMM H x D^T per union expert -> Y [T*k][d_model] fp32.
+//   2. gate_up: grouped GEMM per union expert on MFMA (v_mfma_f32_16x16x32_f16),
+//               the chunk's token rows staged in LDS as fp16, SwiGLU in the
+//               epilogue -> H [T*k][d_ff] fp16.  Chunk 64 (d_model, d_ff
+//               multiples of 256): the raw codes enter MFMA and the affine
+//               step is folded per chunk (the *_fold kernels); otherwise the
+//               codes are dequantised to fp16 in registers (exact when
+//               min = -8 * scale).
+//   3. down:    grouped GEMM H x D^T per union expert -> Y [T*k][d_model] fp32,
+//               in the same two forms.
 //   4. combine: residual[t] += sum_r w[t][r] * Y[position of (t, r)], in rank
 //               order (no atomics).
 // The pages' own prefill FFN kernels keep a thread-per-row layout (Optimizations,
@@ -289,14 +293,8 @@ __device__ __forceinline__ bool slice_info(const PrefillArgs& a, SliceInfo& si) 
   return si.n_rows > 0;
 }
 
-#ifdef SMOE_PF_WAVES_PER_EU
-#define SMOE_PF_OCC __attribute__((amdgpu_waves_per_eu(SMOE_PF_WAVES_PER_EU)))
-#else
-#define SMOE_PF_OCC
-#endif
-
 template <int CHUNK, int KT>
-__global__ __launch_bounds__(256) SMOE_PF_OCC void prefill_gate_up_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ int rows[16];
   SliceInfo si;
@@ -345,7 +343,7 @@ __global__ __launch_bounds__(256) SMOE_PF_OCC void prefill_gate_up_kernel(Prefil
 }
 
 template <int CHUNK, int KT>
-__global__ __launch_bounds__(256) SMOE_PF_OCC void prefill_down_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ int rows[16];
   SliceInfo si;
@@ -570,14 +568,8 @@ __device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _
   }
 }
 
-#ifdef SMOE_PF_FOLD_WAVES_PER_EU
-#define SMOE_PF_FOLD_OCC __attribute__((amdgpu_waves_per_eu(SMOE_PF_FOLD_WAVES_PER_EU)))
-#else
-#define SMOE_PF_FOLD_OCC
-#endif
-
 template <int KT>
-__global__ __launch_bounds__(256) SMOE_PF_FOLD_OCC void prefill_gate_up_fold_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) void prefill_gate_up_fold_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
@@ -717,9 +709,6 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 #ifndef SMOE_PF_GU_KT
 #define SMOE_PF_GU_KT 256  // K block of the gate/up GEMM (codes per row per block)
 #endif
-#ifndef SMOE_PF_FOLD_DN_KT
-#define SMOE_PF_FOLD_DN_KT 256  // K block of the chunk-folded down GEMM (256 or 512)
-#endif
 #ifndef SMOE_PF_DN_KT
 #define SMOE_PF_DN_KT 512  // K block of the down GEMM
 #endif
@@ -735,10 +724,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   constexpr int GKT = SMOE_PF_GU_KT, DKT = SMOE_PF_DN_KT;
   if (a.chunk == 64 && a.d % 256 == 0 && a.f % 256 == 0) {  // affine folded per chunk
     hipLaunchKernelGGL((prefill_gate_up_fold_kernel<256>), gu, dim3(256), 0, s, a);
-    if (SMOE_PF_FOLD_DN_KT == 512 && a.f % 512 == 0)
-      hipLaunchKernelGGL((prefill_down_fold_kernel<512>), dn, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((prefill_down_fold_kernel<256>), dn, dim3(256), 0, s, a);
+    // K blocks of 256 for the down GEMM too (512 measured slower)
+    hipLaunchKernelGGL((prefill_down_fold_kernel<256>), dn, dim3(256), 0, s, a);
   } else if (a.chunk == 64) {
     if (a.d % GKT == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<64, GKT>), gu, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((prefill_gate_up_kernel<64, 128>), gu, dim3(256), 0, s, a);
