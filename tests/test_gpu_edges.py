@@ -49,6 +49,9 @@ BOUNDS = {
     "d_model_8192": synth.Dims(8192, 256, 32, 4, 32),
     "d_ff_8192": synth.Dims(256, 8192, 16, 4, 64),
     "e256_k16": synth.Dims(512, 256, 256, 16, 32),
+    # chunk 64: the chunk-folded prefill GEMMs at their largest K and slice counts
+    "d_model_8192_c64": synth.Dims(8192, 256, 32, 4, 64),
+    "e256_k16_c64": synth.Dims(512, 256, 256, 16, 64),
 }
 
 
@@ -77,7 +80,9 @@ def test_size_bound_decode_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name,T,sample", [("d_model_8192", 20, [0, 7, 19]), ("d_ff_8192", 33, [0, 16, 32]),
-                                           ("e256_k16", 64, [0, 21, 42, 63])])
+                                           ("e256_k16", 64, [0, 21, 42, 63]),
+                                           ("d_model_8192_c64", 17, [0, 9, 16]),
+                                           ("e256_k16_c64", 64, [0, 30, 63])])
 def test_size_bound_prefill_matches_oracle(name, T, sample):
     dims = BOUNDS[name]
     say(f"[bound] prefill {name}: T={T}")
