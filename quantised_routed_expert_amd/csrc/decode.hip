@@ -287,6 +287,10 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     s_w[tid] = w;
     s_ptr[tid] = p;
   }
+  // the residual entries this workgroup updates at the end, loaded now so
+  // that the final read-modify-write does not wait on memory (no other
+  // workgroup touches these rows)
+  const float res_pre = tid < ROWS ? a.residual[(size_t)blockIdx.x * ROWS + tid] : 0.f;
   // Pull the next layer's router rows into cache while this kernel streams:
   // the router workgroup w (rows [2w, 2w + 2)) runs on XCD w % 8, so the down
   // workgroups of that XCD each fetch one slice of those rows.  Each thread
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     const int n = n0 + row;
     float acc = 0.f;
     for (int r = 0; r < a.k; ++r) acc = fmaf(s_w[r], ylds[r][row], acc);
-    a.residual[n] += acc;
+    a.residual[n] = (row == tid ? res_pre : a.residual[n]) + acc;
   }
   // keeps the prefetch loads alive (all four words, so that no register of a
   // pending load is reused early, which would force a wait for it)
