@@ -41,8 +41,14 @@ HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 # while they are unchanged since its counters were read
 GATE_UP_SOURCES = ("quantised_routed_expert_amd/csrc/decode.hip", "quantised_routed_expert_amd/csrc/kernels.h",
                    "quantised_routed_expert_amd/csrc/smoe_internal.h")
-TRAFFIC_FILES = {4: "profiles/hbm_traffic_decode_gate_up_235b.txt",
-                 2: "profiles/hbm_traffic_decode_gate_up_235b_q2.txt"}
+TRAFFIC_FILES = {("235b", 4): "profiles/hbm_traffic_decode_gate_up_235b.txt",
+                 ("235b", 2): "profiles/hbm_traffic_decode_gate_up_235b_q2.txt",
+                 ("30b", 4): "profiles/hbm_traffic_decode_gate_up_30b.txt",
+                 ("30b", 2): "profiles/hbm_traffic_decode_gate_up_30b_q2.txt"}
+# decode stacks by (shape, code width)
+DECODE_WORKLOADS = {("235b", 4): synth.CONFIGS[2], ("235b", 2): synth.Q2_WORKLOADS[0],
+                    ("30b", 4): synth.CONFIGS[1], ("30b", 2): synth.Q2_WORKLOADS[2]}
+SHAPE_LABEL = {"235b": "235B-shape", "30b": "30B-shape"}
 
 
 def sources_digest(paths):
@@ -54,12 +60,12 @@ def sources_digest(paths):
     return h.hexdigest()
 
 
-def stored_traffic(bits=4):
+def stored_traffic(bits=4, shape="235b"):
     """HBM bytes per gate/up launch from the committed counter summary (FETCH_SIZE
-    + WRITE_SIZE, each scaled by the copy-kernel calibration) for the code width
-    ``bits``, or None if there is none or the kernel's sources changed since it
-    was taken."""
-    path = os.path.join(ROOT, TRAFFIC_FILES[bits])
+    + WRITE_SIZE, each scaled by the copy-kernel calibration) for the decode
+    stack ``shape`` at code width ``bits``, or None if there is none or the
+    kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILES[(shape, bits)])
     if not os.path.exists(path):
         return None
     kv = {}
@@ -191,7 +197,7 @@ def cpu_baseline(stack, wl, budget_s=15.0):
 
 
 def bench_decode(args):
-    wl = synth.CONFIGS[2] if args.quant == "q4" else synth.Q2_WORKLOADS[0]
+    wl = DECODE_WORKLOADS[(args.shape, 4 if args.quant == "q4" else 2)]
     dims = wl.dims
     qname = args.quant.upper()
     torch.cuda.set_device(0)
@@ -264,7 +270,7 @@ def bench_decode(args):
 
     bytes_per_token = wl.n_layers * (dims.top_k * off["bytes"] + dims.n_experts * dims.d_model * 2)
     out = {
-        "metric": f"MoE decode tokens/s + achieved HBM GB/s on {qname} expert bytes (235B-shape)",
+        "metric": f"MoE decode tokens/s + achieved HBM GB/s on {qname} expert bytes ({SHAPE_LABEL[args.shape]})",
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -282,7 +288,7 @@ def bench_decode(args):
                    "vault_bytes": stack.vault.numel(), "parallelism": "single GPU"},
         f"gbps_{args.quant}_expert_and_router_bytes": tok_s * bytes_per_token / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(dims.bits),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(dims.bits, args.shape),
                      "kernel": "decode_gate_up_kernel", "bytes_per_launch": per_launch,
                      "avg_launch_us": gu_ms * 1000.0, "launches_timed": len(durs),
                      "timing": "hipExtLaunchKernel start/stop events, eager token with the queue pre-filled",
@@ -744,6 +750,9 @@ def main():
                          "runs all 94)")
     ap.add_argument("--quant", choices=["q4", "q2"], default="q4",
                     help="decode and ring workloads: SMOE-Q4 blobs, or the SMOE-Q2 variant (2-bit codes)")
+    ap.add_argument("--shape", choices=["235b", "30b"], default="235b",
+                    help="decode workload: the Qwen3-235B-A22B-shaped stack (94 layers, d_model 4096) or the "
+                         "Qwen3-30B-A3B-shaped one (48 layers, d_model 2048, 256 steps by default)")
     ap.add_argument("--prewarm", action="store_true",
                     help="ring workload: after the warm-up tokens, load the most claimed experts (idle time)")
     args = ap.parse_args()
@@ -755,7 +764,10 @@ def main():
         print("--quant q2 applies to the decode and ring workloads: layer-major prefill takes SMOE-Q4 blobs only",
               file=sys.stderr)
         sys.exit(2)
-    defaults = {"decode": (64, 8), "prefill": (3, 1), "ring": (256, 8), "ring-prefill": (1, 1),
+    if args.shape != "235b" and args.workload != "decode":
+        print("--shape applies to the decode workload only", file=sys.stderr)
+        sys.exit(2)
+    defaults = {"decode": (256 if args.shape == "30b" else 64, 8), "prefill": (3, 1), "ring": (256, 8), "ring-prefill": (1, 1),
                 "copy": (10, 2)}[args.workload]
     args.steps = defaults[0] if args.steps is None else args.steps
     args.warmup = defaults[1] if args.warmup is None else args.warmup

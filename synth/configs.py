@@ -74,4 +74,9 @@ QWEN235B_RING_Q2 = Workload(
     dims=Dims(4096, 1536, 128, 8, 64, bits=2),
     n_layers=94, steps=256, mode="ring", ring_slots=2764, markov=(0.7, 0.3))
 
-Q2_WORKLOADS = [QWEN235B_DECODE_Q2, QWEN235B_RING_Q2]
+QWEN30B_DECODE_Q2 = Workload(
+    name="qwen3-30b-a3b-shape-decode-48L-d2048-f768-e128-k8-q2c64",
+    dims=Dims(2048, 768, 128, 8, 64, bits=2),
+    n_layers=48, steps=256, mode="decode")
+
+Q2_WORKLOADS = [QWEN235B_DECODE_Q2, QWEN235B_RING_Q2, QWEN30B_DECODE_Q2]
