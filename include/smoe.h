@@ -56,8 +56,8 @@
  * [2i, 2i + 2) of the row's byte j; parameters unchanged.  Chunk 64 only.
  *   blob bytes = 0.75*d_model*d_ff + 12*d_model*d_ff/chunk.
  * SMOE-Q2 is supported by the decode calls (smoe_moe_decode,
- * smoe_moe_decode_slots, smoe_decode_layers) and by the ring, which moves
- * blobs of any size; smoe_moe_prefill_chunk takes SMOE-Q4 only.
+ * smoe_moe_decode_slots, smoe_decode_layers), by smoe_moe_prefill_chunk and
+ * by the ring, which moves blobs of any size.
  */
 #ifndef SMOE_H
 #define SMOE_H
@@ -205,9 +205,11 @@ int smoe_decode_layers(const smoe_dims* dims, int32_t n_layers, float* residual,
  *                offsets[u]..offsets[u+1]-1 list t*k + r of its tokens, t ascending
  *   residual     device fp32 [n_tok][d_model], += the MoE output per token
  * Each union expert's blob is streamed once per chunk; the grouped FFN runs on
- * MFMA with weights dequantised to fp16 (exact for min = -8*scale).  The
- * per-token mix is summed in rank order; no atomics.  SMOE-Q4 blobs only
- * (dims->quant_bits 2 returns SMOE_EINVAL). */
+ * MFMA with fp16 inputs: for SMOE-Q4 at chunk 64 the raw codes, with the
+ * affine step applied per chunk to the fp32 sums; otherwise (chunk 32, and
+ * SMOE-Q2 blobs) the weights dequantised to fp16 (exact for min = -8*scale,
+ * and -2*scale for SMOE-Q2).  The per-token mix is summed in rank order; no
+ * atomics. */
 int smoe_moe_prefill_chunk(const smoe_dims* dims, int32_t n_tok, const uint16_t* x,
                            const int32_t* topk_idx, const float* topk_w,
                            const void* const* expert_table, float* residual, int32_t* union_ids,

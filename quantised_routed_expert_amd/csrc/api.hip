@@ -295,7 +295,6 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
                            size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   if (int e = check_dims(d)) return e;
-  if (quant_bits(d) != 4) return fail(SMOE_EINVAL, "prefill takes SMOE-Q4 blobs only (quant_bits=%d)", d->quant_bits);
   if (n_tok < 1 || n_tok > kMaxPrefillTokens)
     return fail(SMOE_EINVAL, "n_tok=%d must be in [1, %d]", n_tok, kMaxPrefillTokens);
   if (!x || !topk_idx || !topk_w || !expert_table || !residual || !union_ids || !union_count || !offsets || !perm)
@@ -327,7 +326,8 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
   a.E = d->n_experts;
   a.k = d->top_k;
   a.chunk = d->chunk;
-  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk, 4);
+  a.bits = quant_bits(d);
+  a.lay = blob_layout(d->d_model, d->d_ff, d->chunk, a.bits);
   hipError_t he = launch_prefill(a, (hipStream_t)stream);
   if (he != hipSuccess) return hip_fail(he, "prefill launch");
   return SMOE_OK;

@@ -23,9 +23,11 @@ struct PrefillArgs {
     const void* blob;         // first entry (in perm order) and entry count
     int32_t o, n_rows;
   }* recs;                    // [prefill max slices] (workspace, 16-byte aligned)
-  _Float16* H;                // [T*k][f] SwiGLU activations, fp16 pair order
+  _Float16* H;                // [T*k][f] SwiGLU activations, fp16 in the pair order of
+                              // the code width (groups of 8 for Q4, 16 for SMOE-Q2)
   float* Y;                   // [T*k][d] per-entry expert outputs
   int T, d, f, E, k, chunk;
+  int bits;                   // code width: 4 (SMOE-Q4) or 2 (SMOE-Q2)
   BlobLayout lay;
 };
 

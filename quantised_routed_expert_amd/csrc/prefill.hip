@@ -12,9 +12,10 @@
 //               the chunk's token rows staged in LDS as fp16, SwiGLU in the
 //               epilogue -> H [T*k][d_ff] fp16.  Chunk 64 (d_model, d_ff
 //               multiples of 256): the raw codes enter MFMA and the affine
-//               step is folded per chunk (the *_fold kernels); otherwise the
-//               codes are dequantised to fp16 in registers (exact when
-//               min = -8 * scale).
+//               step is folded per chunk (the *_fold kernels); otherwise, and
+//               for SMOE-Q2 blobs, the codes are dequantised to fp16 in
+//               registers (exact when min = -8 * scale, or -2 * scale for
+//               SMOE-Q2).
 //   3. down:    grouped GEMM H x D^T per union expert -> Y [T*k][d_model] fp32,
 //               in the same two forms.
 //   4. combine: residual[t] += sum_r w[t][r] * Y[position of (t, r)], in rank
@@ -163,6 +164,29 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, h2_t s, h2_t s16, h2_t m
   return r;
 }
 
+// SMOE-Q2: one dword holds 16 two-bit codes, element 4j + i in bits 2i..2i+1
+// of byte j.  Its low half (bytes 0 and 2 after the shifts below) gives the
+// pairs (e_p, e_{p+8}) for p = 0..3 in this order; the caller passes w >> 8
+// for p = 4..7.  A code at bits 2..3 of a byte reads as 4 q, so those pairs
+// take s/4; every (scale, min) of the format keeps s/4 a normal fp16.
+__device__ __forceinline__ half8_t dequant8_q2(uint32_t w, h2_t s, h2_t s4, h2_t m) {
+  const uint32_t magic = 0x64006400u;
+  const h2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const uint32_t w4 = w >> 4;
+  const h2_t q0 = as_h2((w & 0x00030003u) | magic) - k1024;   // (e0, e8)
+  const h2_t q1 = as_h2((w & 0x000C000Cu) | magic) - k1024;   // 4 (e1, e9)
+  const h2_t q2 = as_h2((w4 & 0x00030003u) | magic) - k1024;  // (e2, e10)
+  const h2_t q3 = as_h2((w4 & 0x000C000Cu) | magic) - k1024;  // 4 (e3, e11)
+  const h2_t w0 = __builtin_elementwise_fma(q0, s, m);
+  const h2_t w1 = __builtin_elementwise_fma(q1, s4, m);
+  const h2_t w2 = __builtin_elementwise_fma(q2, s, m);
+  const h2_t w3 = __builtin_elementwise_fma(q3, s4, m);
+  half8_t r;
+  r[0] = w0[0]; r[1] = w0[1]; r[2] = w1[0]; r[3] = w1[1];
+  r[4] = w2[0]; r[5] = w2[1]; r[6] = w3[0]; r[7] = w3[1];
+  return r;
+}
+
 // (scale, min) bf16 pair -> fp16 pairs (s, s), (s/16, s/16), (m, m)
 __device__ __forceinline__ void params_f16(uint32_t p, h2_t& s, h2_t& s16, h2_t& m) {
   const _Float16 sv = (_Float16)__uint_as_float(p << 16);
@@ -198,10 +222,13 @@ struct KBlock {
 
 // A slice's token rows for one K block (16 rows x KT fp16) staged in LDS.
 // Thread (r = tid / 16, c = tid % 16) moves KT / 16 consecutive values of row
-// r; load() and store() are separate so the loads run a block ahead.
-template <bool FROM_BF16, int KT>
+// r; load() and store() are separate so the loads run a block ahead.  From
+// bf16, the values are stored in the pair order of code width BITS (groups of
+// 8 for Q4, of 16 for SMOE-Q2); fp16 rows (H) already are.
+template <bool FROM_BF16, int KT, int BITS = 4>
 struct RowStage {
   static constexpr int V = KT / 16 / 8;  // uint4 (8 values) per thread
+  static_assert(!FROM_BF16 || BITS == 4 || V % 2 == 0, "a thread holds whole groups of 16");
   uint4 v[V];
 
   __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
@@ -215,6 +242,26 @@ struct RowStage {
 
   __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8]) const {
     const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * (KT / 16);
+    if constexpr (FROM_BF16 && BITS == 2) {
+#pragma unroll
+      for (int j = 0; j < V; j += 2) {
+        const uint32_t w8[8] = {v[j].x, v[j].y, v[j].z, v[j].w, v[j + 1].x, v[j + 1].y, v[j + 1].z, v[j + 1].w};
+        uint32_t e[16];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          e[2 * p] = f16_bits(bf16_to_f32(w8[p] & 0xFFFF));
+          e[2 * p + 1] = f16_bits(bf16_to_f32(w8[p] >> 16));
+        }
+        // dword p of the group holds (e_p, e_{p+8})
+        const uint4 o0 = make_uint4(e[0] | (e[8] << 16), e[1] | (e[9] << 16), e[2] | (e[10] << 16),
+                                    e[3] | (e[11] << 16));
+        const uint4 o1 = make_uint4(e[4] | (e[12] << 16), e[5] | (e[13] << 16), e[6] | (e[14] << 16),
+                                    e[7] | (e[15] << 16));
+        *reinterpret_cast<uint4*>(&xs[r][c + 8 * j]) = o0;
+        *reinterpret_cast<uint4*>(&xs[r][c + 8 * j + 8]) = o1;
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       uint4 o;
@@ -277,6 +324,80 @@ __device__ __forceinline__ void mma_kblock(float4_t& acc, const WBlock<CHUNK, KT
   }
 }
 
+// SMOE-Q2: one K block of one weight row per lane, KT / 4 codes (KT / 16
+// bytes: one 8-byte load at KT = 128, 16-byte loads above).
+template <int CHUNK, int KT>
+struct WBlockQ2 {
+  static constexpr int KPL = KBlock<KT>::KPL;
+  static constexpr int NDW = KPL / 16;                   // code dwords per lane
+  static constexpr int NP = (KPL + CHUNK - 1) / CHUNK;   // chunks per lane run
+  static_assert(NDW == 2 || NDW % 4 == 0, "K block of 128, 256 or 512 codes");
+  uint32_t c[NDW];
+  uint32_t p[NP];
+
+  __device__ __forceinline__ void load(const uint8_t* codes_row, const uint8_t* par_row, int kb, int lane) {
+    const int k0 = kb + (lane >> 4) * KPL;
+    const uint8_t* src = codes_row + k0 / 4;
+    if constexpr (NDW == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      c[0] = v.x;
+      c[1] = v.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < NDW / 4; ++j) {
+        const uint4 v = gload16(src + 16 * j);
+        c[4 * j] = v.x;
+        c[4 * j + 1] = v.y;
+        c[4 * j + 2] = v.z;
+        c[4 * j + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) p[j] = gload4(par_row + (k0 / CHUNK + j) * 4);
+  }
+};
+
+// acc += A x B for an SMOE-Q2 block: code dword t of the lane covers its k
+// run's elements 16 t .. 16 t + 15, and the A rows in LDS hold each group of
+// 16 in the pair order (e_p, e_{p+8}), so the dword's low and high halves
+// meet the 8 A values at 16 t and at 16 t + 8.
+template <int CHUNK, int KT>
+__device__ __forceinline__ void mma_kblock_q2(float4_t& acc, const WBlockQ2<CHUNK, KT>& w,
+                                              _Float16 (*xs)[KT + 8], int lane) {
+  const int g = lane >> 4, ml = lane & 15;
+#pragma unroll
+  for (int t = 0; t < WBlockQ2<CHUNK, KT>::NDW; ++t) {
+    const uint32_t p = w.p[(16 * t) / CHUNK];
+    const _Float16 sv = (_Float16)__uint_as_float(p << 16);
+    const _Float16 sv4 = (_Float16)(__uint_as_float(p << 16) * 0.25f);
+    const _Float16 mv = (_Float16)__uint_as_float(p & 0xFFFF0000u);
+    const h2_t sc = {sv, sv}, sc4 = {sv4, sv4}, mn = {mv, mv};
+    const _Float16* xr = &xs[ml][g * KBlock<KT>::KPL + 16 * t];
+    const half8_t a0 = *reinterpret_cast<const half8_t*>(xr);
+    const half8_t a1 = *reinterpret_cast<const half8_t*>(xr + 8);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, dequant8_q2(w.c[t], sc, sc4, mn), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, dequant8_q2(w.c[t] >> 8, sc, sc4, mn), acc, 0, 0, 0);
+  }
+}
+
+// The weight block and MFMA step of code width BITS.
+template <int CHUNK, int KT, int BITS>
+struct WFormat;
+template <int CHUNK, int KT>
+struct WFormat<CHUNK, KT, 4> {
+  using Block = WBlock<CHUNK, KT>;
+  static __device__ __forceinline__ void mma(float4_t& acc, const Block& w, _Float16 (*xs)[KT + 8], int lane) {
+    mma_kblock<CHUNK, KT>(acc, w, xs, lane);
+  }
+};
+template <int CHUNK, int KT>
+struct WFormat<CHUNK, KT, 2> {
+  using Block = WBlockQ2<CHUNK, KT>;
+  static __device__ __forceinline__ void mma(float4_t& acc, const Block& w, _Float16 (*xs)[KT + 8], int lane) {
+    mma_kblock_q2<CHUNK, KT>(acc, w, xs, lane);
+  }
+};
+
 struct SliceInfo {
   int u, o, n_rows;
 };
@@ -293,8 +414,9 @@ __device__ __forceinline__ bool slice_info(const PrefillArgs& a, SliceInfo& si) 
   return si.n_rows > 0;
 }
 
-template <int CHUNK, int KT>
+template <int CHUNK, int KT, int BITS = 4>
 __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
+  using F = WFormat<CHUNK, KT, BITS>;
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ int rows[16];
   SliceInfo si;
@@ -306,15 +428,15 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
   if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
   __syncthreads();
   const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
-  const size_t row_bytes = (size_t)a.d / 2, prow = (size_t)(a.d / CHUNK) * 4;
+  const size_t row_bytes = (size_t)a.d * BITS / 8, prow = (size_t)(a.d / CHUNK) * 4;
   const uint8_t* gc = blob + (size_t)n0 * row_bytes;
   const uint8_t* uc = blob + a.lay.up_codes + (size_t)n0 * row_bytes;
   const uint8_t* gp = blob + a.lay.gate_params + (size_t)n0 * prow;
   const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
   const int nk = a.d / KT;
-  RowStage<true, KT> xr;
-  WBlock<CHUNK, KT> g0, u0, g1, u1;
+  RowStage<true, KT, BITS> xr;
+  typename F::Block g0, u0, g1, u1;
   xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
   g0.load(gc, gp, 0, lane);
   u0.load(uc, up, 0, lane);
@@ -326,15 +448,15 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
       g1.load(gc, gp, (i + 1) * KT, lane);
       u1.load(uc, up, (i + 1) * KT, lane);
     }
-    mma_kblock<CHUNK, KT>(ag, g0, xs[i & 1], lane);
-    mma_kblock<CHUNK, KT>(au, u0, xs[i & 1], lane);
+    F::mma(ag, g0, xs[i & 1], lane);
+    F::mma(au, u0, xs[i & 1], lane);
     if (i + 1 < nk) xr.store(xs[(i + 1) & 1]);
     g0 = g1;
     u0 = u1;
     __syncthreads();
   }
   // epilogue: lane holds rows 4 (l / 16) + i of the tile, feature n0
-  const int hcol = (n0 & ~7) + pair_slot(n0 & 7);
+  const int hcol = pair_index<BITS>(n0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * (lane >> 4) + i;
@@ -342,8 +464,9 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
   }
 }
 
-template <int CHUNK, int KT>
+template <int CHUNK, int KT, int BITS = 4>
 __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
+  using F = WFormat<CHUNK, KT, BITS>;
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ int rows[16];
   SliceInfo si;
@@ -355,13 +478,13 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
   if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
   __syncthreads();
   const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
-  const size_t row_bytes = (size_t)a.f / 2, prow = (size_t)(a.f / CHUNK) * 4;
+  const size_t row_bytes = (size_t)a.f * BITS / 8, prow = (size_t)(a.f / CHUNK) * 4;
   const uint8_t* dc = blob + a.lay.down_codes + (size_t)n0 * row_bytes;
   const uint8_t* dp = blob + a.lay.down_params + (size_t)n0 * prow;
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   const int nk = a.f / KT;
   RowStage<false, KT> hr;
-  WBlock<CHUNK, KT> w0, w1;
+  typename F::Block w0, w1;
   hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
   w0.load(dc, dp, 0, lane);
   hr.store(xs[0]);
@@ -371,7 +494,7 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
       hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT);
       w1.load(dc, dp, (i + 1) * KT, lane);
     }
-    mma_kblock<CHUNK, KT>(acc, w0, xs[i & 1], lane);
+    F::mma(acc, w0, xs[i & 1], lane);
     if (i + 1 < nk) hr.store(xs[(i + 1) & 1]);
     w0 = w1;
     __syncthreads();
@@ -722,7 +845,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   // K blocks of 256 codes for gate/up (two matrices in registers), 512 for
   // down, when K allows (runs of 128 / 256 bytes per row); else 128
   constexpr int GKT = SMOE_PF_GU_KT, DKT = SMOE_PF_DN_KT;
-  if (a.chunk == 64 && a.d % 256 == 0 && a.f % 256 == 0) {  // affine folded per chunk
+  if (a.bits == 2) {  // SMOE-Q2 (chunk 64, d_model a multiple of 512): fp16 dequant per weight
+    hipLaunchKernelGGL((prefill_gate_up_kernel<64, 256, 2>), gu, dim3(256), 0, s, a);
+    if (a.f % 512 == 0) hipLaunchKernelGGL((prefill_down_kernel<64, 512, 2>), dn, dim3(256), 0, s, a);
+    else if (a.f % 256 == 0) hipLaunchKernelGGL((prefill_down_kernel<64, 256, 2>), dn, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_down_kernel<64, 128, 2>), dn, dim3(256), 0, s, a);
+  } else if (a.chunk == 64 && a.d % 256 == 0 && a.f % 256 == 0) {  // affine folded per chunk
     hipLaunchKernelGGL((prefill_gate_up_fold_kernel<256>), gu, dim3(256), 0, s, a);
     // K blocks of 256 for the down GEMM too (512 measured slower)
     hipLaunchKernelGGL((prefill_down_fold_kernel<256>), dn, dim3(256), 0, s, a);

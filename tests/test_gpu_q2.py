@@ -1,8 +1,8 @@
-"""SMOE-Q2 decode on the GPU (the 2-bit vault of the Optimizations page, "Q2
-Vaults -- the Next 2x, Twice Over"): the device generator, per-layer and
-chained decode against the CPU oracle, ring-backed decode against resident
-decode and the oracle's LRU run, and the argument checks, all through the C
-ABI."""
+"""SMOE-Q2 on the GPU (the 2-bit vault of the Optimizations page, "Q2 Vaults
+-- the Next 2x, Twice Over"): the device generator, per-layer and chained
+decode and layer-major prefill against the CPU oracle, ring-backed decode
+against resident decode and the oracle's LRU run, and the argument checks,
+all through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -14,6 +14,7 @@ from synth.device import DeviceStack, fill_experts
 from tests.gpu_common import (LazyExperts, bits_u16, check_moe_output, need_gpu, random_residual, say,
                               topk_gap_ok)
 from tests.test_gpu_decode import _decode_one_layer
+from tests.test_gpu_prefill import check_union, run_prefill
 from tests.test_gpu_ring import make_ring, resident_decode, ring_decode
 
 pytestmark = pytest.mark.gpu
@@ -157,9 +158,6 @@ def test_q2_argument_checks():
     table = torch.zeros(dims.n_experts, dtype=torch.int64, device="cuda")
     r = torch.zeros((4, dims.d_model), dtype=torch.float32, device="cuda")
     u = torch.zeros(dims.n_experts + 1, dtype=torch.int32, device="cuda")
-    # layer-major prefill takes SMOE-Q4 blobs only: rejected before any launch
-    with pytest.raises(smoe.SmoeError, match="Q4"):
-        smoe.moe_prefill_chunk(dims, x, idx, w, table, r, u, u, u, idx, ws)
     for bad in (dims.replace(chunk=32), synth.Dims(256, 128, 16, 4, 64, bits=2)):
         with pytest.raises(smoe.SmoeError, match="Q2"):
             smoe.moe_decode(bad, x[0], idx[0], w[0], table, r[0], ws)
@@ -189,3 +187,42 @@ def test_q2_decode_layers_selection_other_expert_counts(E, k):
         check_moe_output(res_next.astype(np.float64) - res.astype(np.float64), ref["y"], f"q2 E{E} k{k} L{L}")
         res = res_next
     assert np.array_equal(res, r.cpu().numpy())
+
+
+# d_ff 256, 384, 768 and 1536 take the down GEMM's K blocks of 256, 128, 256
+# and 512 codes (8-byte code loads at 128)
+@pytest.mark.parametrize("shape,T,zipf,sample", [
+    ("small", 1, 0.0, None), ("small", 64, 0.0, None), ("ragged", 17, 1.1, None), ("ragged", 64, 0.0, None),
+    ("q30b", 64, 1.1, [0, 31, 63]), ("q235b", 64, 1.1, [0, 13, 40, 63]), ("q235b", 9, 0.0, [0, 8]),
+])
+def test_q2_prefill_parity(shape, T, zipf, sample):
+    dims = Q2[shape]
+    say(f"[q2-prefill] {shape} T={T} zipf={zipf}")
+    stack = DeviceStack(1337, dims, 1, zipf_s=zipf)
+    res = random_residual(np.random.default_rng(T + 3), T, dims.d_model, scale=1.5)
+    got = run_prefill(dims, stack, 0, res)
+    say(f"[q2-prefill] |union| = {check_union(got, T, dims.top_k)}")
+    experts = LazyExperts(1337, dims, 0)
+    worst = 0.0
+    for t in (range(T) if sample is None else sample):
+        ref = oracle.moe_layer(res[t].astype(np.float64), stack.router_bits[0], experts, dims,
+                               bias=None if stack.bias_np is None else stack.bias_np[0])
+        assert got["idx"][t].tolist() == ref["idx"], f"token {t}"
+        y = got["r_out"][t].astype(np.float64) - res[t].astype(np.float64)
+        worst = max(worst, check_moe_output(y, ref["y"], f"q2 prefill {shape} t{t}"))
+    say(f"[q2-prefill] {shape} T={T}: worst rel-L2 {worst:.2e}")
+
+
+def test_q2_prefill_full_m_tiles_and_matches_decode():
+    """64 copies of one hidden state (every union expert gets 4 M tiles of 16
+    rows): bitwise equal rows, and within tolerance of SMOE-Q2 decode."""
+    dims = Q2["q30b"]
+    stack = DeviceStack(1337, dims, 1)
+    h = random_residual(np.random.default_rng(21), 1, dims.d_model)
+    res = np.repeat(h, 64, axis=0)
+    got = run_prefill(dims, stack, 0, res)
+    assert check_union(got, 64, dims.top_k) == dims.top_k
+    assert np.all(got["r_out"] == got["r_out"][0:1])
+    _, _, _, r_dec = _decode_one_layer(dims, stack, 0, h[0])
+    check_moe_output(got["r_out"][0].astype(np.float64) - h[0], r_dec.astype(np.float64) - h[0],
+                     "q2 prefill vs decode")
