@@ -346,7 +346,7 @@ def bench_prefill(args):
     weights (mean -scale/2 per element) the residual drifts to one common
     direction within ~10 layers and every token then routes alike, so the
     unions collapse."""
-    wl = synth.CONFIGS[3]
+    wl = synth.CONFIGS[3] if args.quant == "q4" else synth.Q2_WORKLOADS[3]
     dims = wl.dims
     T, C = wl.steps, wl.prefill_chunk
     n_chunks = T // C
@@ -403,10 +403,12 @@ def bench_prefill(args):
     f = res["fresh"]
     out = {
         "metric": "layer-major prefill prompt tokens/s + GB/s on union expert bytes (235B-shape, 512-token "
-                  "prompt, chunks of 64)",
+                  "prompt, chunks of 64" + (")" if dims.bits == 4 else ", SMOE-Q2)"),
         "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q4-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded per chunk; float64 router",
+        "dtype": ("q4-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded per chunk; "
+                  "float64 router" if dims.bits == 4 else
+                  "q2-affine weights dequantised to fp16, fp16 MFMA with fp32 accumulation; float64 router"),
         "data": "synthetic (seeded SplitMix64 codes/scales, N(0,0.02) router, Zipf(1.1) logit bias, N(0,1) bf16 "
                 "prompt hidden states fed to every layer)",
         "config": {"workload": wl.name, "layers": NL, "prompt_tokens": T, "chunk": C,
@@ -669,7 +671,9 @@ def bench_ring_prefill(args):
                   "1536-slot HBM ring over a host vault)",
         "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "q4-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded per chunk; float64 router",
+        "dtype": ("q4-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded per chunk; "
+                  "float64 router" if dims.bits == 4 else
+                  "q2-affine weights dequantised to fp16, fp16 MFMA with fp32 accumulation; float64 router"),
         "data": "synthetic (Zipf(1.1) logit bias, N(0,1) bf16 prompt hidden states fed to every layer)",
         "config": {"workload": wl.name + "-ring1536", "layers": NL, "prompt_tokens": T, "chunk": C,
                    "ring_slots": n_slots, "parallelism": "single GPU"},
@@ -749,7 +753,7 @@ def main():
                     help="prefill workload: run only the first N layers (for counter passes; the default line "
                          "runs all 94)")
     ap.add_argument("--quant", choices=["q4", "q2"], default="q4",
-                    help="decode and ring workloads: SMOE-Q4 blobs, or the SMOE-Q2 variant (2-bit codes)")
+                    help="decode, ring and prefill workloads: SMOE-Q4 blobs, or the SMOE-Q2 variant (2-bit codes)")
     ap.add_argument("--shape", choices=["235b", "30b"], default="235b",
                     help="decode workload: the Qwen3-235B-A22B-shaped stack (94 layers, d_model 4096) or the "
                          "Qwen3-30B-A3B-shaped one (48 layers, d_model 2048, 256 steps by default)")
@@ -760,9 +764,8 @@ def main():
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
               "MI355X (the layer has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
-    if args.quant == "q2" and args.workload not in ("decode", "ring"):
-        print("--quant q2 applies to the decode and ring workloads: layer-major prefill takes SMOE-Q4 blobs only",
-              file=sys.stderr)
+    if args.quant == "q2" and args.workload not in ("decode", "ring", "prefill"):
+        print("--quant q2 applies to the decode, ring and prefill workloads", file=sys.stderr)
         sys.exit(2)
     if args.shape != "235b" and args.workload != "decode":
         print("--shape applies to the decode workload only", file=sys.stderr)

@@ -79,4 +79,9 @@ QWEN30B_DECODE_Q2 = Workload(
     dims=Dims(2048, 768, 128, 8, 64, bits=2),
     n_layers=48, steps=256, mode="decode")
 
-Q2_WORKLOADS = [QWEN235B_DECODE_Q2, QWEN235B_RING_Q2, QWEN30B_DECODE_Q2]
+QWEN235B_PREFILL_Q2 = Workload(
+    name="qwen3-235b-a22b-shape-prefill-512tok-chunk64-94L-zipf1.1-q2c64",
+    dims=Dims(4096, 1536, 128, 8, 64, bits=2),
+    n_layers=94, steps=512, mode="prefill", prefill_chunk=64, zipf_s=1.1)
+
+Q2_WORKLOADS = [QWEN235B_DECODE_Q2, QWEN235B_RING_Q2, QWEN30B_DECODE_Q2, QWEN235B_PREFILL_Q2]
