@@ -12,10 +12,11 @@
 //               the chunk's token rows staged in LDS as fp16, SwiGLU in the
 //               epilogue -> H [T*k][d_ff] fp16.  Chunk 64 (d_model, d_ff
 //               multiples of 256): the raw codes enter MFMA and the affine
-//               step is folded per chunk (the *_fold kernels); otherwise, and
-//               for SMOE-Q2 blobs, the codes are dequantised to fp16 in
-//               registers (exact when min = -8 * scale, or -2 * scale for
-//               SMOE-Q2).
+//               step is folded per chunk (the *_fold kernels; for SMOE-Q2
+//               blobs the *_fold_q2 kernels); otherwise the codes are
+//               dequantised to fp16 in registers (exact when min = -8 * scale,
+//               or -2 * scale for SMOE-Q2, whose down GEMM takes this form
+//               when d_ff is not a multiple of 512).
 //   3. down:    grouped GEMM H x D^T per union expert -> Y [T*k][d_model] fp32,
 //               in the same two forms.
 //   4. combine: residual[t] += sum_r w[t][r] * Y[position of (t, r)], in rank
@@ -223,12 +224,11 @@ struct KBlock {
 // A slice's token rows for one K block (16 rows x KT fp16) staged in LDS.
 // Thread (r = tid / 16, c = tid % 16) moves KT / 16 consecutive values of row
 // r; load() and store() are separate so the loads run a block ahead.  From
-// bf16, the values are stored in the pair order of code width BITS (groups of
-// 8 for Q4, of 16 for SMOE-Q2); fp16 rows (H) already are.
-template <bool FROM_BF16, int KT, int BITS = 4>
+// bf16, the values are stored in the pair order of groups of 8; fp16 rows (H)
+// are copied as they are (in the pair order of their code width).
+template <bool FROM_BF16, int KT>
 struct RowStage {
   static constexpr int V = KT / 16 / 8;  // uint4 (8 values) per thread
-  static_assert(!FROM_BF16 || BITS == 4 || V % 2 == 0, "a thread holds whole groups of 16");
   uint4 v[V];
 
   __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
@@ -242,26 +242,6 @@ struct RowStage {
 
   __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8]) const {
     const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * (KT / 16);
-    if constexpr (FROM_BF16 && BITS == 2) {
-#pragma unroll
-      for (int j = 0; j < V; j += 2) {
-        const uint32_t w8[8] = {v[j].x, v[j].y, v[j].z, v[j].w, v[j + 1].x, v[j + 1].y, v[j + 1].z, v[j + 1].w};
-        uint32_t e[16];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          e[2 * p] = f16_bits(bf16_to_f32(w8[p] & 0xFFFF));
-          e[2 * p + 1] = f16_bits(bf16_to_f32(w8[p] >> 16));
-        }
-        // dword p of the group holds (e_p, e_{p+8})
-        const uint4 o0 = make_uint4(e[0] | (e[8] << 16), e[1] | (e[9] << 16), e[2] | (e[10] << 16),
-                                    e[3] | (e[11] << 16));
-        const uint4 o1 = make_uint4(e[4] | (e[12] << 16), e[5] | (e[13] << 16), e[6] | (e[14] << 16),
-                                    e[7] | (e[15] << 16));
-        *reinterpret_cast<uint4*>(&xs[r][c + 8 * j]) = o0;
-        *reinterpret_cast<uint4*>(&xs[r][c + 8 * j + 8]) = o1;
-      }
-      return;
-    }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       uint4 o;
@@ -414,9 +394,9 @@ __device__ __forceinline__ bool slice_info(const PrefillArgs& a, SliceInfo& si) 
   return si.n_rows > 0;
 }
 
-template <int CHUNK, int KT, int BITS = 4>
+template <int CHUNK, int KT>
 __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
-  using F = WFormat<CHUNK, KT, BITS>;
+  using F = WFormat<CHUNK, KT, 4>;
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ int rows[16];
   SliceInfo si;
@@ -428,14 +408,14 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
   if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
   __syncthreads();
   const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
-  const size_t row_bytes = (size_t)a.d * BITS / 8, prow = (size_t)(a.d / CHUNK) * 4;
+  const size_t row_bytes = (size_t)a.d / 2, prow = (size_t)(a.d / CHUNK) * 4;
   const uint8_t* gc = blob + (size_t)n0 * row_bytes;
   const uint8_t* uc = blob + a.lay.up_codes + (size_t)n0 * row_bytes;
   const uint8_t* gp = blob + a.lay.gate_params + (size_t)n0 * prow;
   const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
   const int nk = a.d / KT;
-  RowStage<true, KT, BITS> xr;
+  RowStage<true, KT> xr;
   typename F::Block g0, u0, g1, u1;
   xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
   g0.load(gc, gp, 0, lane);
@@ -456,7 +436,7 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
     __syncthreads();
   }
   // epilogue: lane holds rows 4 (l / 16) + i of the tile, feature n0
-  const int hcol = pair_index<BITS>(n0);
+  const int hcol = pair_index<4>(n0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * (lane >> 4) + i;
@@ -644,7 +624,8 @@ __device__ __forceinline__ void load_lines256(FoldW<256>& w, const uint8_t* code
     w.c[q] = gload16(codes_row0 + (size_t)(8 * q + (lane >> 3)) * row_bytes + kb / 2 + 16 * (lane & 7));
   w.p[0] = gload16(par_row + (kb / 64) * 4);
 }
-__device__ __forceinline__ void relayout256(FoldW<256>& w, uint8_t* stage, int lane) {
+template <class W>
+__device__ __forceinline__ void relayout256(W& w, uint8_t* stage, int lane) {
 #pragma unroll
   for (int q = 0; q < 2; ++q)
     *reinterpret_cast<uint4*>(stage + (8 * q + (lane >> 3)) * kLineStageRow + 16 * (lane & 7)) = w.c[q];
@@ -814,6 +795,255 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 2-3 for SMOE-Q2 blobs: the chunk fold above on 2-bit codes.  A K block is
+// 512 codes, one 128-byte line per row and eight chunks: each 16-byte piece
+// of the line is one chunk, so the line-wise loads, the LDS relayout and the
+// 4x4 transpose above serve unchanged, and after the transpose lane group g
+// holds dword g (the chunk's elements 16 g .. 16 g + 15) of every chunk.
+// Masking a code at bits 2..3 of a byte gives 4 q 2^-24, so the odd elements'
+// inputs are staged divided by 4.  Token rows and H are in the pair order of
+// groups of 16 (dword p of a group = (e_p, e_{p+8})): MFMA step (chunk c, half
+// h) takes from lane group g the A values at 64 c + 16 g + 8 h and the codes
+// of the low (h = 0) or high half of its dword.
+// ---------------------------------------------------------------------------
+
+// Codes (e0, e8, 4 e1, 4 e9, e2, e10, 4 e3, 4 e11) * 2^-24 of a code dword
+// (the caller passes the dword shifted right by 8 for e4..e7, e12..e15).
+__device__ __forceinline__ half8_t codes8_q2(uint32_t w) {
+  const uint32_t w4 = w >> 4;
+  const uint4 r = make_uint4(w & 0x00030003u, w & 0x000C000Cu, w4 & 0x00030003u, w4 & 0x000C000Cu);
+  return __builtin_bit_cast(half8_t, r);
+}
+
+// A slice's 16 token rows for one K block of 512 as fp16 in the 16-group pair
+// order, the odd elements divided by 4, and each row's sum over each chunk of
+// 64 (xsum[chunk of the block][row]).  Thread (r = tid / 16, k = tid % 16)
+// takes the groups 16 j + k (two adjacent 16-byte pieces each) of row r; a
+// chunk's four groups sit in four adjacent lanes.
+template <bool FROM_BF16>
+struct FoldStageQ2 {
+  uint4 v[4];
+
+  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (r < n_rows)
+        v[i] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb +
+                       16 * (16 * (i >> 1) + k) + 8 * (i & 1));
+    }
+  }
+
+  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16]) const {
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
+    const uint32_t k4 = 0x34003400u;  // (1/4, 1/4) in fp16
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 o0, o1;
+      float part = 0.f;
+      if (FROM_BF16) {  // bf16 in natural order -> fp16 pairs (e_p, e_{p+8})
+        const uint32_t w8[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
+                                v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+        float f[16];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          f[2 * p] = (float)(_Float16)bf16_to_f32(w8[p] & 0xFFFF);
+          f[2 * p + 1] = (float)(_Float16)bf16_to_f32(w8[p] >> 16);
+        }
+#pragma unroll
+        for (int p = 0; p < 16; ++p) part += f[p];
+        o0.x = f16_bits(f[0]) | (f16_bits(f[8]) << 16);
+        o0.y = f16_bits(f[1] * 0.25f) | (f16_bits(f[9] * 0.25f) << 16);
+        o0.z = f16_bits(f[2]) | (f16_bits(f[10]) << 16);
+        o0.w = f16_bits(f[3] * 0.25f) | (f16_bits(f[11] * 0.25f) << 16);
+        o1.x = f16_bits(f[4]) | (f16_bits(f[12]) << 16);
+        o1.y = f16_bits(f[5] * 0.25f) | (f16_bits(f[13] * 0.25f) << 16);
+        o1.z = f16_bits(f[6]) | (f16_bits(f[14]) << 16);
+        o1.w = f16_bits(f[7] * 0.25f) | (f16_bits(f[15] * 0.25f) << 16);
+      } else {  // fp16 already in pair order (H): divide the odd dwords by 4
+        const uint32_t w8[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
+                                v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const h2_t hv = as_h2(w8[p]);
+          part += (float)hv[0] + (float)hv[1];
+        }
+        o0 = v[2 * j];
+        o1 = v[2 * j + 1];
+        o0.y = __builtin_bit_cast(uint32_t, as_h2(o0.y) * as_h2(k4));
+        o0.w = __builtin_bit_cast(uint32_t, as_h2(o0.w) * as_h2(k4));
+        o1.y = __builtin_bit_cast(uint32_t, as_h2(o1.y) * as_h2(k4));
+        o1.w = __builtin_bit_cast(uint32_t, as_h2(o1.w) * as_h2(k4));
+      }
+      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k)]) = o0;
+      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k) + 8]) = o1;
+      part = group_sum<4>(part);
+      if ((k & 3) == 0) xsum[4 * j + (k >> 2)][r] = part;
+    }
+  }
+};
+
+// One K block (512 codes) of one weight row per lane after the relayout:
+// pieces (= chunks) 4 q + g, and the (scale, min) words of the block's eight
+// chunks.
+struct FoldWQ2 {
+  uint4 c[2];
+  uint4 p[2];
+};
+
+// Line-wise loads of one K block for the 16 rows of a wave (as load_lines256).
+__device__ __forceinline__ void load_lines_q2(FoldWQ2& w, const uint8_t* codes_row0, size_t row_bytes,
+                                              const uint8_t* par_row, int kb, int lane) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    w.c[q] = gload16(codes_row0 + (size_t)(8 * q + (lane >> 3)) * row_bytes + kb / 4 + 16 * (lane & 7));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) w.p[q] = gload16(par_row + (kb / 64) * 4 + 16 * q);
+}
+
+// acc += sum over the block's eight chunks of s_c P_c + m_c X_c, four chunks
+// (one transposed piece row) at a time: their MFMA chains first, then the
+// folds.
+__device__ __forceinline__ void fold_kblock_q2(float4_t& acc, const FoldWQ2& w, _Float16 (*xs)[512 + 8],
+                                               float (*xsum)[16], int lane) {
+  const int g = lane >> 4, ml = lane & 15, r4 = 4 * (lane >> 4);
+  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    uint32_t u[4] = {w.c[q].x, w.c[q].y, w.c[q].z, w.c[q].w};
+    xpose4(u);  // u[j] = dword g of chunk 4 q + j
+    float4_t P[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16* xr = &xs[ml][64 * (4 * q + j) + 16 * g];
+      const half8_t a0 = *reinterpret_cast<const half8_t*>(xr);
+      const half8_t a1 = *reinterpret_cast<const half8_t*>(xr + 8);
+      P[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, codes8_q2(u[j]), zero, 0, 0, 0);
+      P[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, codes8_q2(u[j] >> 8), P[j], 0, 0, 0);
+    }
+    const uint32_t pw[4] = {w.p[q].x, w.p[q].y, w.p[q].z, w.p[q].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float S = __uint_as_float(pw[j] << 16) * 16777216.0f;  // scale * 2^24
+      const float M = __uint_as_float(pw[j] & 0xFFFF0000u);
+      const float4 X = *reinterpret_cast<const float4*>(&xsum[4 * q + j][r4]);
+      acc[0] = fmaf(S, P[j][0], fmaf(M, X.x, acc[0]));
+      acc[1] = fmaf(S, P[j][1], fmaf(M, X.y, acc[1]));
+      acc[2] = fmaf(S, P[j][2], fmaf(M, X.z, acc[2]));
+      acc[3] = fmaf(S, P[j][3], fmaf(M, X.w, acc[3]));
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void prefill_gate_up_fold_q2_kernel(PrefillArgs a) {
+  constexpr int KT = 512;
+  __shared__ _Float16 xs[2][16][KT + 8];
+  __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
+  __shared__ int rows[16];
+  __shared__ __attribute__((aligned(16))) uint8_t wst[4][2][16 * kLineStageRow];
+  const int n_slices = *a.n_slices;
+  const PrefillArgs::SliceRec rec = a.recs[blockIdx.y];
+  if ((int)blockIdx.y >= n_slices || !rec.blob) return;
+  const int o = rec.o, n_rows = rec.n_rows;
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(rec.blob);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const size_t row_bytes = (size_t)a.d / 4, prow = (size_t)(a.d / 64) * 4;
+  const uint8_t* gp = blob + a.lay.gate_params + (size_t)n0 * prow;
+  const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
+  float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
+  const int nk = a.d / KT;
+  FoldStageQ2<true> xr;
+  FoldWQ2 g0, u0, g1, u1;
+  const size_t nw0 = (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;  // the wave's first row
+  const uint8_t* gc0 = blob + nw0;  // gate codes start the blob
+  const uint8_t* uc0 = blob + a.lay.up_codes + nw0;
+  uint8_t* gst = wst[wave][0];
+  uint8_t* ust = wst[wave][1];
+  load_lines_q2(g0, gc0, row_bytes, gp, 0, lane);
+  load_lines_q2(u0, uc0, row_bytes, up, 0, lane);
+  if (tid < n_rows) rows[tid] = a.perm[o + tid] / a.k;  // token of each entry
+  __syncthreads();
+  xr.load(a.x, (size_t)a.d, rows, n_rows, 0);
+  xr.store(xs[0], xsum[0]);
+  relayout256(g0, gst, lane);
+  relayout256(u0, ust, lane);
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) {
+      xr.load(a.x, (size_t)a.d, rows, n_rows, (i + 1) * KT);
+      load_lines_q2(g1, gc0, row_bytes, gp, (i + 1) * KT, lane);
+      load_lines_q2(u1, uc0, row_bytes, up, (i + 1) * KT, lane);
+    }
+    fold_kblock_q2(ag, g0, xs[i & 1], xsum[i & 1], lane);
+    fold_kblock_q2(au, u0, xs[i & 1], xsum[i & 1], lane);
+    if (i + 1 < nk) {
+      xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+      relayout256(g1, gst, lane);
+      relayout256(u1, ust, lane);
+    }
+    g0 = g1;
+    u0 = u1;
+    __syncthreads();
+  }
+  const int hcol = pair_index<2>(n0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    if (row < n_rows) a.H[(size_t)(o + row) * a.f + hcol] = (_Float16)(silu_f32(ag[i]) * au[i]);
+  }
+}
+
+__global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a) {
+  constexpr int KT = 512;
+  __shared__ _Float16 xs[2][16][KT + 8];
+  __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
+  __shared__ int rows[16];
+  __shared__ __attribute__((aligned(16))) uint8_t wst[4][16 * kLineStageRow];
+  const int n_slices = *a.n_slices;
+  const PrefillArgs::SliceRec rec = a.recs[blockIdx.y];
+  if ((int)blockIdx.y >= n_slices || !rec.blob) return;
+  const int o = rec.o, n_rows = rec.n_rows;
+  const uint8_t* blob = reinterpret_cast<const uint8_t*>(rec.blob);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const size_t row_bytes = (size_t)a.f / 4, prow = (size_t)(a.f / 64) * 4;
+  const uint8_t* dp = blob + a.lay.down_params + (size_t)n0 * prow;
+  const uint8_t* dc0 = blob + a.lay.down_codes + (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;
+  uint8_t* dst = wst[wave];
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  const int nk = a.f / KT;
+  FoldStageQ2<false> hr;
+  FoldWQ2 w0, w1;
+  load_lines_q2(w0, dc0, row_bytes, dp, 0, lane);
+  if (tid < n_rows) rows[tid] = o + tid;  // H rows of this slice
+  __syncthreads();
+  hr.load(a.H, (size_t)a.f, rows, n_rows, 0);
+  hr.store(xs[0], xsum[0]);
+  relayout256(w0, dst, lane);
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    if (i + 1 < nk) {
+      hr.load(a.H, (size_t)a.f, rows, n_rows, (i + 1) * KT);
+      load_lines_q2(w1, dc0, row_bytes, dp, (i + 1) * KT, lane);
+    }
+    fold_kblock_q2(acc, w0, xs[i & 1], xsum[i & 1], lane);
+    if (i + 1 < nk) {
+      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+      relayout256(w1, dst, lane);
+    }
+    w0 = w1;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    if (row < n_rows) a.Y[(size_t)(o + row) * a.d + n0] = acc[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 4. Combine.  grid = (ceil(d / 256), T), 256 threads: residual[t][n] +=
 // sum_r w[t][r] * Y[invperm[t*k + r]][n], r ascending.
 // ---------------------------------------------------------------------------
@@ -845,9 +1075,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   // K blocks of 256 codes for gate/up (two matrices in registers), 512 for
   // down, when K allows (runs of 128 / 256 bytes per row); else 128
   constexpr int GKT = SMOE_PF_GU_KT, DKT = SMOE_PF_DN_KT;
-  if (a.bits == 2) {  // SMOE-Q2 (chunk 64, d_model a multiple of 512): fp16 dequant per weight
-    hipLaunchKernelGGL((prefill_gate_up_kernel<64, 256, 2>), gu, dim3(256), 0, s, a);
-    if (a.f % 512 == 0) hipLaunchKernelGGL((prefill_down_kernel<64, 512, 2>), dn, dim3(256), 0, s, a);
+  if (a.bits == 2) {  // SMOE-Q2 (chunk 64, d_model a multiple of 512): folded per chunk in K
+    // blocks of 512; a d_ff that is not a multiple of 512 takes the fp16-dequant down GEMM
+    hipLaunchKernelGGL(prefill_gate_up_fold_q2_kernel, gu, dim3(256), 0, s, a);
+    if (a.f % 512 == 0) hipLaunchKernelGGL(prefill_down_fold_q2_kernel, dn, dim3(256), 0, s, a);
     else if (a.f % 256 == 0) hipLaunchKernelGGL((prefill_down_kernel<64, 256, 2>), dn, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((prefill_down_kernel<64, 128, 2>), dn, dim3(256), 0, s, a);
   } else if (a.chunk == 64 && a.d % 256 == 0 && a.f % 256 == 0) {  // affine folded per chunk

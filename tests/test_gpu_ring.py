@@ -222,11 +222,12 @@ def prefill_layers(dims, stack, chunk, ring=None):
     return outs, unions
 
 
-@pytest.mark.parametrize("n_slots", [64, 150])
-def test_ring_backed_prefill_matches_resident_and_oracle_log(n_slots):
+@pytest.mark.parametrize("bits,n_slots", [(4, 64), (4, 150), (2, 64)])
+def test_ring_backed_prefill_matches_resident_and_oracle_log(bits, n_slots):
     """Ring-backed layer-major prefill: acquisitions are whole chunk unions
-    (up to min(E, n_slots) experts, fills issued in first-touch order)."""
-    dims = synth.Dims(256, 128, 64, 4, 32)
+    (up to min(E, n_slots) experts, fills issued in first-touch order), on
+    SMOE-Q4 and SMOE-Q2 blobs."""
+    dims = synth.Dims(256, 128, 64, 4, 32) if bits == 4 else synth.Dims(512, 128, 64, 4, 64, bits=2)
     n_layers, T = 4, 20
     stack = DeviceStack(1337, dims, n_layers, zipf_s=1.1)
     rng = np.random.default_rng(5)
