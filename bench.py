@@ -406,9 +406,8 @@ def bench_prefill(args):
                   "prompt, chunks of 64" + (")" if dims.bits == 4 else ", SMOE-Q2)"),
         "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("q4-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded per chunk; "
-                  "float64 router" if dims.bits == 4 else
-                  "q2-affine weights dequantised to fp16, fp16 MFMA with fp32 accumulation; float64 router"),
+        "dtype": f"q{dims.bits}-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded "
+                 "per chunk; float64 router",
         "data": "synthetic (seeded SplitMix64 codes/scales, N(0,0.02) router, Zipf(1.1) logit bias, N(0,1) bf16 "
                 "prompt hidden states fed to every layer)",
         "config": {"workload": wl.name, "layers": NL, "prompt_tokens": T, "chunk": C,
@@ -671,9 +670,8 @@ def bench_ring_prefill(args):
                   "1536-slot HBM ring over a host vault)",
         "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("q4-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded per chunk; "
-                  "float64 router" if dims.bits == 4 else
-                  "q2-affine weights dequantised to fp16, fp16 MFMA with fp32 accumulation; float64 router"),
+        "dtype": f"q{dims.bits}-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded "
+                 "per chunk; float64 router",
         "data": "synthetic (Zipf(1.1) logit bias, N(0,1) bf16 prompt hidden states fed to every layer)",
         "config": {"workload": wl.name + "-ring1536", "layers": NL, "prompt_tokens": T, "chunk": C,
                    "ring_slots": n_slots, "parallelism": "single GPU"},
