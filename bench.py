@@ -566,7 +566,8 @@ def bench_ring(args):
 
 
 def bench_ring_prefill(args):
-    """Layer-major prefill through the 1536-slot HBM ring over the host vault:
+    """Layer-major prefill through the HBM ring over the host vault (1536 slots for
+    SMOE-Q4, 2764 for SMOE-Q2: the same 16.31 GB of HBM):
     the 512-token prompt in chunks of 64 with the Zipf(1.1) logit bias, every
     layer fed the prompt (as the prefill workload does).  Per chunk and layer
     the routing is read back, the expert union is acquired in first-touch
@@ -579,12 +580,13 @@ def bench_ring_prefill(args):
     ``layer_outer`` takes the layers in turn, each over all chunks, so that a
     layer's union is loaded once and the later chunks hit it in the ring."""
     from synth.device import router_stack, u16_to_device
-    wl = synth.CONFIGS[3]
+    wl = synth.CONFIGS[3] if args.quant == "q4" else synth.Q2_WORKLOADS[3]
     dims = wl.dims
     E, NL, k = dims.n_experts, wl.n_layers, dims.top_k
     T, C = wl.steps, wl.prefill_chunk
     n_chunks = T // C
-    n_slots = synth.CONFIGS[4].ring_slots
+    # the decode ring's slot count for the code width (the same 16.31 GB of HBM)
+    n_slots = (synth.CONFIGS[4] if args.quant == "q4" else synth.Q2_WORKLOADS[1]).ring_slots
     torch.cuda.set_device(0)
     off = synth.blob_sections(dims)
     stride = off["stride"]
@@ -667,13 +669,13 @@ def bench_ring_prefill(args):
     f = res["chunk"]
     out = {
         "metric": "ring-backed layer-major prefill prompt tokens/s (235B-shape, 512-token prompt, chunks of 64, "
-                  "1536-slot HBM ring over a host vault)",
+                  f"{n_slots}-slot HBM ring over a host vault" + (")" if dims.bits == 4 else ", SMOE-Q2)"),
         "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": f"q{dims.bits}-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded "
                  "per chunk; float64 router",
         "data": "synthetic (Zipf(1.1) logit bias, N(0,1) bf16 prompt hidden states fed to every layer)",
-        "config": {"workload": wl.name + "-ring1536", "layers": NL, "prompt_tokens": T, "chunk": C,
+        "config": {"workload": f"{wl.name}-ring{n_slots}", "layers": NL, "prompt_tokens": T, "chunk": C,
                    "ring_slots": n_slots, "parallelism": "single GPU"},
         "mean_union": f["mean_union"], "hit_rate": f["hit_rate"], "misses_per_prompt": f["misses_per_prompt"],
         "h2d_bytes_per_prompt": f["h2d_bytes_per_prompt"], "h2d_gbps": f["h2d_gbps"],
@@ -751,7 +753,7 @@ def main():
                     help="prefill workload: run only the first N layers (for counter passes; the default line "
                          "runs all 94)")
     ap.add_argument("--quant", choices=["q4", "q2"], default="q4",
-                    help="decode, ring and prefill workloads: SMOE-Q4 blobs, or the SMOE-Q2 variant (2-bit codes)")
+                    help="SMOE-Q4 blobs, or the SMOE-Q2 variant (2-bit codes)")
     ap.add_argument("--shape", choices=["235b", "30b"], default="235b",
                     help="decode workload: the Qwen3-235B-A22B-shaped stack (94 layers, d_model 4096) or the "
                          "Qwen3-30B-A3B-shaped one (48 layers, d_model 2048, 256 steps by default)")
@@ -762,8 +764,8 @@ def main():
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
               "MI355X (the layer has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
-    if args.quant == "q2" and args.workload not in ("decode", "ring", "prefill"):
-        print("--quant q2 applies to the decode, ring and prefill workloads", file=sys.stderr)
+    if args.quant == "q2" and args.workload == "copy":
+        print("--quant q2 applies to the decode, ring, prefill and ring-prefill workloads", file=sys.stderr)
         sys.exit(2)
     if args.shape != "235b" and args.workload != "decode":
         print("--shape applies to the decode workload only", file=sys.stderr)
