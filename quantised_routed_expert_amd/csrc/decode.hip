@@ -27,6 +27,8 @@
 #ifndef SMOE_GU_WAVES
 #define SMOE_GU_WAVES 4        // waves per gate/up workgroup (a multiple of 2)
 #endif
+// every gate/up thread stages one logit and one blob pointer of the layer
+static_assert(64 * SMOE_GU_WAVES >= smoe::kMaxExperts, "a gate/up workgroup needs a thread per expert");
 #ifndef SMOE_GU_ROWS_MAX
 #define SMOE_GU_ROWS_MAX 4     // rows per wave of the gate/up kernel (upper bound)
 #endif
