@@ -213,6 +213,26 @@ def test_q2_prefill_parity(shape, T, zipf, sample):
     say(f"[q2-prefill] {shape} T={T}: worst rel-L2 {worst:.2e}")
 
 
+@pytest.mark.parametrize("dims,T,sample", [
+    # the largest K of the folded gate/up GEMM (16 blocks of 512) and a d_ff of one down block
+    (synth.Dims(8192, 512, 32, 4, 64, bits=2), 17, [0, 9, 16]),
+    # 256 experts, top-16: up to 256 union experts and their slices; d_ff 8192 (16 down blocks)
+    (synth.Dims(512, 256, 256, 16, 64, bits=2), 64, [0, 30, 63]),
+    (synth.Dims(512, 8192, 16, 4, 64, bits=2), 33, [0, 16, 32]),
+], ids=["d_model_8192", "e256_k16", "d_ff_8192"])
+def test_q2_prefill_size_bounds(dims, T, sample):
+    say(f"[q2-prefill-bound] {dims} T={T}")
+    stack = DeviceStack(1337, dims, 1)
+    res = random_residual(np.random.default_rng(T + 5), T, dims.d_model, scale=1.5)
+    got = run_prefill(dims, stack, 0, res)
+    say(f"[q2-prefill-bound] |union| = {check_union(got, T, dims.top_k)}")
+    experts = LazyExperts(1337, dims, 0)
+    for t in sample:
+        ref = oracle.moe_layer(res[t].astype(np.float64), stack.router_bits[0], experts, dims)
+        assert got["idx"][t].tolist() == ref["idx"], f"token {t}"
+        check_moe_output(got["r_out"][t].astype(np.float64) - res[t].astype(np.float64), ref["y"], f"t{t}")
+
+
 def test_q2_prefill_full_m_tiles_and_matches_decode():
     """64 copies of one hidden state (every union expert gets 4 M tiles of 16
     rows): bitwise equal rows, and within tolerance of SMOE-Q2 decode."""
