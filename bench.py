@@ -606,7 +606,6 @@ def bench_ring_prefill(args):
     x = torch.empty((C, dims.d_model), dtype=torch.int16, device="cuda")
     idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
     w = torch.empty((C, k), dtype=torch.float32, device="cuda")
-    idx_host = torch.empty((C, k), dtype=torch.int32, pin_memory=True)
     mu = min(E, C * k)
     uids = torch.empty(mu, dtype=torch.int32, device="cuda")
     ucount = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -619,13 +618,9 @@ def bench_ring_prefill(args):
         r = resid[c * C:(c + 1) * C]
         r.copy_(prompt[c * C:(c + 1) * C])
         smoe.route(dims, r, x, router[L], bias[L], idx, w, ws)
-        idx_host.copy_(idx)
-        torch.cuda.current_stream().synchronize()
-        flat = idx_host.numpy().reshape(-1)              # entry t * k + r
-        first = np.unique(flat, return_index=True)[1]
-        union = flat[np.sort(first)].tolist()            # first-touch order
-        unions.append(len(union))
-        ring.acquire_table(L, union, table)
+        # the library reads the routing back, forms the union in first-touch
+        # order and acquires it (fills in that order), then writes the table
+        unions.append(len(ring.acquire_routed(L, idx, table)))
         smoe.moe_prefill_chunk(dims, x, idx, w, table, r, uids, ucount, offs, perm, ws)
 
     def prompt_run(tag, order):

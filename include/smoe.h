@@ -80,8 +80,8 @@ typedef enum {
 
 /* Geometry of one MoE layer. */
 typedef struct {
-  int32_t d_model;        /* hidden size; multiple of 256, <= 8192          */
-  int32_t d_ff;           /* expert FFN size; multiple of 64, <= 8192        */
+  int32_t d_model;        /* hidden size; multiple of 256, <= 8192           */
+  int32_t d_ff;           /* expert FFN size; multiple of 128, <= 8192       */
   int32_t n_experts;      /* E, 1..256                                       */
   int32_t top_k;          /* k, 1..min(E, 16)                                */
   int32_t chunk;          /* Q4 affine chunk along the reduction dim: 32, 64 */
@@ -153,7 +153,10 @@ int smoe_route_ext(const smoe_dims* dims, int32_t n_tok, const float* residual, 
  *   topk_idx      device int32 [k], topk_w device fp32 [k]
  *   expert_table  device array [E] of device blob pointers (this layer)
  *   residual      device fp32 [d_model], updated in place
- * Deterministic: no atomics, fixed reduction order. */
+ * The activations h_r are kept in fp32 and reach the down projection as fp16
+ * with one power-of-two scale per 32 (SMOE-Q4) or 64 (SMOE-Q2) values, so
+ * they cannot overflow fp16.  An index outside [0, E) or a NULL table entry
+ * contributes nothing.  Deterministic: no atomics, fixed reduction order. */
 int smoe_moe_decode(const smoe_dims* dims, const uint16_t* x, const int32_t* topk_idx,
                     const float* topk_w, const void* const* expert_table, float* residual,
                     void* workspace, size_t workspace_bytes, void* stream);
@@ -205,11 +208,17 @@ int smoe_decode_layers(const smoe_dims* dims, int32_t n_layers, float* residual,
  *                offsets[u]..offsets[u+1]-1 list t*k + r of its tokens, t ascending
  *   residual     device fp32 [n_tok][d_model], += the MoE output per token
  * Each union expert's blob is streamed once per chunk; the grouped FFN runs on
- * MFMA with fp16 inputs: for SMOE-Q4 at chunk 64 the raw codes, with the
- * affine step applied per chunk to the fp32 sums; otherwise (chunk 32, and
- * SMOE-Q2 blobs) the weights dequantised to fp16 (exact for min = -8*scale,
- * and -2*scale for SMOE-Q2).  The per-token mix is summed in rank order; no
- * atomics. */
+ * MFMA with fp16 inputs: at chunk 64 the raw codes, with the affine step
+ * applied per chunk to the fp32 sums; otherwise (chunk 32, and SMOE-Q2 down
+ * projections whose d_ff is not a multiple of 512) the weights dequantised to
+ * fp16 (exact for min = -8*scale, and -2*scale for SMOE-Q2).  The SwiGLU
+ * activations go to the down GEMM as fp16 with one power-of-two scale per
+ * token and 64 features (the tile's largest |h| mapped into [2^14, 2^15)), so
+ * they cannot overflow fp16.  The per-token mix is summed in rank order; no
+ * atomics.  An entry whose expert is outside [0, E) or whose table entry is
+ * NULL (e.g. a ring table that holds only an acquired union) takes no part:
+ * it is left out of the union and contributes nothing.  A token that lists
+ * an expert more than once gets one row per entry (each weight applies). */
 int smoe_moe_prefill_chunk(const smoe_dims* dims, int32_t n_tok, const uint16_t* x,
                            const int32_t* topk_idx, const float* topk_w,
                            const void* const* expert_table, float* residual, int32_t* union_ids,
@@ -289,6 +298,29 @@ int smoe_ring_acquire(smoe_ring* ring, int32_t layer, const int32_t* experts_hos
  * smoe_ring_acquire, plus SMOE_EINVAL for a NULL or unaligned table_dev. */
 int smoe_ring_acquire_table(smoe_ring* ring, int32_t layer, const int32_t* experts_host, int32_t k,
                             void* table_dev, void* compute_stream);
+
+/* Ring-backed layer-major prefill of one chunk ("Prefill Reads Each Expert
+ * Once, Not Once Per Token"): reads the chunk's routing back from the device
+ * (waiting for the work on compute_stream that writes it), forms the chunk's
+ * expert union in first-touch order (t ascending, then rank -- the order in
+ * which the section has each expert sent to the streamer), acquires it (as
+ * smoe_ring_acquire: hits, fills in union order, holds) and writes the
+ * layer's expert table as smoe_ring_acquire_table does, for
+ * smoe_moe_prefill_chunk.
+ *   n_tok, k        the routing's shape: 1..64 tokens, 1..16 ranks
+ *   topk_idx_dev    device int32 [n_tok][k] (smoe_route's topk_idx); ids
+ *                   outside [0, E) take no part
+ *   table_dev       device [E] blob pointers (caller-owned, 8-byte aligned)
+ *   union_host      host int32 [min(E, n_tok*k)] or NULL: the union, in
+ *                   first-touch order
+ *   n_union         host int32 or NULL: |union|
+ * Blocks the calling thread until the routing is on the host (one read of at
+ * most 4 KiB into page-locked memory the ring owns); allocates nothing.
+ * Errors: as smoe_ring_acquire_table (SMOE_EINVAL also when the union exceeds
+ * min(E, n_slots) or holds no valid expert). */
+int smoe_ring_acquire_routed(smoe_ring* ring, int32_t layer, int32_t n_tok, int32_t k,
+                             const int32_t* topk_idx_dev, void* table_dev, int32_t* union_host,
+                             int32_t* n_union, void* compute_stream);
 
 /* Speculative loads ("Speculative prefetch"; "Idle-time popularity
  * prewarm"): each of the n experts of `layer` (host array) that is not

@@ -163,19 +163,24 @@ def expert_ffn(expert: dict, x, chunk: int, return_h: bool = False):
     return y
 
 
-def moe_layer(residual, w_router_bits, experts, dims, bias=None, return_h: bool = False):
+def moe_layer(residual, w_router_bits, experts, dims, bias=None, return_h: bool = False, ffn=None):
     """One routed-MoE layer on one token.
 
     ``experts`` maps an expert index to its logical codes/params (only the
-    selected ones are touched, so a lazy mapping works).  Returns a dict with
-    x (values, bits), logits, idx, w, y (the MoE output, float64) and
-    r_out = residual + y."""
+    selected ones are touched, so a lazy mapping works).  ``ffn``, if given,
+    is called as ffn(e, x, x_bits) in place of expert_ffn(experts[e], x, chunk)
+    (a caller may memoise expert outputs; it must return the same values).
+    Returns a dict with x (values, bits), logits, idx, w, y (the MoE output,
+    float64) and r_out = residual + y."""
     x, xbits = rmsnorm_bf16(residual, dims.rms_eps)
     l = router_logits(w_router_bits, x, bias)
     idx, w = select_topk(l, dims.top_k, dims.norm_topk_prob)
     y = np.zeros(dims.d_model, dtype=np.float64)
     hs = []
     for r, e in enumerate(idx):                       # rank order
+        if ffn is not None and not return_h:
+            y = y + w[r] * ffn(e, x, xbits)
+            continue
         out = expert_ffn(experts[e], x, dims.chunk, return_h=return_h)
         if return_h:
             out, h = out

@@ -22,7 +22,7 @@ EXPORTED = [
     "smoe_workspace_bytes", "smoe_route", "smoe_moe_decode", "smoe_moe_decode_slots",
     "smoe_decode_layers", "smoe_moe_prefill_chunk", "smoe_ring_create", "smoe_ring_acquire",
     "smoe_ring_release", "smoe_ring_stats", "smoe_ring_log", "smoe_ring_destroy", "smoe_ring_acquire_table",
-    "smoe_ring_prefetch", "smoe_ring_hottest", "smoe_route_ext",
+    "smoe_ring_prefetch", "smoe_ring_hottest", "smoe_route_ext", "smoe_ring_acquire_routed",
 ]
 
 
@@ -83,6 +83,8 @@ def lib():
             "smoe_ring_acquire": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, P(VP), VP]),
             "smoe_ring_release": (I, [VP]),
             "smoe_ring_acquire_table": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, VP, VP]),
+            "smoe_ring_acquire_routed": (I, [VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, VP, VP,
+                                             P(ctypes.c_int32), P(ctypes.c_int32), VP]),
             "smoe_ring_prefetch": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, P(ctypes.c_int32), VP]),
             "smoe_ring_hottest": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_uint64),
                                       P(ctypes.c_int32)]),
@@ -219,6 +221,17 @@ class Ring:
         table of blob pointers (NULL for the experts not requested)."""
         ex = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
         _check(lib().smoe_ring_acquire_table(self.h, int(layer), ex, len(experts), _ptr(table), _stream(stream)))
+
+    def acquire_routed(self, layer, topk_idx, table, stream=None):
+        """Acquire the union of a prefill chunk's routing (device int32
+        [n_tok][k]) in first-touch order and write the layer's [E] device
+        table; returns the union (host list)."""
+        n_tok, k = int(topk_idx.shape[0]), int(topk_idx.shape[1])
+        uni = (ctypes.c_int32 * (n_tok * k))()
+        nu = ctypes.c_int32(0)
+        _check(lib().smoe_ring_acquire_routed(self.h, int(layer), n_tok, k, _ptr(topk_idx), _ptr(table), uni,
+                                              ctypes.byref(nu), _stream(stream)))
+        return [int(uni[i]) for i in range(nu.value)]
 
     def prefetch(self, layer, experts, stream=None):
         """Speculative loads of the experts not resident; returns loads issued."""

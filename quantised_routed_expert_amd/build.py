@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libsmoe.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # no packed-fp32 instructions (see the design notes on v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),

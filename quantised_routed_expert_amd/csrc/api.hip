@@ -34,16 +34,14 @@ int check_dims(const smoe_dims* d) {
   if (!d) return fail(SMOE_EINVAL, "dims is NULL");
   if (d->d_model <= 0 || d->d_model > 8192 || d->d_model % 256)
     return fail(SMOE_EINVAL, "d_model=%d must be a multiple of 256 in [256, 8192]", d->d_model);
-  if (d->d_ff <= 0 || d->d_ff > 8192 || d->d_ff % 64)
-    return fail(SMOE_EINVAL, "d_ff=%d must be a multiple of 64 in [64, 8192]", d->d_ff);
+  if (d->d_ff <= 0 || d->d_ff > 8192 || d->d_ff % 128)
+    return fail(SMOE_EINVAL, "d_ff=%d must be a multiple of 128 in [128, 8192]", d->d_ff);
   if (d->n_experts < 1 || d->n_experts > kMaxExperts)
     return fail(SMOE_EINVAL, "n_experts=%d must be in [1, %d]", d->n_experts, kMaxExperts);
   if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > kMaxTopK)
     return fail(SMOE_EINVAL, "top_k=%d must be in [1, min(n_experts, %d)]", d->top_k, kMaxTopK);
   if (d->chunk != 32 && d->chunk != 64) return fail(SMOE_EINVAL, "chunk=%d must be 32 or 64", d->chunk);
   if (!(d->rms_eps >= 0.0f) || d->rms_eps > 1.0f) return fail(SMOE_EINVAL, "rms_eps out of range");
-  if (d->d_model % 128 || d->d_ff % 128)
-    return fail(SMOE_EINVAL, "d_model=%d and d_ff=%d must be multiples of 128", d->d_model, d->d_ff);
   const int bits = quant_bits(d);
   if (bits != 4 && bits != 2) return fail(SMOE_EINVAL, "quant_bits=%d must be 4 (or 0) or 2", d->quant_bits);
   if (bits == 2 && (d->chunk != 64 || d->d_model % 512))
@@ -56,7 +54,7 @@ int check_dims(const smoe_dims* d) {
 
 // Workspace carve-up (offsets from the workspace base, 256-byte aligned).
 struct Workspace {
-  size_t logits, plog, idx, w, ptr, x, px, h, ph, py, pinv, slices, recs, end;
+  size_t logits, plog, idx, w, ptr, x, px, h, ph, phs, py, pinv, slices, recs, end;
 };
 
 Workspace ws_layout(const smoe_dims* d, int max_tokens) {
@@ -71,8 +69,9 @@ Workspace ws_layout(const smoe_dims* d, int max_tokens) {
   w.ptr = o;    o = align_up(o + k * 8, 256);
   w.x = o;      o = align_up(o + T * D * 2, 256);
   w.px = o;     o = align_up(o + D * 2, 256);
-  w.h = o;      o = align_up(o + k * F * 2, 256);
+  w.h = o;      o = align_up(o + k * F * 4, 256);
   w.ph = o;     o = align_up(o + T * k * F * 2, 256);
+  w.phs = o;    o = align_up(o + T * k * (F / 64) * 4, 256);
   w.py = o;     o = align_up(o + T * k * D * 4, 256);
   w.pinv = o;   o = align_up(o + T * k * 4, 256);
   w.slices = o; o = align_up(o + ((T * k + 15) / 16 + (E < T * k ? E : T * k) + 1) * 4, 256);
@@ -101,7 +100,7 @@ static DecodeArgs decode_args(const smoe_dims* d, char* ws, const Workspace& L) 
   a.norm = d->norm_topk_prob ? 1 : 0;
   a.bits = quant_bits(d);
   a.lay = blob_layout(d->d_model, d->d_ff, d->chunk, a.bits);
-  a.h = reinterpret_cast<_Float16*>(ws + L.h);
+  a.h = reinterpret_cast<float*>(ws + L.h);
   return a;
 }
 
@@ -319,6 +318,7 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
   a.n_slices = a.slices + prefill_max_slices(n_tok, d->top_k, d->n_experts);
   a.recs = reinterpret_cast<PrefillArgs::SliceRec*>(base + L.recs);
   a.H = reinterpret_cast<_Float16*>(base + L.ph);
+  a.Hs = reinterpret_cast<float*>(base + L.phs);
   a.Y = reinterpret_cast<float*>(base + L.py);
   a.T = n_tok;
   a.d = d->d_model;

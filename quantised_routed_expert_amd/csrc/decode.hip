@@ -62,10 +62,10 @@ struct LaneRun {
 
 // Pair-ordered f16 input of a lane's NSEG segments (SEGV values each, the
 // columns of its code segments: SEGV * (s * LR + li) onwards) and the
-// per-segment sums, from bf16 (x) or pair-ordered f16 (h) storage.  The raw
-// loads are separate from the conversion so that the weight loads can be
-// issued in between.  `base` points at the lane's first segment; segments are
-// LR * NQ * 16 bytes apart (SEGV two-byte values per lane).
+// per-segment sums, from bf16 or pair-ordered f16 storage (x), or fp32 (h,
+// below).  The raw loads are separate from the conversion so that the weight
+// loads can be issued in between.  `base` points at the lane's first segment;
+// segments are LR * NQ * 16 bytes apart (NQ 16-byte pieces per segment).
 template <int LR, int NSEG, int NQ>
 __device__ __forceinline__ void load_raw(const void* base, uint4 (*raw)[NQ]) {
 #pragma unroll
@@ -95,7 +95,7 @@ __device__ __forceinline__ void pack_bf16_run(const uint4 (*raw)[NQ], uint32_t (
   }
 }
 
-// Pair-ordered f16 storage (the router's prepared x, or h) is used as is.
+// Pair-ordered f16 storage (the router's prepared x) is used as is.
 template <int NSEG, int NQ>
 __device__ __forceinline__ void pack_f16_run(const uint4 (*raw)[NQ], uint32_t (*hp)[NQ * 4], float* xseg) {
 #pragma unroll
@@ -106,6 +106,40 @@ __device__ __forceinline__ void pack_f16_run(const uint4 (*raw)[NQ], uint32_t (*
       hp[s][4 * q + 2] = raw[s][q].z; hp[s][4 * q + 3] = raw[s][q].w;
     }
     xseg[s] = seg_sum<NQ * 4>(hp[s]);
+  }
+}
+
+// fp32 activations (h) of a lane's NSEG segments as pair-ordered f16, each
+// segment with its own power-of-two scale: the segment's largest magnitude is
+// brought into [2^14, 2^15), so no value overflows fp16 (whose largest finite
+// value is 65504) and the largest values keep fp16's full precision; fac[s] is
+// the inverse scale, by which the segment's contribution is multiplied back.
+// Scaling by a power of two is exact; only the f16 rounding is new.  v: the
+// raw fp32 values, NQ4 16-byte pieces (4 floats each) per segment.
+template <int NSEG, int NQ4, int BITS>
+__device__ __forceinline__ void pack_scaled_run(const uint4 (*raw)[NQ4], uint32_t (*hp)[NQ4 * 2], float* xseg,
+                                                float* fac) {
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) {
+    float v[NQ4 * 4];
+#pragma unroll
+    for (int q = 0; q < NQ4; ++q) {
+      v[4 * q + 0] = __uint_as_float(raw[s][q].x);
+      v[4 * q + 1] = __uint_as_float(raw[s][q].y);
+      v[4 * q + 2] = __uint_as_float(raw[s][q].z);
+      v[4 * q + 3] = __uint_as_float(raw[s][q].w);
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQ4 * 4; ++i) mx = fmaxf(mx, fabsf(v[i]));
+    const int sh = f16_block_shift(mx);
+    const float up = __builtin_ldexpf(1.0f, sh);
+    fac[s] = __builtin_ldexpf(1.0f, -sh);
+#pragma unroll
+    for (int i = 0; i < NQ4 * 4; ++i) v[i] *= up;
+    if constexpr (BITS == 4) pack_segment(v, hp[s]);
+    else pack_segment_q2(v, hp[s]);
+    xseg[s] = seg_sum<NQ4 * 2>(hp[s]);
   }
 }
 
@@ -175,10 +209,7 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
     }
     g = group_sum<LR>(g);
     u = group_sum<LR>(u);
-    if (li == 0) {
-      const int n = n_begin + p * P + grp;
-      a.h[(size_t)r * a.f + pair_index<BITS>(n)] = (_Float16)(silu_f32(g) * u);
-    }
+    if (li == 0) a.h[(size_t)r * a.f + n_begin + p * P + grp] = silu_f32(g) * u;
   }
 }
 
@@ -239,10 +270,7 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
     if (blob) {
       gate_up_rows<LR, NSEG, NP, CHUNK, BITS>(a, blob, r, n_begin, li, grp, xraw);
     } else {  // an index outside [0, E) or a null table entry: the rank contributes nothing
-      for (int it = lane; it < RPW; it += kWave) {
-        const int n = n_begin + it;
-        a.h[(size_t)r * a.f + pair_index<BITS>(n)] = (_Float16)0.0f;
-      }
+      for (int it = lane; it < RPW; it += kWave) a.h[(size_t)r * a.f + n_begin + it] = 0.f;
     }
   }
 
@@ -337,14 +365,15 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     const uint8_t* par = blob + a.lay.down_params;
     // an idle lane (li >= LA) keeps zero codes, parameters and inputs, so its
     // contribution is exactly 0
-    uint4 hraw[NSEG][Run::NQ];
+    constexpr int NQ4 = Run::SEGV / 4;  // 16-byte pieces of a segment's fp32 activations
+    uint4 hraw[NSEG][NQ4];
     if (act) {
-      load_raw<LR, NSEG, Run::NQ>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
+      load_raw<LR, NSEG, NQ4>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
     } else {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s)
 #pragma unroll
-        for (int q = 0; q < Run::NQ; ++q) hraw[s][q] = make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < NQ4; ++q) hraw[s][q] = make_uint4(0, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);  // h first: the math can start when it lands
     uint4 c[NPASS][NSEG];
@@ -364,16 +393,17 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
       for (int i = 0; i < kPrefetchPerThread; ++i) pf[i] = gload16(pf_addr[i]);
     }
     __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
-    // h_r for this lane's columns (already pair-ordered) and its segment sums
+    // h_r for this lane's columns as scaled pair-ordered f16, its segment sums
+    // and the segments' inverse scales
     uint32_t hp[NSEG][Run::NDW];
-    float xseg[NSEG];
-    pack_f16_run<NSEG, Run::NQ>(hraw, hp, xseg);
+    float xseg[NSEG], fac[NSEG];
+    pack_scaled_run<NSEG, NQ4, BITS>(hraw, hp, xseg, fac);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       float y = 0.f;
 #pragma unroll
       for (int s = 0; s < NSEG; ++s)
-        y += seg_contrib_b<BITS>(c[p][s], hp[s], xseg[s], pr[p][s]);
+        y = fmaf(fac[s], seg_contrib_b<BITS>(c[p][s], hp[s], xseg[s], pr[p][s]), y);
       y = group_sum<LR>(y);
       if (li == 0) ylds[r][p * P + grp] = y;
     }
@@ -494,6 +524,9 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   const int P = 64 / sp.lr;
   int np = 1;
   while (np * 2 <= SMOE_DN_PASSES_MAX && a.d / (P * np * 2) >= SMOE_DN_MIN_WG) np *= 2;
+  // a lane holding more than 128 fp32 activations takes one row pass (more
+  // would spill registers)
+  if (sp.nseg * (128 / a.bits) > 128) np = 1;
   const int rows = np * P;
   if (a.d % rows) return hipErrorInvalidValue;  // every workgroup owns full rows
   const int nw = a.k < 8 ? a.k : 8;

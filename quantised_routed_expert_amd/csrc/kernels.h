@@ -271,7 +271,7 @@ struct DecodeArgs {
   FusedTopk sel;
   const float* w;           // [k] mixing weights (device), read by the down kernel
   const void* const* ptrs;   // [k] device blob pointers from the router, or null
-  _Float16* h;              // [k][d_ff], pair-ordered within groups of 8 (Q4) or 16 (Q2)
+  float* h;                 // [k][d_ff] SwiGLU activations, fp32 in natural order
   float* residual;          // [d]
   const uint8_t* pf_base;   // next layer's router [E][d] bf16 to pull into cache, or null
   int d, f, E, k, chunk, norm;

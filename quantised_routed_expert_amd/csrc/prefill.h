@@ -24,7 +24,9 @@ struct PrefillArgs {
     int32_t o, n_rows;
   }* recs;                    // [prefill max slices] (workspace, 16-byte aligned)
   _Float16* H;                // [T*k][f] SwiGLU activations, fp16 in the pair order of
-                              // the code width (groups of 8 for Q4, 16 for SMOE-Q2)
+                              // the code width (groups of 8 for Q4, 16 for SMOE-Q2), each
+                              // row's 64-feature tile scaled by a power of two
+  float* Hs;                  // [T*k][f / 64] inverse scale of each tile: H = fp16 * Hs
   float* Y;                   // [T*k][d] per-entry expert outputs
   int T, d, f, E, k, chunk;
   int bits;                   // code width: 4 (SMOE-Q4) or 2 (SMOE-Q2)

@@ -32,7 +32,11 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // 1. Union and permutation.  One workgroup of 1024 threads (thread i <-> entry
-// i = t * k + r of the routing).
+// i = t * k + r of the routing).  An entry whose expert is outside [0, E) or
+// has a NULL table entry takes no part (its invperm is -1, so it contributes
+// nothing, as a null blob does in decode).  Entries are listed per expert in
+// (t, r) order; a token that lists an expert more than once gets one slot per
+// entry (the router never does this; such chunks take a slower serial path).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void prefill_union_kernel(PrefillArgs a) {
   __shared__ int first[kMaxExperts];
@@ -40,27 +44,36 @@ __global__ __launch_bounds__(1024) void prefill_union_kernel(PrefillArgs a) {
   __shared__ unsigned long long tmask[kMaxExperts];
   __shared__ int rank_of[kMaxExperts];
   __shared__ int uid[kMaxExperts];
+  __shared__ int usable[kMaxExperts];
+  __shared__ int eidx[kMaxPrefillTokens * kMaxTopK];
+  __shared__ int pos_of[kMaxPrefillTokens * kMaxTopK];
   __shared__ int scan[2][kMaxExperts + 1];
   __shared__ int sscan[2][kMaxExperts + 1];
-  __shared__ int s_nu;
+  __shared__ int s_nu, s_dup;
   const int tid = threadIdx.x;
   const int n = a.T * a.k;
   if (tid < a.E) {
     first[tid] = 0x7FFFFFFF;
     cnt[tid] = 0;
     tmask[tid] = 0ull;
+    usable[tid] = a.table[tid] != nullptr;
   }
+  if (tid == 0) s_dup = 0;
   __syncthreads();
   int e = -1;
   if (tid < n) {
     e = a.idx[tid];
-    if (e >= 0 && e < a.E) {
-      atomicMin(&first[e], tid);
-      atomicAdd(&cnt[e], 1);
-      atomicOr(&tmask[e], 1ull << (tid / a.k));
-    } else {
-      e = -1;
-    }
+    if (!(e >= 0 && e < a.E && usable[e])) e = -1;
+    eidx[tid] = e;
+  }
+  __syncthreads();
+  if (e >= 0) {
+    atomicMin(&first[e], tid);
+    atomicAdd(&cnt[e], 1);
+    atomicOr(&tmask[e], 1ull << (tid / a.k));
+    const int t0 = tid - tid % a.k;  // the token's first entry
+    for (int j = t0; j < tid; ++j)
+      if (eidx[j] == e) s_dup = 1;   // (benign race: every writer stores 1)
   }
   __syncthreads();
   // rank of each touched expert in first-touch order
@@ -123,16 +136,33 @@ __global__ __launch_bounds__(1024) void prefill_union_kernel(PrefillArgs a) {
     if (tid == nu - 1) *a.n_slices = end;
   }
   if (tid == 0 && nu == 0) *a.n_slices = 0;
-  if (tid < n) {
-    int pos = -1;
-    if (e >= 0) {
-      const int u = rank_of[e];
-      const int base = u == 0 ? 0 : scan[src][u - 1];
-      const int t = tid / a.k;
-      pos = base + __popcll(tmask[e] & ((1ull << t) - 1ull));
-      a.perm[pos] = tid;
+  if (!s_dup) {  // uniform: one entry per (token, expert), placed by its token's rank
+    if (tid < n) {
+      int pos = -1;
+      if (e >= 0) {
+        const int u = rank_of[e];
+        const int base = u == 0 ? 0 : scan[src][u - 1];
+        const int t = tid / a.k;
+        pos = base + __popcll(tmask[e] & ((1ull << t) - 1ull));
+        a.perm[pos] = tid;
+      }
+      a.invperm[tid] = pos;
     }
-    a.invperm[tid] = pos;
+  } else {  // some token lists an expert twice: each expert walks the entries in order
+    if (tid < n) pos_of[tid] = -1;
+    __syncthreads();
+    if (tid < a.E && rank_of[tid] >= 0) {
+      const int u = rank_of[tid];
+      int pos = u == 0 ? 0 : scan[src][u - 1];
+      for (int j = 0; j < n; ++j) {
+        if (eidx[j] == tid) {
+          a.perm[pos] = j;
+          pos_of[j] = pos++;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < n) a.invperm[tid] = pos_of[tid];
   }
 }
 
@@ -200,6 +230,42 @@ __device__ __forceinline__ void params_f16(uint32_t p, h2_t& s, h2_t& s16, h2_t&
 
 
 // ---------------------------------------------------------------------------
+// SwiGLU epilogue of a gate/up tile: up to 16 entries x the 64 features of
+// workgroup column blockIdx.x.  The lane computes h = silu(g) * u for its
+// feature (stored at column hcol of H) and its rows 4 (lane / 16) + i.  Each
+// row of the tile is scaled by one power of two (f16_block_shift of the row's
+// largest |h| over the tile) before it is rounded to fp16, and the inverse
+// scale goes to Hs[row][tile]: H stays fp16 without overflow, and the down
+// GEMM multiplies each tile's contribution back (a tile is one chunk of 64 of
+// the down projection's reduction).  red: [4][16] floats of LDS.  Every thread
+// of the workgroup calls it (it holds a barrier).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_h_tile(const PrefillArgs& a, const float4_t& ag, const float4_t& au, int o,
+                                             int n_rows, int hcol, float (*red)[16]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = silu_f32(ag[i]) * au[i];
+    const float m = row_max16(fabsf(h[i]));  // over the wave's 16 features
+    if ((lane & 15) == 0) red[wave][4 * (lane >> 4) + i] = m;
+  }
+  __syncthreads();
+  const int tiles = a.f / 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    const float mx = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
+    const int sh = f16_block_shift(mx);
+    if (row < n_rows) {
+      a.H[(size_t)(o + row) * a.f + hcol] = (_Float16)(h[i] * __builtin_ldexpf(1.0f, sh));
+      if (wave == 0 && (lane & 15) == 0)
+        a.Hs[(size_t)(o + row) * tiles + blockIdx.x] = __builtin_ldexpf(1.0f, -sh);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 2-3. Grouped GEMMs over slices: a slice is up to 16 consecutive entries of
 // one union expert (one MFMA M tile).  grid = (N / 64, max slices), 256
 // threads; workgroup (nt, s) computes features [64 nt, 64 nt + 64) of slice s,
@@ -226,22 +292,40 @@ struct KBlock {
 // r; load() and store() are separate so the loads run a block ahead.  From
 // bf16, the values are stored in the pair order of groups of 8; fp16 rows (H)
 // are copied as they are (in the pair order of their code width).
+// For H rows (FROM_BF16 false) the stage also brings the rows' tile scales:
+// the values of a K block are put on one common scale per row (the block's
+// largest tile scale F, a power of two; a tile's values are multiplied by its
+// scale / F <= 1, exactly unless they fall below the fp16 normal range), and
+// F goes to fblk[row] for the caller to multiply the block's result by.  A
+// thread's KT / 16 values lie in one tile, and the 16 threads of a row are
+// one row of lanes, so F is a 16-lane maximum.
 template <bool FROM_BF16, int KT>
 struct RowStage {
   static constexpr int V = KT / 16 / 8;  // uint4 (8 values) per thread
   uint4 v[V];
+  float fs;                              // tile scale of this thread's values (H rows)
 
-  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
+  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb,
+                                       const float* hs = nullptr, int tiles = 0) {
     const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * (KT / 16);
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       v[j] = make_uint4(0, 0, 0, 0);
       if (r < n_rows) v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + c + 8 * j);
     }
+    fs = 1.0f;
+    if (!FROM_BF16 && r < n_rows) fs = hs[(size_t)rows[r] * tiles + (kb + c) / 64];
   }
 
-  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8]) const {
+  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float* fblk = nullptr) const {
     const int tid = threadIdx.x, r = tid >> 4, c = (tid & 15) * (KT / 16);
+    h2_t ratio = {(_Float16)1.0f, (_Float16)1.0f};
+    if (!FROM_BF16) {
+      const float fb = row_max16(fs);
+      const _Float16 rh = (_Float16)(fs / fb);  // a power of two <= 1 (0 below fp16's range)
+      ratio = h2_t{rh, rh};
+      if ((tid & 15) == 0) fblk[r] = fb;
+    }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       uint4 o;
@@ -257,8 +341,11 @@ struct RowStage {
         o.y = f16_bits(f[1]) | (f16_bits(f[5]) << 16);
         o.z = f16_bits(f[2]) | (f16_bits(f[6]) << 16);
         o.w = f16_bits(f[3]) | (f16_bits(f[7]) << 16);
-      } else {
-        o = v[j];  // already fp16 in pair order
+      } else {  // already fp16 in pair order: onto the block's common scale
+        o.x = __builtin_bit_cast(uint32_t, as_h2(v[j].x) * ratio);
+        o.y = __builtin_bit_cast(uint32_t, as_h2(v[j].y) * ratio);
+        o.z = __builtin_bit_cast(uint32_t, as_h2(v[j].z) * ratio);
+        o.w = __builtin_bit_cast(uint32_t, as_h2(v[j].w) * ratio);
       }
       *reinterpret_cast<uint4*>(&xs[r][c + 8 * j]) = o;
     }
@@ -399,6 +486,7 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
   using F = WFormat<CHUNK, KT, 4>;
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ int rows[16];
+  __shared__ float red[4][16];
   SliceInfo si;
   if (!slice_info(a, si)) return;
   const int e = a.union_ids[si.u];
@@ -436,18 +524,14 @@ __global__ __launch_bounds__(256) void prefill_gate_up_kernel(PrefillArgs a) {
     __syncthreads();
   }
   // epilogue: lane holds rows 4 (l / 16) + i of the tile, feature n0
-  const int hcol = pair_index<4>(n0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (lane >> 4) + i;
-    if (row < si.n_rows) a.H[(size_t)(si.o + row) * a.f + hcol] = (_Float16)(silu_f32(ag[i]) * au[i]);
-  }
+  store_h_tile(a, ag, au, si.o, si.n_rows, pair_index<4>(n0), red);
 }
 
 template <int CHUNK, int KT, int BITS = 4>
 __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
   using F = WFormat<CHUNK, KT, BITS>;
   __shared__ _Float16 xs[2][16][KT + 8];
+  __shared__ __attribute__((aligned(16))) float fblk[2][16];  // the H rows' scale per K block
   __shared__ int rows[16];
   SliceInfo si;
   if (!slice_info(a, si)) return;
@@ -461,21 +545,28 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(PrefillArgs a) {
   const size_t row_bytes = (size_t)a.f * BITS / 8, prow = (size_t)(a.f / CHUNK) * 4;
   const uint8_t* dc = blob + a.lay.down_codes + (size_t)n0 * row_bytes;
   const uint8_t* dp = blob + a.lay.down_params + (size_t)n0 * prow;
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  const int nk = a.f / KT;
+  const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+  float4_t acc = zero;
+  const int nk = a.f / KT, tiles = a.f / 64;
   RowStage<false, KT> hr;
   typename F::Block w0, w1;
-  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
+  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0, a.Hs, tiles);
   w0.load(dc, dp, 0, lane);
-  hr.store(xs[0]);
+  hr.store(xs[0], fblk[0]);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
-      hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT);
+      hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT, a.Hs, tiles);
       w1.load(dc, dp, (i + 1) * KT, lane);
     }
-    F::mma(acc, w0, xs[i & 1], lane);
-    if (i + 1 < nk) hr.store(xs[(i + 1) & 1]);
+    float4_t P = zero;  // this block on the rows' common scale, then scaled back
+    F::mma(P, w0, xs[i & 1], lane);
+    const float4 fb = *reinterpret_cast<const float4*>(&fblk[i & 1][4 * (lane >> 4)]);
+    acc[0] = fmaf(fb.x, P[0], acc[0]);
+    acc[1] = fmaf(fb.y, P[1], acc[1]);
+    acc[2] = fmaf(fb.z, P[2], acc[2]);
+    acc[3] = fmaf(fb.w, P[3], acc[3]);
+    if (i + 1 < nk) hr.store(xs[(i + 1) & 1], fblk[(i + 1) & 1]);
     w0 = w1;
     __syncthreads();
   }
@@ -537,20 +628,26 @@ template <bool FROM_BF16, int KT>
 struct FoldStage {
   static constexpr int V = KT / 128;  // 16-byte pieces (8 values) per thread
   uint4 v[V];
+  float fs[V];                        // H rows: the tile scale of each piece's chunk
 
   // thread (r, k) takes pieces 16 j + k of row r: the 16 threads of a row
-  // read 256 contiguous bytes per load instruction
-  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
+  // read 256 contiguous bytes per load instruction.  For H rows the first
+  // thread of each chunk also loads the chunk's tile scale (hs, tiles).
+  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb,
+                                       const float* hs = nullptr, int tiles = 0) {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       v[j] = make_uint4(0, 0, 0, 0);
       if (r < n_rows)
         v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + 8 * (16 * j + k));
+      fs[j] = 1.0f;
+      if (!FROM_BF16 && r < n_rows && (k & 7) == 0) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 2 * j + (k >> 3)];
     }
   }
 
-  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16]) const {
+  // fsc (H rows only): [chunk of the block][row] tile scales
+  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16], float (*fsc)[16] = nullptr) const {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
     const uint32_t k16 = 0x2C002C00u;  // (1/16, 1/16) in fp16
 #pragma unroll
@@ -586,7 +683,10 @@ struct FoldStage {
       *reinterpret_cast<uint4*>(&xs[r][8 * (16 * j + k)]) = o;
       // a chunk is 8 pieces: threads 8h .. 8h + 7 of the row (adjacent lanes)
       part = group_sum<8>(part);
-      if ((k & 7) == 0) xsum[2 * j + (k >> 3)][r] = part;
+      if ((k & 7) == 0) {
+        xsum[2 * j + (k >> 3)][r] = part;
+        if (!FROM_BF16) fsc[2 * j + (k >> 3)][r] = fs[j];
+      }
     }
   }
 };
@@ -638,9 +738,11 @@ __device__ __forceinline__ void relayout256(W& w, uint8_t* stage, int lane) {
 // column (feature) and its four rows 4 (lane / 16) + i; chunks in order.  All
 // of the block's MFMA chains are issued before the first result is folded, so
 // the VALU epilogue of one chunk overlaps the MFMAs of the next.
-template <int KT>
+// With SCALED, the A rows are H tiles stored at a power-of-two scale and the
+// chunk's term is multiplied by its tile scale fsc[chunk][row].
+template <int KT, bool SCALED = false>
 __device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _Float16 (*xs)[KT + 8],
-                                            float (*xsum)[16], int lane) {
+                                            float (*xsum)[16], int lane, float (*fsc)[16] = nullptr) {
   constexpr int NC = FoldW<KT>::NPW;
   const int g = lane >> 4, ml = lane & 15, r4 = 4 * (lane >> 4);
   const float4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -665,10 +767,18 @@ __device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _
     const float S = __uint_as_float(prm << 16) * 16777216.0f;  // scale * 2^24
     const float M = __uint_as_float(prm & 0xFFFF0000u);
     const float4 X = *reinterpret_cast<const float4*>(&xsum[cl][r4]);
-    acc[0] = fmaf(S, P[cl][0], fmaf(M, X.x, acc[0]));
-    acc[1] = fmaf(S, P[cl][1], fmaf(M, X.y, acc[1]));
-    acc[2] = fmaf(S, P[cl][2], fmaf(M, X.z, acc[2]));
-    acc[3] = fmaf(S, P[cl][3], fmaf(M, X.w, acc[3]));
+    if constexpr (SCALED) {
+      const float4 Fs = *reinterpret_cast<const float4*>(&fsc[cl][r4]);
+      acc[0] = fmaf(Fs.x, fmaf(S, P[cl][0], M * X.x), acc[0]);
+      acc[1] = fmaf(Fs.y, fmaf(S, P[cl][1], M * X.y), acc[1]);
+      acc[2] = fmaf(Fs.z, fmaf(S, P[cl][2], M * X.z), acc[2]);
+      acc[3] = fmaf(Fs.w, fmaf(S, P[cl][3], M * X.w), acc[3]);
+    } else {
+      acc[0] = fmaf(S, P[cl][0], fmaf(M, X.x, acc[0]));
+      acc[1] = fmaf(S, P[cl][1], fmaf(M, X.y, acc[1]));
+      acc[2] = fmaf(S, P[cl][2], fmaf(M, X.z, acc[2]));
+      acc[3] = fmaf(S, P[cl][3], fmaf(M, X.w, acc[3]));
+    }
   }
 }
 
@@ -677,6 +787,7 @@ __global__ __launch_bounds__(256) void prefill_gate_up_fold_kernel(PrefillArgs a
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
+  __shared__ float red[4][16];
   __shared__ __attribute__((aligned(16))) uint8_t wst[4][2][16 * kLineStageRow];
   // the slice's record (written by the union kernel) and the slice count are
   // independent loads: one round trip before the weights stream
@@ -727,18 +838,14 @@ __global__ __launch_bounds__(256) void prefill_gate_up_fold_kernel(PrefillArgs a
     u0 = u1;
     __syncthreads();
   }
-  const int hcol = (n0 & ~7) + pair_slot(n0 & 7);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (lane >> 4) + i;
-    if (row < si.n_rows) a.H[(size_t)(si.o + row) * a.f + hcol] = (_Float16)(silu_f32(ag[i]) * au[i]);
-  }
+  store_h_tile(a, ag, au, si.o, si.n_rows, pair_index<4>(n0), red);
 }
 
 template <int KT>
 __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
+  __shared__ __attribute__((aligned(16))) float fsc[2][KT / 64][16];  // H tile scales
   __shared__ int rows[16];
   __shared__ __attribute__((aligned(16))) uint8_t wst[4][KT == 256 ? 16 * kLineStageRow : 16];
   const int n_slices = *a.n_slices;
@@ -767,21 +874,22 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   auto wlay = [&](FoldW<KT>& w) {
     if constexpr (KT == 256) relayout256(w, dst, lane);
   };
+  const int tiles = a.f / 64;
   wload(w0, 0);
   if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
   __syncthreads();
-  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0);
-  hr.store(xs[0], xsum[0]);
+  hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0, a.Hs, tiles);
+  hr.store(xs[0], xsum[0], fsc[0]);
   wlay(w0);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
-      hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT);
+      hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT, a.Hs, tiles);
       wload(w1, (i + 1) * KT);
     }
-    fold_kblock<KT>(acc, w0, xs[i & 1], xsum[i & 1], lane);
+    fold_kblock<KT, true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fsc[i & 1]);
     if (i + 1 < nk) {
-      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fsc[(i + 1) & 1]);
       wlay(w1);
     }
     w0 = w1;
@@ -823,8 +931,10 @@ __device__ __forceinline__ half8_t codes8_q2(uint32_t w) {
 template <bool FROM_BF16>
 struct FoldStageQ2 {
   uint4 v[4];
+  float fs[2];  // H rows: the tile scale of each group pair's chunk
 
-  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb) {
+  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb,
+                                       const float* hs = nullptr, int tiles = 0) {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -833,9 +943,14 @@ struct FoldStageQ2 {
         v[i] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb +
                        16 * (16 * (i >> 1) + k) + 8 * (i & 1));
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      fs[j] = 1.0f;
+      if (!FROM_BF16 && r < n_rows && (k & 3) == 0) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 4 * j + (k >> 2)];
+    }
   }
 
-  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16]) const {
+  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16], float (*fsc)[16] = nullptr) const {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
     const uint32_t k4 = 0x34003400u;  // (1/4, 1/4) in fp16
 #pragma unroll
@@ -879,7 +994,10 @@ struct FoldStageQ2 {
       *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k)]) = o0;
       *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k) + 8]) = o1;
       part = group_sum<4>(part);
-      if ((k & 3) == 0) xsum[4 * j + (k >> 2)][r] = part;
+      if ((k & 3) == 0) {
+        xsum[4 * j + (k >> 2)][r] = part;
+        if (!FROM_BF16) fsc[4 * j + (k >> 2)][r] = fs[j];
+      }
     }
   }
 };
@@ -905,8 +1023,9 @@ __device__ __forceinline__ void load_lines_q2(FoldWQ2& w, const uint8_t* codes_r
 // acc += sum over the block's eight chunks of s_c P_c + m_c X_c, four chunks
 // (one transposed piece row) at a time: their MFMA chains first, then the
 // folds.
+template <bool SCALED = false>
 __device__ __forceinline__ void fold_kblock_q2(float4_t& acc, const FoldWQ2& w, _Float16 (*xs)[512 + 8],
-                                               float (*xsum)[16], int lane) {
+                                               float (*xsum)[16], int lane, float (*fsc)[16] = nullptr) {
   const int g = lane >> 4, ml = lane & 15, r4 = 4 * (lane >> 4);
   const float4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -928,10 +1047,18 @@ __device__ __forceinline__ void fold_kblock_q2(float4_t& acc, const FoldWQ2& w, 
       const float S = __uint_as_float(pw[j] << 16) * 16777216.0f;  // scale * 2^24
       const float M = __uint_as_float(pw[j] & 0xFFFF0000u);
       const float4 X = *reinterpret_cast<const float4*>(&xsum[4 * q + j][r4]);
-      acc[0] = fmaf(S, P[j][0], fmaf(M, X.x, acc[0]));
-      acc[1] = fmaf(S, P[j][1], fmaf(M, X.y, acc[1]));
-      acc[2] = fmaf(S, P[j][2], fmaf(M, X.z, acc[2]));
-      acc[3] = fmaf(S, P[j][3], fmaf(M, X.w, acc[3]));
+      if constexpr (SCALED) {
+        const float4 Fs = *reinterpret_cast<const float4*>(&fsc[4 * q + j][r4]);
+        acc[0] = fmaf(Fs.x, fmaf(S, P[j][0], M * X.x), acc[0]);
+        acc[1] = fmaf(Fs.y, fmaf(S, P[j][1], M * X.y), acc[1]);
+        acc[2] = fmaf(Fs.z, fmaf(S, P[j][2], M * X.z), acc[2]);
+        acc[3] = fmaf(Fs.w, fmaf(S, P[j][3], M * X.w), acc[3]);
+      } else {
+        acc[0] = fmaf(S, P[j][0], fmaf(M, X.x, acc[0]));
+        acc[1] = fmaf(S, P[j][1], fmaf(M, X.y, acc[1]));
+        acc[2] = fmaf(S, P[j][2], fmaf(M, X.z, acc[2]));
+        acc[3] = fmaf(S, P[j][3], fmaf(M, X.w, acc[3]));
+      }
     }
   }
 }
@@ -941,6 +1068,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_fold_q2_kernel(Prefill
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
+  __shared__ float red[4][16];
   __shared__ __attribute__((aligned(16))) uint8_t wst[4][2][16 * kLineStageRow];
   const int n_slices = *a.n_slices;
   const PrefillArgs::SliceRec rec = a.recs[blockIdx.y];
@@ -987,18 +1115,14 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_fold_q2_kernel(Prefill
     u0 = u1;
     __syncthreads();
   }
-  const int hcol = pair_index<2>(n0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (lane >> 4) + i;
-    if (row < n_rows) a.H[(size_t)(o + row) * a.f + hcol] = (_Float16)(silu_f32(ag[i]) * au[i]);
-  }
+  store_h_tile(a, ag, au, o, n_rows, pair_index<2>(n0), red);
 }
 
 __global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a) {
   constexpr int KT = 512;
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
+  __shared__ __attribute__((aligned(16))) float fsc[2][KT / 64][16];  // H tile scales
   __shared__ int rows[16];
   __shared__ __attribute__((aligned(16))) uint8_t wst[4][16 * kLineStageRow];
   const int n_slices = *a.n_slices;
@@ -1016,21 +1140,22 @@ __global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a
   const int nk = a.f / KT;
   FoldStageQ2<false> hr;
   FoldWQ2 w0, w1;
+  const int tiles = a.f / 64;
   load_lines_q2(w0, dc0, row_bytes, dp, 0, lane);
   if (tid < n_rows) rows[tid] = o + tid;  // H rows of this slice
   __syncthreads();
-  hr.load(a.H, (size_t)a.f, rows, n_rows, 0);
-  hr.store(xs[0], xsum[0]);
+  hr.load(a.H, (size_t)a.f, rows, n_rows, 0, a.Hs, tiles);
+  hr.store(xs[0], xsum[0], fsc[0]);
   relayout256(w0, dst, lane);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
-      hr.load(a.H, (size_t)a.f, rows, n_rows, (i + 1) * KT);
+      hr.load(a.H, (size_t)a.f, rows, n_rows, (i + 1) * KT, a.Hs, tiles);
       load_lines_q2(w1, dc0, row_bytes, dp, (i + 1) * KT, lane);
     }
-    fold_kblock_q2(acc, w0, xs[i & 1], xsum[i & 1], lane);
+    fold_kblock_q2<true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fsc[i & 1]);
     if (i + 1 < nk) {
-      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
+      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fsc[(i + 1) & 1]);
       relayout256(w1, dst, lane);
     }
     w0 = w1;

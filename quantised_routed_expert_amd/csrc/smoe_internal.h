@@ -118,6 +118,26 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Maximum over each row of 16 lanes, valid in every lane of the row.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  return v;
+}
+
+// Power-of-two scaling of a block of activations for fp16 storage: the shift
+// sh such that mx * 2^sh lies in [2^14, 2^15) for the block's largest
+// magnitude mx (so no value of the block overflows fp16, whose largest finite
+// value is 65504, and the largest keep fp16's full precision); 15 for zero,
+// infinity or NaN (v_frexp_exp gives 0 for them), and clamped so that 2^sh and
+// 2^-sh are normal floats.
+__device__ __forceinline__ int f16_block_shift(float mx) {
+  const int sh = 15 - __builtin_amdgcn_frexp_expf(mx);
+  return sh < -120 ? -120 : (sh > 120 ? 120 : sh);
+}
+
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = (uint64_t)__double_as_longlong(v);

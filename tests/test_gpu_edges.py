@@ -10,7 +10,8 @@ import oracle
 import quantised_routed_expert_amd as smoe
 import synth
 from synth.device import DeviceStack
-from tests.gpu_common import LazyExperts, check_moe_output, need_gpu, random_residual, say
+from tests.gpu_common import (LazyExperts, check_moe_output, check_prefill_against_oracle, need_gpu,
+                              random_residual, say)
 from tests.test_gpu_decode import _decode_one_layer
 from tests.test_gpu_prefill import check_union, run_prefill
 
@@ -79,11 +80,9 @@ def test_size_bound_decode_matches_oracle(name):
     assert np.array_equal(r.cpu().numpy(), r_out)
 
 
-@pytest.mark.parametrize("name,T,sample", [("d_model_8192", 20, [0, 7, 19]), ("d_ff_8192", 33, [0, 16, 32]),
-                                           ("e256_k16", 64, [0, 21, 42, 63]),
-                                           ("d_model_8192_c64", 17, [0, 9, 16]),
-                                           ("e256_k16_c64", 64, [0, 30, 63])])
-def test_size_bound_prefill_matches_oracle(name, T, sample):
+@pytest.mark.parametrize("name,T", [("d_model_8192", 20), ("d_ff_8192", 33), ("e256_k16", 64),
+                                    ("d_model_8192_c64", 17), ("e256_k16_c64", 64)])
+def test_size_bound_prefill_matches_oracle(name, T):
     dims = BOUNDS[name]
     say(f"[bound] prefill {name}: T={T}")
     stack = DeviceStack(1337, dims, 1)
@@ -91,10 +90,4 @@ def test_size_bound_prefill_matches_oracle(name, T, sample):
     got = run_prefill(dims, stack, 0, res)
     n_union = check_union(got, T, dims.top_k)
     say(f"[bound] |union| = {n_union}")
-    experts = LazyExperts(1337, dims, 0)
-    for t in sample:
-        ref = oracle.moe_layer(res[t].astype(np.float64), stack.router_bits[0], experts, dims)
-        assert got["idx"][t].tolist() == ref["idx"], f"token {t}"
-        assert np.allclose(got["w"][t], ref["w"], rtol=2e-6, atol=1e-7)
-        y = got["r_out"][t].astype(np.float64) - res[t].astype(np.float64)
-        check_moe_output(y, ref["y"], f"{name} t{t}")
+    check_prefill_against_oracle(got, res, stack, dims, 0, f"bound {name}")

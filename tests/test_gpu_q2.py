@@ -11,9 +11,9 @@ import oracle
 import quantised_routed_expert_amd as smoe
 import synth
 from synth.device import DeviceStack, fill_experts
-from tests.gpu_common import (LazyExperts, bits_u16, check_moe_output, need_gpu, random_residual, say,
-                              topk_gap_ok)
-from tests.test_gpu_decode import _decode_one_layer
+from tests.gpu_common import (LazyExperts, check_chain_against_oracle, check_moe_output, check_prefill_against_oracle,
+                              need_gpu, random_residual, say)
+from tests.test_gpu_decode import _decode_one_layer, run_chain_and_per_layer
 from tests.test_gpu_prefill import check_union, run_prefill
 from tests.test_gpu_ring import make_ring, resident_decode, ring_decode
 
@@ -83,38 +83,17 @@ def test_q2_special_routings_and_size_bounds():
         check_moe_output(r_out.astype(np.float64) - res, ref["y"], str(dims))
 
 
-def test_q2_decode_layers_chain_matches_per_layer_calls_and_oracle():
-    dims = Q2["q30b"]
-    n_layers = 5
+@pytest.mark.parametrize("shape,n_layers,stream", [("q30b", 5, 2), ("q235b", 4, 5)])
+def test_q2_decode_layers_chain_matches_per_layer_calls_and_oracle(shape, n_layers, stream):
+    """The chained SMOE-Q2 entry point at the 30B and 235B shapes: bitwise
+    equal to per-layer calls, teacher-forced oracle parity per layer, and the
+    free-running oracle chain."""
+    dims = Q2[shape]
+    say(f"[q2-chain] {shape} {n_layers} layers")
     stack = DeviceStack(1337, dims, n_layers)
-    h0 = synth.hidden_bf16(1337, 2, dims.d_model)
-    r = torch.from_numpy(h0.copy()).cuda()
-    x_rec = torch.empty((n_layers, dims.d_model), dtype=torch.int16, device="cuda")
-    i_rec = torch.empty((n_layers, dims.top_k), dtype=torch.int32, device="cuda")
-    w_rec = torch.empty((n_layers, dims.top_k), dtype=torch.float32, device="cuda")
-    smoe.decode_layers(dims, n_layers, r, stack.router, None, stack.tables, smoe.workspace(dims, 1), x_rec,
-                       i_rec, w_rec)
-    torch.cuda.synchronize()
-    chain = r.cpu().numpy()
-    res = h0.copy()
-    for L in range(n_layers):
-        xb, ig, wg, res = _decode_one_layer(dims, stack, L, res)
-        assert np.array_equal(xb, bits_u16(x_rec)[L])
-        assert np.array_equal(ig, i_rec.cpu().numpy()[L])
-        assert np.array_equal(wg, w_rec.cpu().numpy()[L])
-    assert np.array_equal(res, chain)
-    ro = h0.astype(np.float64)
-    for L in range(n_layers):
-        ref = oracle.moe_layer(ro, stack.router_bits[L], LazyExperts(1337, dims, L), dims)
-        gi = i_rec.cpu().numpy()[L].tolist()
-        if gi != ref["idx"]:
-            assert topk_gap_ok(ref["logits"], gi, ref["idx"], dims.top_k, 1e-4), f"layer {L}"
-            say(f"[q2-chain] near-tie flip at layer {L}; stopping comparison")
-            return
-        ro = ref["r_out"]
-    rel = np.linalg.norm(chain - ro) / np.linalg.norm(ro - h0)
-    say(f"[q2-chain] final residual rel error (vs MoE delta) {rel:.2e}")
-    assert rel <= 2e-3
+    h0 = synth.hidden_bf16(1337, stream, dims.d_model)
+    chain, per_layer, ir, wr = run_chain_and_per_layer(dims, stack, h0, n_layers)
+    check_chain_against_oracle(dims, stack, h0, chain, per_layer, ir, wr, f"q2 chain {shape}")
 
 
 def test_q2_decode_is_deterministic():
@@ -191,46 +170,34 @@ def test_q2_decode_layers_selection_other_expert_counts(E, k):
 
 # d_ff 256, 384, 768 and 1536 take the down GEMM's K blocks of 256, 128, 256
 # and 512 codes (8-byte code loads at 128)
-@pytest.mark.parametrize("shape,T,zipf,sample", [
-    ("small", 1, 0.0, None), ("small", 64, 0.0, None), ("ragged", 17, 1.1, None), ("ragged", 64, 0.0, None),
-    ("q30b", 64, 1.1, [0, 31, 63]), ("q235b", 64, 1.1, [0, 13, 40, 63]), ("q235b", 9, 0.0, [0, 8]),
+@pytest.mark.parametrize("shape,T,zipf", [
+    ("small", 1, 0.0), ("small", 64, 0.0), ("ragged", 17, 1.1), ("ragged", 64, 0.0),
+    ("q30b", 64, 1.1), ("q235b", 64, 1.1), ("q235b", 9, 0.0),
 ])
-def test_q2_prefill_parity(shape, T, zipf, sample):
+def test_q2_prefill_parity(shape, T, zipf):
     dims = Q2[shape]
     say(f"[q2-prefill] {shape} T={T} zipf={zipf}")
     stack = DeviceStack(1337, dims, 1, zipf_s=zipf)
     res = random_residual(np.random.default_rng(T + 3), T, dims.d_model, scale=1.5)
     got = run_prefill(dims, stack, 0, res)
     say(f"[q2-prefill] |union| = {check_union(got, T, dims.top_k)}")
-    experts = LazyExperts(1337, dims, 0)
-    worst = 0.0
-    for t in (range(T) if sample is None else sample):
-        ref = oracle.moe_layer(res[t].astype(np.float64), stack.router_bits[0], experts, dims,
-                               bias=None if stack.bias_np is None else stack.bias_np[0])
-        assert got["idx"][t].tolist() == ref["idx"], f"token {t}"
-        y = got["r_out"][t].astype(np.float64) - res[t].astype(np.float64)
-        worst = max(worst, check_moe_output(y, ref["y"], f"q2 prefill {shape} t{t}"))
-    say(f"[q2-prefill] {shape} T={T}: worst rel-L2 {worst:.2e}")
+    check_prefill_against_oracle(got, res, stack, dims, 0, f"q2 prefill {shape} T={T}")
 
 
-@pytest.mark.parametrize("dims,T,sample", [
+@pytest.mark.parametrize("dims,T", [
     # the largest K of the folded gate/up GEMM (16 blocks of 512) and a d_ff of one down block
-    (synth.Dims(8192, 512, 32, 4, 64, bits=2), 17, [0, 9, 16]),
+    (synth.Dims(8192, 512, 32, 4, 64, bits=2), 17),
     # 256 experts, top-16: up to 256 union experts and their slices; d_ff 8192 (16 down blocks)
-    (synth.Dims(512, 256, 256, 16, 64, bits=2), 64, [0, 30, 63]),
-    (synth.Dims(512, 8192, 16, 4, 64, bits=2), 33, [0, 16, 32]),
+    (synth.Dims(512, 256, 256, 16, 64, bits=2), 64),
+    (synth.Dims(512, 8192, 16, 4, 64, bits=2), 33),
 ], ids=["d_model_8192", "e256_k16", "d_ff_8192"])
-def test_q2_prefill_size_bounds(dims, T, sample):
+def test_q2_prefill_size_bounds(dims, T):
     say(f"[q2-prefill-bound] {dims} T={T}")
     stack = DeviceStack(1337, dims, 1)
     res = random_residual(np.random.default_rng(T + 5), T, dims.d_model, scale=1.5)
     got = run_prefill(dims, stack, 0, res)
     say(f"[q2-prefill-bound] |union| = {check_union(got, T, dims.top_k)}")
-    experts = LazyExperts(1337, dims, 0)
-    for t in sample:
-        ref = oracle.moe_layer(res[t].astype(np.float64), stack.router_bits[0], experts, dims)
-        assert got["idx"][t].tolist() == ref["idx"], f"token {t}"
-        check_moe_output(got["r_out"][t].astype(np.float64) - res[t].astype(np.float64), ref["y"], f"t{t}")
+    check_prefill_against_oracle(got, res, stack, dims, 0, f"q2 bound T={T}")
 
 
 def test_q2_prefill_full_m_tiles_and_matches_decode():

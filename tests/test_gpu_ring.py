@@ -189,9 +189,10 @@ def test_ring_lru_at_full_scale_with_markov_routing():
 def prefill_layers(dims, stack, chunk, ring=None):
     """Layer-major prefill of one chunk through every layer of the stack, each
     layer fed the chunk's own residual (as the prefill workload does).  With a
-    ring, each layer's expert union is acquired in first-touch order and the
-    GEMMs find the blobs through the ring's table.  Returns the per-layer
-    outputs and unions."""
+    ring, the library forms each layer's expert union from the routing and
+    acquires it in first-touch order (smoe_ring_acquire_routed), and the GEMMs
+    find the blobs through the ring's table; the oracle's union only checks
+    it.  Returns the per-layer outputs and unions."""
     T = chunk.shape[0]
     E, k = dims.n_experts, dims.top_k
     ws = smoe.workspace(dims, T)
@@ -208,13 +209,14 @@ def prefill_layers(dims, stack, chunk, ring=None):
     for L in range(stack.n_layers):
         r = torch.from_numpy(chunk.copy()).cuda()
         smoe.route(dims, r, x, stack.router_layer(L), stack.bias_layer(L), idx, w, ws)
-        union = oracle.expert_union(idx.cpu().numpy().tolist())[0]   # synchronises with the router
-        unions.append(union)
         if ring is None:
             tab = stack.table(L)
+            union = oracle.expert_union(idx.cpu().numpy().tolist())[0]   # synchronises with the router
         else:
-            ring.acquire_table(L, union, table)
+            union = ring.acquire_routed(L, idx, table)
+            assert union == oracle.expert_union(idx.cpu().numpy().tolist())[0]
             tab = table
+        unions.append(union)
         smoe.moe_prefill_chunk(dims, x, idx, w, tab, r, uids, ucount, offs, perm, ws)
         torch.cuda.synchronize()
         assert uids.cpu().numpy()[: int(ucount.item())].tolist() == union
@@ -252,6 +254,26 @@ def test_ring_backed_prefill_matches_resident_and_oracle_log(bits, n_slots):
     assert stats["h2d_bytes"] == ref.misses * stack.blob_bytes
     say(f"[ring-prefill] slots={n_slots}: unions {[len(u) for u in unions]}, hits {ref.hits} misses {ref.misses} "
         f"evictions {ref.evictions}")
+
+
+def test_ring_acquire_routed_rejects_bad_arguments():
+    dims = synth.Dims(256, 128, 128, 8, 32)
+    stack = DeviceStack(1337, dims, 1)
+    ring, keep = make_ring(dims, stack, 64)
+    table = torch.empty(dims.n_experts, dtype=torch.int64, device="cuda")
+    idx = torch.arange(65 * 8, dtype=torch.int32, device="cuda").reshape(65, 8) % dims.n_experts
+    with pytest.raises(smoe.SmoeError):
+        ring.acquire_routed(0, idx, table)                       # 65 tokens
+    with pytest.raises(smoe.SmoeError):
+        ring.acquire_routed(0, idx[:16], table)                  # a union of 128 experts > 64 slots
+    with pytest.raises(smoe.SmoeError):
+        ring.acquire_routed(1, idx[:2], table)                   # layer out of range
+    bad = torch.full((2, 8), dims.n_experts, dtype=torch.int32, device="cuda")
+    with pytest.raises(smoe.SmoeError):
+        ring.acquire_routed(0, bad, table)                       # no valid expert
+    assert ring.acquire_routed(0, idx[:2], table) == list(range(16))
+    ring.release()
+    ring.destroy()
 
 
 def test_ring_acquire_table_rejects_oversized_unions():
