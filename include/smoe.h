@@ -196,6 +196,22 @@ int smoe_decode_layers(const smoe_dims* dims, int32_t n_layers, float* residual,
                        float* w_rec, void* const* events, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* smoe_decode_layers without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the scratch lives in a 2 MiB array that
+ * the library holds in each GPU's memory until the process ends (every valid
+ * smoe_dims needs at most about 1.5 MiB of it; larger needs are rejected with
+ * SMOE_EINVAL).  Arguments and results as smoe_decode_layers (no per-kernel
+ * events).  The call allocates nothing: the array's device address is looked
+ * up once per device, on the first call with that device current.  Every
+ * call on one GPU uses that GPU's one array, whose contents carry over from
+ * call to call (nothing in it needs to start at zero): calls that overlap on
+ * one GPU (other streams, other threads) race; serialise them. */
+int smoe_decode_layers_static(const smoe_dims* dims, int32_t n_layers, float* residual,
+                              const uint16_t* w_router, const float* bias,
+                              const void* const* expert_tables, uint16_t* x_rec, int32_t* idx_rec,
+                              float* w_rec, void* stream);
+
 /* Layer-major prefill of one chunk through one layer ("Prefill Reads Each
  * Expert Once, Not Once Per Token").  Inputs x/topk_idx/topk_w come from
  * smoe_route over the chunk's n_tok tokens (1..64).

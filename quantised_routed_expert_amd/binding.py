@@ -23,6 +23,7 @@ EXPORTED = [
     "smoe_decode_layers", "smoe_moe_prefill_chunk", "smoe_ring_create", "smoe_ring_acquire",
     "smoe_ring_release", "smoe_ring_stats", "smoe_ring_log", "smoe_ring_destroy", "smoe_ring_acquire_table",
     "smoe_ring_prefetch", "smoe_ring_hottest", "smoe_route_ext", "smoe_ring_acquire_routed",
+    "smoe_decode_layers_static",
 ]
 
 
@@ -78,6 +79,7 @@ def lib():
             "smoe_moe_decode": (I, [D, VP, VP, VP, VP, VP, VP, S, VP]),
             "smoe_moe_decode_slots": (I, [D, VP, VP, P(VP), VP, VP, S, VP]),
             "smoe_decode_layers": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, P(VP), VP, S, VP]),
+            "smoe_decode_layers_static": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, VP]),
             "smoe_moe_prefill_chunk": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]),
             "smoe_ring_create": (I, [P(SmoeRingDesc), P(VP)]),
             "smoe_ring_acquire": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, P(VP), VP]),
@@ -183,6 +185,14 @@ def decode_layers(dims, n_layers, residual, w_router, bias, expert_tables, ws, x
     _check(lib().smoe_decode_layers(ctypes.byref(dims_struct(dims)), int(n_layers), _ptr(residual),
                                     _ptr(w_router), _ptr(bias), _ptr(expert_tables), _ptr(x_rec),
                                     _ptr(idx_rec), _ptr(w_rec), ev, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_layers_static(dims, n_layers, residual, w_router, bias, expert_tables, x_rec=None, idx_rec=None,
+                         w_rec=None, stream=None):
+    """decode_layers on the library's own per-GPU scratch (no workspace)."""
+    _check(lib().smoe_decode_layers_static(ctypes.byref(dims_struct(dims)), int(n_layers), _ptr(residual),
+                                           _ptr(w_router), _ptr(bias), _ptr(expert_tables), _ptr(x_rec),
+                                           _ptr(idx_rec), _ptr(w_rec), _stream(stream)))
 
 
 def moe_prefill_chunk(dims, x, topk_idx, topk_w, expert_table, residual, union_ids, union_count, offsets,

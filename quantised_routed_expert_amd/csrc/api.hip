@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "prefill.h"
 
@@ -102,6 +104,89 @@ static DecodeArgs decode_args(const smoe_dims* d, char* ws, const Workspace& L) 
   a.lay = blob_layout(d->d_model, d->d_ff, d->chunk, a.bits);
   a.h = reinterpret_cast<float*>(ws + L.h);
   return a;
+}
+
+// The chained decode of smoe_decode_layers on a carved workspace.
+static int decode_layers_on(const smoe_dims* d, int32_t n_layers, float* residual, const uint16_t* w_router,
+                            const float* bias, const void* const* expert_tables, uint16_t* x_rec, int32_t* idx_rec,
+                            float* w_rec, void* const* events, char* base, const Workspace& L, hipStream_t s) {
+  double* logits = reinterpret_cast<double*>(base + L.logits);
+  uint16_t* xbuf = reinterpret_cast<uint16_t*>(base + L.x);
+  const size_t D = d->d_model, E = d->n_experts, K = d->top_k;
+  for (int layer = 0; layer < n_layers; ++layer) {
+    uint16_t* xl = x_rec ? x_rec + (size_t)layer * D : xbuf;
+    _Float16* px = reinterpret_cast<_Float16*>(base + L.px);
+    const RouteArgs ra{residual, xl, px, w_router + (size_t)layer * E * D, bias ? bias + (size_t)layer * E : nullptr,
+                       logits, 1, d->d_model, d->n_experts, d->rms_eps, nullptr, quant_bits(d) == 2 ? 1 : 0};
+    int groups = 0;  // one token: the logits are written directly
+    hipError_t he = launch_route_logits(ra, s, &groups);
+    if (he != hipSuccess) return hip_fail(he, "route_logits launch");
+    // the top-k selection runs inside the gate/up kernel, which publishes ids,
+    // weights and blob pointers for the down kernel
+    DecodeArgs a = decode_args(d, base, L);
+    a.x = xl;
+    a.px = px;
+    a.src.table = expert_tables + (size_t)layer * E;
+    a.sel.logits = logits;
+    a.sel.idx_out = reinterpret_cast<int32_t*>(base + L.idx);
+    a.sel.w_out = reinterpret_cast<float*>(base + L.w);
+    a.sel.ptr_out = reinterpret_cast<const void**>(base + L.ptr);
+    a.sel.idx_rec = idx_rec ? idx_rec + (size_t)layer * K : nullptr;
+    a.sel.w_rec = w_rec ? w_rec + (size_t)layer * K : nullptr;
+    a.ptrs = a.sel.ptr_out;
+    a.w = a.sel.w_out;
+    a.residual = residual;
+    if (layer + 1 < n_layers) a.pf_base = reinterpret_cast<const uint8_t*>(w_router + (size_t)(layer + 1) * E * D);
+    he = events ? launch_decode_gate_up(a, s, (hipEvent_t)events[2 * layer], (hipEvent_t)events[2 * layer + 1])
+                : launch_decode_gate_up(a, s);
+    if (he != hipSuccess) return hip_fail(he, "decode gate/up launch");
+    he = launch_decode_down(a, s);
+    if (he != hipSuccess) return hip_fail(he, "decode down launch");
+  }
+  return SMOE_OK;
+}
+
+static int check_decode_layers_args(const smoe_dims* d, int32_t n_layers, const float* residual,
+                                    const uint16_t* w_router, const void* const* expert_tables,
+                                    const uint16_t* x_rec) {
+  if (!residual || !w_router || !expert_tables) return fail(SMOE_EINVAL, "NULL tensor argument");
+  if (!aligned16(residual) || !aligned16(w_router) || (x_rec && !aligned16(x_rec)))
+    return fail(SMOE_EINVAL, "residual, w_router and x_rec must be 16-byte aligned");
+  (void)d;
+  (void)n_layers;
+  return SMOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch for smoe_decode_layers_static (callers that cannot
+// allocate).  Each GPU the library runs on holds its own copy of this array
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)2 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_dev[kMaxDevices];
+
+// The current device's address of `scratch`: looked up on the first call on
+// that device (with it current), then read from g_scratch_dev.  Concurrent
+// first calls may both look it up; they store the same address.
+static int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SMOE_EINVAL, "device %d beyond the %d the library tracks", dev,
+                                                 kMaxDevices);
+  void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (he != hipSuccess || !p) return hip_fail(he, "hipGetSymbolAddress(scratch)");
+    g_scratch_dev[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SMOE_OK;
 }
 
 }  // namespace smoe
@@ -245,47 +330,29 @@ int smoe_decode_layers(const smoe_dims* d, int32_t n_layers, float* residual, co
   if (int e = check_dims(d)) return e;
   if (n_layers < 0) return fail(SMOE_EINVAL, "n_layers=%d < 0", n_layers);
   if (n_layers == 0) return SMOE_OK;  // nothing to run; the buffers may be NULL
-  if (!residual || !w_router || !expert_tables) return fail(SMOE_EINVAL, "NULL tensor argument");
-  if (!aligned16(residual) || !aligned16(w_router) || (x_rec && !aligned16(x_rec)))
-    return fail(SMOE_EINVAL, "residual, w_router and x_rec must be 16-byte aligned");
+  if (int e = check_decode_layers_args(d, n_layers, residual, w_router, expert_tables, x_rec)) return e;
   Workspace L;
   if (int e = check_ws(d, 1, ws, ws_bytes, &L)) return e;
-  hipStream_t s = (hipStream_t)stream;
-  char* base = (char*)ws;
-  double* logits = reinterpret_cast<double*>(base + L.logits);
-  uint16_t* xbuf = reinterpret_cast<uint16_t*>(base + L.x);
-  const size_t D = d->d_model, E = d->n_experts, K = d->top_k;
-  for (int layer = 0; layer < n_layers; ++layer) {
-    uint16_t* xl = x_rec ? x_rec + (size_t)layer * D : xbuf;
-    _Float16* px = reinterpret_cast<_Float16*>(base + L.px);
-    const RouteArgs ra{residual, xl, px, w_router + (size_t)layer * E * D, bias ? bias + (size_t)layer * E : nullptr,
-                       logits, 1, d->d_model, d->n_experts, d->rms_eps, nullptr, quant_bits(d) == 2 ? 1 : 0};
-    int groups = 0;  // one token: the logits are written directly
-    hipError_t he = launch_route_logits(ra, s, &groups);
-    if (he != hipSuccess) return hip_fail(he, "route_logits launch");
-    // the top-k selection runs inside the gate/up kernel, which publishes ids,
-    // weights and blob pointers for the down kernel
-    DecodeArgs a = decode_args(d, base, L);
-    a.x = xl;
-    a.px = px;
-    a.src.table = expert_tables + (size_t)layer * E;
-    a.sel.logits = logits;
-    a.sel.idx_out = reinterpret_cast<int32_t*>(base + L.idx);
-    a.sel.w_out = reinterpret_cast<float*>(base + L.w);
-    a.sel.ptr_out = reinterpret_cast<const void**>(base + L.ptr);
-    a.sel.idx_rec = idx_rec ? idx_rec + (size_t)layer * K : nullptr;
-    a.sel.w_rec = w_rec ? w_rec + (size_t)layer * K : nullptr;
-    a.ptrs = a.sel.ptr_out;
-    a.w = a.sel.w_out;
-    a.residual = residual;
-    if (layer + 1 < n_layers) a.pf_base = reinterpret_cast<const uint8_t*>(w_router + (size_t)(layer + 1) * E * D);
-    he = events ? launch_decode_gate_up(a, s, (hipEvent_t)events[2 * layer], (hipEvent_t)events[2 * layer + 1])
-                : launch_decode_gate_up(a, s);
-    if (he != hipSuccess) return hip_fail(he, "decode gate/up launch");
-    he = launch_decode_down(a, s);
-    if (he != hipSuccess) return hip_fail(he, "decode down launch");
-  }
-  return SMOE_OK;
+  return decode_layers_on(d, n_layers, residual, w_router, bias, expert_tables, x_rec, idx_rec, w_rec, events,
+                          (char*)ws, L, (hipStream_t)stream);
+}
+
+int smoe_decode_layers_static(const smoe_dims* d, int32_t n_layers, float* residual, const uint16_t* w_router,
+                              const float* bias, const void* const* expert_tables, uint16_t* x_rec,
+                              int32_t* idx_rec, float* w_rec, void* stream) {
+  g_err[0] = 0;
+  if (int e = check_dims(d)) return e;
+  if (n_layers < 0) return fail(SMOE_EINVAL, "n_layers=%d < 0", n_layers);
+  if (n_layers == 0) return SMOE_OK;  // nothing to run; the buffers may be NULL
+  if (int e = check_decode_layers_args(d, n_layers, residual, w_router, expert_tables, x_rec)) return e;
+  const Workspace L = ws_layout(d, 1);
+  if (L.end > kStaticScratchBytes)
+    return fail(SMOE_EINVAL, "these dims need %zu bytes of scratch; the library's static scratch holds %zu",
+                L.end, kStaticScratchBytes);
+  void* base = nullptr;
+  if (int e = static_scratch(&base)) return e;
+  return decode_layers_on(d, n_layers, residual, w_router, bias, expert_tables, x_rec, idx_rec, w_rec, nullptr,
+                          (char*)base, L, (hipStream_t)stream);
 }
 
 int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x, const int32_t* topk_idx,
