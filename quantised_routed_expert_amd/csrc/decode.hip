@@ -305,6 +305,17 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;
   constexpr int ROWS = NPASS * P;
+  // With a row over LR < 64 lanes, the P row groups of a wave need the same
+  // activation segments: the wave converts each segment once (lane l takes
+  // segments l, l + 64, ...) into its own LDS stage, with the segment's sum
+  // and inverse scale, and every lane reads back the ones it needs.  The
+  // stage is private to the wave, so no workgroup barrier is involved.
+  constexpr int NQ4 = Run::SEGV / 4;   // 16-byte pieces of a segment's fp32 activations
+  constexpr int SSEG = NSEG * LR;      // segments of a row (those with s % LR < LA are used)
+  constexpr bool STAGE = P > 1 && SSEG * Run::NDW * 4 <= 8192;
+  constexpr int PER = (SSEG + kWave - 1) / kWave;  // segments each lane converts
+  __shared__ uint4 hst[STAGE ? 8 : 1][STAGE ? SSEG : 1][Run::NDW / 4];
+  __shared__ float2 hsx[STAGE ? 8 : 1][STAGE ? SSEG : 1];
   __shared__ float ylds[kMaxTopK][ROWS];
   __shared__ const void* s_ptr[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
@@ -365,9 +376,20 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     const uint8_t* par = blob + a.lay.down_params;
     // an idle lane (li >= LA) keeps zero codes, parameters and inputs, so its
     // contribution is exactly 0
-    constexpr int NQ4 = Run::SEGV / 4;  // 16-byte pieces of a segment's fp32 activations
-    uint4 hraw[NSEG][NQ4];
-    if (act) {
+    constexpr int NRAW = STAGE ? PER : NSEG;
+    uint4 hraw[NRAW][NQ4];
+    bool conv[NRAW];  // (staging) this lane converts its m-th segment
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const int j = lane + kWave * m;
+        conv[m] = j < SSEG && (j % LR) < LA;
+#pragma unroll
+        for (int q = 0; q < NQ4; ++q)
+          hraw[m][q] = conv[m] ? gload16(a.h + (size_t)r * a.f + (size_t)j * Run::SEGV + 4 * q)
+                               : make_uint4(0, 0, 0, 0);
+      }
+    } else if (act) {
       load_raw<LR, NSEG, NQ4>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
     } else {
 #pragma unroll
@@ -397,7 +419,51 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     // and the segments' inverse scales
     uint32_t hp[NSEG][Run::NDW];
     float xseg[NSEG], fac[NSEG];
-    pack_scaled_run<NSEG, NQ4, BITS>(hraw, hp, xseg, fac);
+    if constexpr (STAGE) {
+      uint32_t cp[PER][Run::NDW];
+      float cx[PER], cf[PER];
+      pack_scaled_run<PER, NQ4, BITS>(hraw, cp, cx, cf);
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        if (conv[m]) {
+          const int j = lane + kWave * m;
+#pragma unroll
+          for (int q = 0; q < Run::NDW / 4; ++q)
+            hst[wave][j][q] = make_uint4(cp[m][4 * q], cp[m][4 * q + 1], cp[m][4 * q + 2], cp[m][4 * q + 3]);
+          hsx[wave][j] = make_float2(cx[m], cf[m]);
+        }
+      }
+      // the stage is read by other lanes of this wave: LDS operations of a
+      // wave complete in order; keep the compiler from reordering them
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s) {
+        const int j = s * LR + li;
+        if (act) {
+#pragma unroll
+          for (int q = 0; q < Run::NDW / 4; ++q) {
+            const uint4 v = hst[wave][j][q];
+            hp[s][4 * q] = v.x; hp[s][4 * q + 1] = v.y; hp[s][4 * q + 2] = v.z; hp[s][4 * q + 3] = v.w;
+          }
+          const float2 sx = hsx[wave][j];
+          xseg[s] = sx.x;
+          fac[s] = sx.y;
+        } else {
+#pragma unroll
+          for (int q = 0; q < Run::NDW; ++q) hp[s][q] = 0u;
+          xseg[s] = 0.f;
+          fac[s] = 0.f;
+        }
+      }
+      // before the stage is written again (next rank of this wave)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      pack_scaled_run<NSEG, NQ4, BITS>(hraw, hp, xseg, fac);
+    }
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       float y = 0.f;
