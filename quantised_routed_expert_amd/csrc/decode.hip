@@ -358,7 +358,6 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   uint4 pf[kPrefetchPerThread];
 #pragma unroll
   for (int i = 0; i < kPrefetchPerThread; ++i) pf[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
 
   const int li = lane % LR, grp = lane / LR;
   const bool act = LA == LR || li < LA;
@@ -366,19 +365,15 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   const size_t row_bytes = (size_t)a.f * BITS / 8;
   const size_t prow_bytes = (size_t)(a.f / CHUNK) * 4;
 
-  for (int r = wave, it = 0; r < a.k; r += nw, ++it) {
-    const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
-    if (!blob) {
-      for (int row = lane; row < ROWS; row += kWave) ylds[r][row] = 0.f;
-      continue;
-    }
-    const uint8_t* codes = blob + a.lay.down_codes + li * 16;
-    const uint8_t* par = blob + a.lay.down_params;
-    // an idle lane (li >= LA) keeps zero codes, parameters and inputs, so its
-    // contribution is exactly 0
-    constexpr int NRAW = STAGE ? PER : NSEG;
-    uint4 hraw[NRAW][NQ4];
-    bool conv[NRAW];  // (staging) this lane converts its m-th segment
+  // h_r for this lane's columns as scaled pair-ordered f16, its segment sums
+  // and the segments' inverse scales.  An idle lane (li >= LA) keeps zero
+  // inputs (and below zero codes and parameters), so its contribution is 0.
+  uint32_t hp[NSEG][Run::NDW];
+  float xseg[NSEG], fac[NSEG];
+  constexpr int NRAW = STAGE ? PER : NSEG;
+  uint4 hraw[NRAW][NQ4];
+  bool conv[NRAW];  // (staging) this lane converts its m-th segment
+  auto load_h = [&](int r) {
     if constexpr (STAGE) {
 #pragma unroll
       for (int m = 0; m < PER; ++m) {
@@ -397,28 +392,8 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int q = 0; q < NQ4; ++q) hraw[s][q] = make_uint4(0, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);  // h first: the math can start when it lands
-    uint4 c[NPASS][NSEG];
-    uint32_t pr[NPASS][NSEG];
-#pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      const int n = n0 + p * P + grp;  // < d: the launcher checks d % ROWS == 0
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s)
-        c[p][s] = act ? gload16(codes + (size_t)n * row_bytes + s * Run::STRIDE) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int s = 0; s < NSEG; ++s)
-        pr[p][s] = act ? gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, s) * 4) : 0u;
-    }
-    if (it == 0 && a.pf_base) {
-#pragma unroll
-      for (int i = 0; i < kPrefetchPerThread; ++i) pf[i] = gload16(pf_addr[i]);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
-    // h_r for this lane's columns as scaled pair-ordered f16, its segment sums
-    // and the segments' inverse scales
-    uint32_t hp[NSEG][Run::NDW];
-    float xseg[NSEG], fac[NSEG];
+  };
+  auto convert_h = [&]() {
     if constexpr (STAGE) {
       uint32_t cp[PER][Run::NDW];
       float cx[PER], cf[PER];
@@ -464,6 +439,41 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     } else {
       pack_scaled_run<NSEG, NQ4, BITS>(hraw, hp, xseg, fac);
     }
+  };
+  // The first rank's activations do not depend on the expert pointers: their
+  // loads go out with the pointers' (the conversion waits until the weight
+  // loads are in flight).
+  if (wave < a.k) load_h(wave);
+  __syncthreads();
+
+  for (int r = wave, it = 0; r < a.k; r += nw, ++it) {
+    const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
+    if (!blob) {
+      for (int row = lane; row < ROWS; row += kWave) ylds[r][row] = 0.f;
+      continue;
+    }
+    const uint8_t* codes = blob + a.lay.down_codes + li * 16;
+    const uint8_t* par = blob + a.lay.down_params;
+    if (it > 0) load_h(r);
+    __builtin_amdgcn_sched_barrier(0);  // h first: the math can start when it lands
+    uint4 c[NPASS][NSEG];
+    uint32_t pr[NPASS][NSEG];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int n = n0 + p * P + grp;  // < d: the launcher checks d % ROWS == 0
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+        c[p][s] = act ? gload16(codes + (size_t)n * row_bytes + s * Run::STRIDE) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < NSEG; ++s)
+        pr[p][s] = act ? gload4(par + (size_t)n * prow_bytes + Run::chunk_of(li, s) * 4) : 0u;
+    }
+    if (it == 0 && a.pf_base) {
+#pragma unroll
+      for (int i = 0; i < kPrefetchPerThread; ++i) pf[i] = gload16(pf_addr[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all weight loads are in flight before any math
+    convert_h();
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       float y = 0.f;

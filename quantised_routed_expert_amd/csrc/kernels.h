@@ -248,7 +248,7 @@ struct ExpertSource {
 
 // Router rows per workgroup of the one-token logits kernel; the down kernel
 // uses it to prefetch the next layer's router rows per XCD.
-constexpr int kRouteDecRowsPerWG = 2;
+constexpr int kRouteDecRowsPerWG = 1;
 constexpr int kXcds = 8;  // MI355X: workgroup i is dispatched to XCD i % 8
 
 // Selection inside the gate/up kernel: every workgroup ranks the layer's E
