@@ -36,7 +36,7 @@ static_assert(64 * SMOE_GU_WAVES >= smoe::kMaxExperts, "a gate/up workgroup need
 #define SMOE_GU_MIN_WAVES 2048 // keep at least this many waves per gate/up launch
 #endif
 #ifndef SMOE_DN_PASSES_MAX
-#define SMOE_DN_PASSES_MAX 4   // row passes per wave of the down kernel (upper bound)
+#define SMOE_DN_PASSES_MAX 8   // row passes per wave of the down kernel (upper bound)
 #endif
 #ifndef SMOE_DN_MIN_WG
 #define SMOE_DN_MIN_WG 256     // keep at least this many down workgroups
@@ -141,6 +141,43 @@ __device__ __forceinline__ void pack_scaled_run(const uint4 (*raw)[NQ4], uint32_
     else pack_segment_q2(v, hp[s]);
     xseg[s] = seg_sum<NQ4 * 2>(hp[s]);
   }
+}
+
+// One 32-value piece of a segment of fp32 activations as 16 pair-ordered f16
+// dwords at the segment's power-of-two scale, with the segment's sum and
+// inverse scale.  A SMOE-Q4 segment (32 values) is one piece; a SMOE-Q2
+// segment (64 values) is two, held by lanes 2i and 2i + 1, which combine
+// their maxima and sums with one DPP swap (every lane must call this).
+template <int BITS>
+__device__ __forceinline__ void pack_scaled_piece(const uint4 (&raw)[8], uint32_t (&hp)[16], float& xsum,
+                                                  float& fac) {
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    v[4 * q + 0] = __uint_as_float(raw[q].x);
+    v[4 * q + 1] = __uint_as_float(raw[q].y);
+    v[4 * q + 2] = __uint_as_float(raw[q].z);
+    v[4 * q + 3] = __uint_as_float(raw[q].w);
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  if constexpr (BITS == 2) mx = fmaxf(mx, dpp_f32<0xB1>(mx));  // the segment's other half
+  const int sh = f16_block_shift(mx);
+  const float up = __builtin_ldexpf(1.0f, sh);
+  fac = __builtin_ldexpf(1.0f, -sh);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] *= up;
+  if constexpr (BITS == 4) {
+    pack_segment(v, hp);
+  } else {  // two groups of 16 in pair order: dword p of a group holds (e_p, e_{p+8})
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) hp[8 * g + p] = f16_bits(v[16 * g + p]) | (f16_bits(v[16 * g + p + 8]) << 16);
+  }
+  xsum = seg_sum<16>(hp);
+  if constexpr (BITS == 2) xsum += dpp_f32<0xB1>(xsum);
 }
 
 // One 16-byte code segment's contribution for code width BITS.
@@ -306,14 +343,16 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   constexpr int P = kWave / LR;
   constexpr int ROWS = NPASS * P;
   // With a row over LR < 64 lanes, the P row groups of a wave need the same
-  // activation segments: the wave converts each segment once (lane l takes
-  // segments l, l + 64, ...) into its own LDS stage, with the segment's sum
-  // and inverse scale, and every lane reads back the ones it needs.  The
-  // stage is private to the wave, so no workgroup barrier is involved.
+  // activation segments: the wave converts each segment once, 32 values per
+  // lane (lane l takes piece l, l + 64, ...; a SMOE-Q2 segment is two pieces),
+  // into its own LDS stage, with the segment's sum and inverse scale, and
+  // every lane reads back the segments it multiplies.  The stage is private
+  // to the wave, so no workgroup barrier is involved.
   constexpr int NQ4 = Run::SEGV / 4;   // 16-byte pieces of a segment's fp32 activations
   constexpr int SSEG = NSEG * LR;      // segments of a row (those with s % LR < LA are used)
+  constexpr int LPS = Run::SEGV / 32;  // 32-value pieces (lanes) per segment
   constexpr bool STAGE = P > 1 && SSEG * Run::NDW * 4 <= 8192;
-  constexpr int PER = (SSEG + kWave - 1) / kWave;  // segments each lane converts
+  constexpr int PER = (SSEG * LPS + kWave - 1) / kWave;  // pieces each lane converts
   __shared__ uint4 hst[STAGE ? 8 : 1][STAGE ? SSEG : 1][Run::NDW / 4];
   __shared__ float2 hsx[STAGE ? 8 : 1][STAGE ? SSEG : 1];
   __shared__ float ylds[kMaxTopK][ROWS];
@@ -371,18 +410,18 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   uint32_t hp[NSEG][Run::NDW];
   float xseg[NSEG], fac[NSEG];
   constexpr int NRAW = STAGE ? PER : NSEG;
-  uint4 hraw[NRAW][NQ4];
-  bool conv[NRAW];  // (staging) this lane converts its m-th segment
+  constexpr int NQR = STAGE ? 8 : NQ4;  // 16-byte pieces per raw entry
+  uint4 hraw[NRAW][NQR];
+  bool conv[NRAW];  // (staging) this lane converts its m-th piece
   auto load_h = [&](int r) {
     if constexpr (STAGE) {
 #pragma unroll
       for (int m = 0; m < PER; ++m) {
-        const int j = lane + kWave * m;
+        const int u = lane + kWave * m, j = u / LPS;
         conv[m] = j < SSEG && (j % LR) < LA;
 #pragma unroll
-        for (int q = 0; q < NQ4; ++q)
-          hraw[m][q] = conv[m] ? gload16(a.h + (size_t)r * a.f + (size_t)j * Run::SEGV + 4 * q)
-                               : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < 8; ++q)
+          hraw[m][q] = conv[m] ? gload16(a.h + (size_t)r * a.f + (size_t)u * 32 + 4 * q) : make_uint4(0, 0, 0, 0);
       }
     } else if (act) {
       load_raw<LR, NSEG, NQ4>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
@@ -395,17 +434,17 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   };
   auto convert_h = [&]() {
     if constexpr (STAGE) {
-      uint32_t cp[PER][Run::NDW];
-      float cx[PER], cf[PER];
-      pack_scaled_run<PER, NQ4, BITS>(hraw, cp, cx, cf);
 #pragma unroll
       for (int m = 0; m < PER; ++m) {
+        uint32_t cp[16];
+        float cx, cf;
+        pack_scaled_piece<BITS>(hraw[m], cp, cx, cf);
         if (conv[m]) {
-          const int j = lane + kWave * m;
+          const int u = lane + kWave * m, j = u / LPS, part = u % LPS;
 #pragma unroll
-          for (int q = 0; q < Run::NDW / 4; ++q)
-            hst[wave][j][q] = make_uint4(cp[m][4 * q], cp[m][4 * q + 1], cp[m][4 * q + 2], cp[m][4 * q + 3]);
-          hsx[wave][j] = make_float2(cx[m], cf[m]);
+          for (int q = 0; q < 4; ++q)
+            hst[wave][j][4 * part + q] = make_uint4(cp[4 * q], cp[4 * q + 1], cp[4 * q + 2], cp[4 * q + 3]);
+          if (part == 0) hsx[wave][j] = make_float2(cx, cf);
         }
       }
       // the stage is read by other lanes of this wave: LDS operations of a
@@ -542,6 +581,10 @@ bool decode_shape_supported(int d, int f, int chunk, int bits) {
   switch (V) { SMOE_CASE(1, NAME, __VA_ARGS__) SMOE_CASE(2, NAME, __VA_ARGS__)             \
                SMOE_CASE(4, NAME, __VA_ARGS__)                                             \
                default: return hipErrorInvalidValue; }
+#define SMOE_NP8_SWITCH(V, NAME, ...)                                                       \
+  switch (V) { SMOE_CASE(1, NAME, __VA_ARGS__) SMOE_CASE(2, NAME, __VA_ARGS__)             \
+               SMOE_CASE(4, NAME, __VA_ARGS__) SMOE_CASE(8, NAME, __VA_ARGS__)             \
+               default: return hipErrorInvalidValue; }
 // (code width, chunk): SMOE-Q4 with chunks of 32 or 64, SMOE-Q2 with chunks of 64
 #define SMOE_FORMAT_SWITCH(B, C, ...)                                                      \
   if ((B) == 4 && (C) == 32) { constexpr int BITS = 4, CHUNK = 32; __VA_ARGS__; }          \
@@ -600,9 +643,10 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   const int P = 64 / sp.lr;
   int np = 1;
   while (np * 2 <= SMOE_DN_PASSES_MAX && a.d / (P * np * 2) >= SMOE_DN_MIN_WG) np *= 2;
-  // a lane holding more than 128 fp32 activations takes one row pass (more
-  // would spill registers)
+  // register budget: a lane holding more than 128 fp32 activations takes one
+  // row pass, three or more segments at most four (more would spill)
   if (sp.nseg * (128 / a.bits) > 128) np = 1;
+  if (sp.nseg >= 3 && np > 4) np = 4;
   const int rows = np * P;
   if (a.d % rows) return hipErrorInvalidValue;  // every workgroup owns full rows
   const int nw = a.k < 8 ? a.k : 8;
@@ -610,12 +654,12 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   if (sp.la != sp.lr) {  // one segment per active lane: LA = 3 LR / 4
     if (a.bits != 2 || a.chunk != 64) return hipErrorInvalidValue;
     constexpr int BITS = 2, CHUNK = 64;
-    SMOE_LR_SWITCH(sp.lr, SMOE_NP_SWITCH(np, NPASS,
+    SMOE_LR_SWITCH(sp.lr, SMOE_NP8_SWITCH(np, NPASS,
         hipLaunchKernelGGL((decode_down_kernel<LR, 1, NPASS, CHUNK, BITS, LR * 3 / 4>), grid, dim3(64 * nw), 0, s,
                            a)));
     return hipGetLastError();
   }
-  SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NPASS,
+  SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP8_SWITCH(np, NPASS,
       hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS, LR>), grid, dim3(64 * nw), 0, s, a)))));
   return hipGetLastError();
 }
