@@ -28,7 +28,7 @@
 #define SMOE_GU_WAVES 4        // waves per gate/up workgroup (a multiple of 2)
 #endif
 // every gate/up thread stages one logit and one blob pointer of the layer
-static_assert(64 * SMOE_GU_WAVES >= smoe::kMaxExperts, "a gate/up workgroup needs a thread per expert");
+static_assert(64 * SMOE_GU_WAVES == smoe::kMaxExperts, "a gate/up workgroup has one thread per expert slot");
 #ifndef SMOE_GU_ROWS_MAX
 #define SMOE_GU_ROWS_MAX 4     // rows per wave of the gate/up kernel (upper bound)
 #endif
@@ -199,7 +199,7 @@ __device__ __forceinline__ const void* expert_pointer(const DecodeArgs& a, int r
 
 // The NP * (64 / LR) rows of one wave (all in expert r, starting at row
 // n_begin): every weight load is issued before any is consumed.
-template <int LR, int NSEG, int NP, int CHUNK, int BITS>
+template <int LR, int NSEG, int NP, int CHUNK, int BITS, bool PX>
 __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t* blob, int r, int n_begin, int li,
                                              int grp, const uint4 (*xraw)[LaneRun<LR, CHUNK, BITS>::NQ]) {
   using Run = LaneRun<LR, CHUNK, BITS>;
@@ -233,7 +233,7 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
   // this lane's input columns as f16 pairs, converted while the weights stream
   uint32_t xp[NSEG][Run::NDW];
   float xseg[NSEG];
-  if (a.px) pack_f16_run<NSEG, Run::NQ>(xraw, xp, xseg);
+  if constexpr (PX) pack_f16_run<NSEG, Run::NQ>(xraw, xp, xseg);
   else pack_bf16_run<NSEG, Run::NQ>(xraw, xp, xseg);
 
 #pragma unroll
@@ -253,12 +253,17 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
 // ---------------------------------------------------------------------------
 // Gate + up + SwiGLU.  One wave owns NP * (64 / LR) consecutive rows of the
 // flattened (rank, row) space, all inside one expert; LR lanes share a row.
-// With a.sel.logits set, the workgroup first selects the top k itself from the
-// layer's logits (every workgroup reaches the same, deterministic selection)
-// and finds the blobs in src.table; workgroup 0 also publishes ids, weights and
-// pointers.  grid = ceil(k * d_ff / (4 * rows per wave)) workgroups of 4 waves.
+// FUSED (the chained decode): the workgroup first selects the top k itself
+// from the layer's logits (every workgroup reaches the same, deterministic
+// selection), finds the blobs in src.table and reads the router's
+// pair-ordered f16 x; workgroup 0 also publishes ids, weights and pointers.
+// Otherwise the k experts come from src (or ptrs) and x is bf16.  The
+// prologue's loads are unconditional (clamped indices), so the kernel
+// arguments they need are fetched together rather than one dependent scalar
+// load after another.  grid = ceil(k * d_ff / (4 * rows per wave)) workgroups
+// of 4 waves.
 // ---------------------------------------------------------------------------
-template <int LR, int NSEG, int NP, int CHUNK, int BITS>
+template <int LR, int NSEG, int NP, int CHUNK, int BITS, bool FUSED>
 __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(DecodeArgs a) {
   using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;  // rows per pass
@@ -268,34 +273,34 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
   __shared__ const void* s_tab[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane % LR, grp = lane / LR;
+  const int E = a.E;
 
-  const bool fused = a.sel.logits != nullptr;
   double lv = 0.0;
   const void* tv = nullptr;
-  if (fused) {
-    if (tid < a.E) {  // the layer's logits and blob table
-      lv = a.sel.logits[tid];
-      tv = a.src.table[tid];
-    }
-  } else if (tid < a.k) {
-    s_ptr[tid] = expert_pointer(a, tid);
+  if constexpr (FUSED) {  // the layer's logits and blob table (clamped: no branch)
+    const int te = tid < E ? tid : E - 1;
+    lv = a.sel.logits[te];
+    tv = a.src.table[te];
+    __builtin_amdgcn_sched_barrier(0);  // these first: the selection waits on them, not on x
+  } else {
+    if (tid < a.k) s_ptr[tid] = expert_pointer(a, tid);
   }
   // (the router writes its pair-ordered f16 copy of x in the order of BITS)
   uint4 xraw[NSEG][Run::NQ];
-  if (a.px) load_raw<LR, NSEG, Run::NQ>(a.px + li * Run::SEGV, xraw);
+  if constexpr (FUSED) load_raw<LR, NSEG, Run::NQ>(a.px + li * Run::SEGV, xraw);
   else load_raw<LR, NSEG, Run::NQ>(a.x + li * Run::SEGV, xraw);
-  if (fused && tid < kMaxExperts) {  // stored after the input loads are issued
+  if constexpr (FUSED) {  // stored after the input loads are issued (one thread per expert slot)
     // padding, and a NaN logit (from a non-finite residual), rank as -inf
-    const double l = (tid < a.E && lv == lv) ? lv : -__builtin_inf();
+    const double l = (tid < E && lv == lv) ? lv : -__builtin_inf();
     tk.log[tid] = l;
     tk.logf[tid] = (float)l;
-    if (tid < a.E) s_tab[tid] = tv;
+    if (tid < E) s_tab[tid] = tv;
     if (tid < kMaxTopK) tk.idx[tid] = -1;
   }
   __syncthreads();
-  if (fused) {
-    if (a.E <= 128) topk_select_fast128<64 * SMOE_GU_WAVES>(tk, a.E, a.k, s_tab, s_ptr);
-    else topk_select_fast(tk, a.E, a.k, s_tab, s_ptr);
+  if constexpr (FUSED) {
+    if (E <= 128) topk_select_fast128<64 * SMOE_GU_WAVES>(tk, E, a.k, s_tab, s_ptr);
+    else topk_select_fast(tk, E, a.k, s_tab, s_ptr);
   }
 
   const int gw = blockIdx.x * (blockDim.x >> 6) + wave;
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
     const int n_begin = row0 - r * a.f;
     const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
     if (blob) {
-      gate_up_rows<LR, NSEG, NP, CHUNK, BITS>(a, blob, r, n_begin, li, grp, xraw);
+      gate_up_rows<LR, NSEG, NP, CHUNK, BITS, FUSED>(a, blob, r, n_begin, li, grp, xraw);
     } else {  // an index outside [0, E) or a null table entry: the rank contributes nothing
       for (int it = lane; it < RPW; it += kWave) a.h[(size_t)r * a.f + n_begin + it] = 0.f;
     }
@@ -313,8 +318,8 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
 
   // Workgroup 0 publishes the selection for the down kernel after its own rows
   // (uniform branch: every wave of the workgroup reaches the barriers inside).
-  if (fused && blockIdx.x == 0) {
-    topk_weights(tk, a.E, a.k, a.norm);
+  if (FUSED && blockIdx.x == 0) {
+    topk_weights(tk, E, a.k, a.norm);
     if (tid < a.k) {
       const int e = tk.idx[tid];
       a.sel.idx_out[tid] = e;
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
 // share one expert's h as few times as possible); the others contribute 0.
 // grid = ceil(d / rows per workgroup), block = 64 * min(k, 8).
 // ---------------------------------------------------------------------------
-template <int LR, int NSEG, int NPASS, int CHUNK, int BITS, int LA>
+template <int LR, int NSEG, int NPASS, int CHUNK, int BITS, int LA, bool FROM_PTRS>
 __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;
@@ -360,17 +365,22 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   __shared__ float s_w[kMaxTopK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nw = blockDim.x >> 6;
-  if (tid < a.k) {
-    // both loads in flight before either is stored
-    const float w = a.w[tid];
-    const void* p = expert_pointer(a, tid);
-    s_w[tid] = w;
-    s_ptr[tid] = p;
+  {
+    // the mixing weights and blob pointers (FROM_PTRS: the ones the chained
+    // gate/up kernel published), both loads in flight before either is
+    // stored; clamped indices keep branches out of the loads' way
+    const int tk = tid < a.k ? tid : 0;
+    const float w = a.w[tk];
+    const void* p = FROM_PTRS ? a.ptrs[tk] : expert_pointer(a, tk);
+    if (tid < a.k) {
+      s_w[tid] = w;
+      s_ptr[tid] = p;
+    }
   }
   // the residual entries this workgroup updates at the end, loaded now so
   // that the final read-modify-write does not wait on memory (no other
   // workgroup touches these rows)
-  const float res_pre = tid < ROWS ? a.residual[(size_t)blockIdx.x * ROWS + tid] : 0.f;
+  const float res_pre = a.residual[(size_t)blockIdx.x * ROWS + (tid < ROWS ? tid : 0)];
   // Pull the next layer's router rows into cache while this kernel streams:
   // the router workgroup w (rows [2w, 2w + 2)) runs on XCD w % 8, so the down
   // workgroups of that XCD each fetch one slice of those rows.  Each thread
@@ -610,13 +620,27 @@ hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t 
   // the launch bounds and the selection's thread count are SMOE_GU_WAVES waves
   constexpr int nw = SMOE_GU_WAVES;
   const dim3 grid((waves + nw - 1) / nw);
-  SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
-      if (start || stop) {
-        hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS>), grid, dim3(64 * nw), 0, s,
-                              start, stop, 0, a);
-      } else {
-        hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS>), grid, dim3(64 * nw), 0, s, a);
-      }))));
+  // the chained decode selects inside the kernel and reads the router's
+  // pair-ordered x; the per-layer calls give experts and bf16 x
+  const bool fused = a.sel.logits != nullptr;
+  if (fused != (a.px != nullptr)) return hipErrorInvalidValue;
+  if (fused) {
+    SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
+        if (start || stop) {
+          hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, true>), grid, dim3(64 * nw), 0, s,
+                                start, stop, 0, a);
+        } else {
+          hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, true>), grid, dim3(64 * nw), 0, s, a);
+        }))));
+  } else {
+    SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
+        if (start || stop) {
+          hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, false>), grid, dim3(64 * nw), 0, s,
+                                start, stop, 0, a);
+        } else {
+          hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, false>), grid, dim3(64 * nw), 0, s, a);
+        }))));
+  }
   return hipGetLastError();
 }
 
@@ -651,16 +675,31 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   if (a.d % rows) return hipErrorInvalidValue;  // every workgroup owns full rows
   const int nw = a.k < 8 ? a.k : 8;
   const dim3 grid(a.d / rows);
+  // the chained decode's pointers, published by its gate/up kernel
+  const bool from_ptrs = a.ptrs != nullptr && !a.src.direct[0];
   if (sp.la != sp.lr) {  // one segment per active lane: LA = 3 LR / 4
     if (a.bits != 2 || a.chunk != 64) return hipErrorInvalidValue;
     constexpr int BITS = 2, CHUNK = 64;
-    SMOE_LR_SWITCH(sp.lr, SMOE_NP8_SWITCH(np, NPASS,
-        hipLaunchKernelGGL((decode_down_kernel<LR, 1, NPASS, CHUNK, BITS, LR * 3 / 4>), grid, dim3(64 * nw), 0, s,
-                           a)));
+    if (from_ptrs) {
+      SMOE_LR_SWITCH(sp.lr, SMOE_NP8_SWITCH(np, NPASS,
+          hipLaunchKernelGGL((decode_down_kernel<LR, 1, NPASS, CHUNK, BITS, LR * 3 / 4, true>), grid, dim3(64 * nw),
+                             0, s, a)));
+    } else {
+      SMOE_LR_SWITCH(sp.lr, SMOE_NP8_SWITCH(np, NPASS,
+          hipLaunchKernelGGL((decode_down_kernel<LR, 1, NPASS, CHUNK, BITS, LR * 3 / 4, false>), grid, dim3(64 * nw),
+                             0, s, a)));
+    }
     return hipGetLastError();
   }
-  SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP8_SWITCH(np, NPASS,
-      hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS, LR>), grid, dim3(64 * nw), 0, s, a)))));
+  if (from_ptrs) {
+    SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP8_SWITCH(np, NPASS,
+        hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS, LR, true>), grid, dim3(64 * nw), 0, s,
+                           a)))));
+  } else {
+    SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP8_SWITCH(np, NPASS,
+        hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS, LR, false>), grid, dim3(64 * nw), 0, s,
+                           a)))));
+  }
   return hipGetLastError();
 }
 

@@ -31,12 +31,15 @@ __global__ __launch_bounds__(1024) void route_logits_decode_kernel(RouteArgs a) 
   const int d = a.d, e = blockIdx.x;
   const int j = tid * 8;
   const bool has = j < d;
-  uint4 wv = make_uint4(0, 0, 0, 0);
-  float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0;
-  if (has) {
-    wv = gload16(a.w_router + (size_t)e * d + j);
-    r0 = *reinterpret_cast<const float4*>(a.residual + j);
-    r1 = *reinterpret_cast<const float4*>(a.residual + j + 4);
+  // loads at clamped columns, zeroed when the thread owns none (no branch
+  // before the loads: the kernel arguments they need arrive together)
+  const int jc = has ? j : 0;
+  uint4 wv = gload16(a.w_router + (size_t)e * d + jc);
+  float4 r0 = *reinterpret_cast<const float4*>(a.residual + jc);
+  float4 r1 = *reinterpret_cast<const float4*>(a.residual + jc + 4);
+  if (!has) {
+    wv = make_uint4(0, 0, 0, 0);
+    r0 = r1 = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   double ss = (((double)r0.x * r0.x + (double)r0.y * r0.y) + ((double)r0.z * r0.z + (double)r0.w * r0.w)) +
               (((double)r1.x * r1.x + (double)r1.y * r1.y) + ((double)r1.z * r1.z + (double)r1.w * r1.w));
