@@ -14,6 +14,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # no packed-fp32 instructions (see the design notes on v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments arrive in SGPRs at dispatch, so a
+    # kernel's first loads need not wait for a kernel-argument fetch
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -264,7 +264,10 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint8_t*
 // of 4 waves.
 // ---------------------------------------------------------------------------
 template <int LR, int NSEG, int NP, int CHUNK, int BITS, bool FUSED>
-__global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(const double* logits,
+                                                                             const void* const* table,
+                                                                             const uint16_t* xin, int E,
+                                                                             DecodeArgs a) {
   using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;  // rows per pass
   constexpr int RPW = NP * P;    // rows per wave
@@ -273,22 +276,20 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
   __shared__ const void* s_tab[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane % LR, grp = lane / LR;
-  const int E = a.E;
 
   double lv = 0.0;
   const void* tv = nullptr;
   if constexpr (FUSED) {  // the layer's logits and blob table (clamped: no branch)
     const int te = tid < E ? tid : E - 1;
-    lv = a.sel.logits[te];
-    tv = a.src.table[te];
+    lv = logits[te];
+    tv = table[te];
     __builtin_amdgcn_sched_barrier(0);  // these first: the selection waits on them, not on x
   } else {
     if (tid < a.k) s_ptr[tid] = expert_pointer(a, tid);
   }
   // (the router writes its pair-ordered f16 copy of x in the order of BITS)
   uint4 xraw[NSEG][Run::NQ];
-  if constexpr (FUSED) load_raw<LR, NSEG, Run::NQ>(a.px + li * Run::SEGV, xraw);
-  else load_raw<LR, NSEG, Run::NQ>(a.x + li * Run::SEGV, xraw);
+  load_raw<LR, NSEG, Run::NQ>(xin + li * Run::SEGV, xraw);
   if constexpr (FUSED) {  // stored after the input loads are issued (one thread per expert slot)
     // padding, and a NaN logit (from a non-finite residual), rank as -inf
     const double l = (tid < E && lv == lv) ? lv : -__builtin_inf();
@@ -343,7 +344,9 @@ __global__ __launch_bounds__(64 * SMOE_GU_WAVES) void decode_gate_up_kernel(Deco
 // grid = ceil(d / rows per workgroup), block = 64 * min(k, 8).
 // ---------------------------------------------------------------------------
 template <int LR, int NSEG, int NPASS, int CHUNK, int BITS, int LA, bool FROM_PTRS>
-__global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(512) void decode_down_kernel(const float* w_mix, const void* const* ptrs,
+                                                          const float* h, float* residual, int k, int f,
+                                                          DecodeArgs a) {
   using Run = LaneRun<LR, CHUNK, BITS>;
   constexpr int P = kWave / LR;
   constexpr int ROWS = NPASS * P;
@@ -369,10 +372,10 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
     // the mixing weights and blob pointers (FROM_PTRS: the ones the chained
     // gate/up kernel published), both loads in flight before either is
     // stored; clamped indices keep branches out of the loads' way
-    const int tk = tid < a.k ? tid : 0;
-    const float w = a.w[tk];
-    const void* p = FROM_PTRS ? a.ptrs[tk] : expert_pointer(a, tk);
-    if (tid < a.k) {
+    const int tk = tid < k ? tid : 0;
+    const float w = w_mix[tk];
+    const void* p = FROM_PTRS ? ptrs[tk] : expert_pointer(a, tk);
+    if (tid < k) {
       s_w[tid] = w;
       s_ptr[tid] = p;
     }
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   // the residual entries this workgroup updates at the end, loaded now so
   // that the final read-modify-write does not wait on memory (no other
   // workgroup touches these rows)
-  const float res_pre = a.residual[(size_t)blockIdx.x * ROWS + (tid < ROWS ? tid : 0)];
+  const float res_pre = residual[(size_t)blockIdx.x * ROWS + (tid < ROWS ? tid : 0)];
   // Pull the next layer's router rows into cache while this kernel streams:
   // the router workgroup w (rows [2w, 2w + 2)) runs on XCD w % 8, so the down
   // workgroups of that XCD each fetch one slice of those rows.  Each thread
@@ -411,8 +414,8 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   const int li = lane % LR, grp = lane / LR;
   const bool act = LA == LR || li < LA;
   const int n0 = blockIdx.x * ROWS;
-  const size_t row_bytes = (size_t)a.f * BITS / 8;
-  const size_t prow_bytes = (size_t)(a.f / CHUNK) * 4;
+  const size_t row_bytes = (size_t)f * BITS / 8;
+  const size_t prow_bytes = (size_t)(f / CHUNK) * 4;
 
   // h_r for this lane's columns as scaled pair-ordered f16, its segment sums
   // and the segments' inverse scales.  An idle lane (li >= LA) keeps zero
@@ -431,10 +434,10 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
         conv[m] = j < SSEG && (j % LR) < LA;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          hraw[m][q] = conv[m] ? gload16(a.h + (size_t)r * a.f + (size_t)u * 32 + 4 * q) : make_uint4(0, 0, 0, 0);
+          hraw[m][q] = conv[m] ? gload16(h + (size_t)r * f + (size_t)u * 32 + 4 * q) : make_uint4(0, 0, 0, 0);
       }
     } else if (act) {
-      load_raw<LR, NSEG, NQ4>(a.h + (size_t)r * a.f + li * Run::SEGV, hraw);
+      load_raw<LR, NSEG, NQ4>(h + (size_t)r * f + li * Run::SEGV, hraw);
     } else {
 #pragma unroll
       for (int s = 0; s < NSEG; ++s)
@@ -492,10 +495,10 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   // The first rank's activations do not depend on the expert pointers: their
   // loads go out with the pointers' (the conversion waits until the weight
   // loads are in flight).
-  if (wave < a.k) load_h(wave);
+  if (wave < k) load_h(wave);
   __syncthreads();
 
-  for (int r = wave, it = 0; r < a.k; r += nw, ++it) {
+  for (int r = wave, it = 0; r < k; r += nw, ++it) {
     const uint8_t* blob = reinterpret_cast<const uint8_t*>(s_ptr[r]);
     if (!blob) {
       for (int row = lane; row < ROWS; row += kWave) ylds[r][row] = 0.f;
@@ -537,8 +540,8 @@ __global__ __launch_bounds__(512) void decode_down_kernel(DecodeArgs a) {
   for (int row = tid; row < ROWS; row += blockDim.x) {
     const int n = n0 + row;
     float acc = 0.f;
-    for (int r = 0; r < a.k; ++r) acc = fmaf(s_w[r], ylds[r][row], acc);
-    a.residual[n] = (row == tid ? res_pre : a.residual[n]) + acc;
+    for (int r = 0; r < k; ++r) acc = fmaf(s_w[r], ylds[r][row], acc);
+    residual[n] = (row == tid ? res_pre : residual[n]) + acc;
   }
   // keeps the prefetch loads alive (all four words, so that no register of a
   // pending load is reused early, which would force a wait for it)
@@ -624,21 +627,24 @@ hipError_t launch_decode_gate_up(const DecodeArgs& a, hipStream_t s, hipEvent_t 
   // pair-ordered x; the per-layer calls give experts and bf16 x
   const bool fused = a.sel.logits != nullptr;
   if (fused != (a.px != nullptr)) return hipErrorInvalidValue;
+  const uint16_t* px = reinterpret_cast<const uint16_t*>(a.px);
   if (fused) {
     SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
         if (start || stop) {
           hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, true>), grid, dim3(64 * nw), 0, s,
-                                start, stop, 0, a);
+                                start, stop, 0, a.sel.logits, a.src.table, px, a.E, a);
         } else {
-          hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, true>), grid, dim3(64 * nw), 0, s, a);
+          hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, true>), grid, dim3(64 * nw), 0, s,
+                             a.sel.logits, a.src.table, px, a.E, a);
         }))));
   } else {
     SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP_SWITCH(np, NP,
         if (start || stop) {
           hipExtLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, false>), grid, dim3(64 * nw), 0, s,
-                                start, stop, 0, a);
+                                start, stop, 0, a.sel.logits, a.src.table, a.x, a.E, a);
         } else {
-          hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, false>), grid, dim3(64 * nw), 0, s, a);
+          hipLaunchKernelGGL((decode_gate_up_kernel<LR, NSEG, NP, CHUNK, BITS, false>), grid, dim3(64 * nw), 0, s,
+                             a.sel.logits, a.src.table, a.x, a.E, a);
         }))));
   }
   return hipGetLastError();
@@ -662,6 +668,10 @@ static DownSplit split_down(int f, int bits) {
   return {sp.lr, sp.nseg, sp.lr};
 }
 
+// the down kernel's leading scalar arguments (preloaded into registers at
+// dispatch) and the argument block
+#define SMOE_DOWN_HOT_ARGS(a) (a).w, (a).ptrs, (a).h, (a).residual, (a).k, (a).f, (a)
+
 hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
   const DownSplit sp = split_down(a.f, a.bits);
   const int P = 64 / sp.lr;
@@ -683,22 +693,22 @@ hipError_t launch_decode_down(const DecodeArgs& a, hipStream_t s) {
     if (from_ptrs) {
       SMOE_LR_SWITCH(sp.lr, SMOE_NP8_SWITCH(np, NPASS,
           hipLaunchKernelGGL((decode_down_kernel<LR, 1, NPASS, CHUNK, BITS, LR * 3 / 4, true>), grid, dim3(64 * nw),
-                             0, s, a)));
+                             0, s, SMOE_DOWN_HOT_ARGS(a))));
     } else {
       SMOE_LR_SWITCH(sp.lr, SMOE_NP8_SWITCH(np, NPASS,
           hipLaunchKernelGGL((decode_down_kernel<LR, 1, NPASS, CHUNK, BITS, LR * 3 / 4, false>), grid, dim3(64 * nw),
-                             0, s, a)));
+                             0, s, SMOE_DOWN_HOT_ARGS(a))));
     }
     return hipGetLastError();
   }
   if (from_ptrs) {
     SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP8_SWITCH(np, NPASS,
         hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS, LR, true>), grid, dim3(64 * nw), 0, s,
-                           a)))));
+                           SMOE_DOWN_HOT_ARGS(a))))));
   } else {
     SMOE_FORMAT_SWITCH(a.bits, a.chunk, SMOE_LR_SWITCH(sp.lr, SMOE_NSEG_SWITCH(sp.nseg, SMOE_NP8_SWITCH(np, NPASS,
         hipLaunchKernelGGL((decode_down_kernel<LR, NSEG, NPASS, CHUNK, BITS, LR, false>), grid, dim3(64 * nw), 0, s,
-                           a)))));
+                           SMOE_DOWN_HOT_ARGS(a))))));
   }
   return hipGetLastError();
 }

@@ -24,19 +24,20 @@ constexpr int kRouteMaxR = 8;   // float4 of residual per thread: d <= 8192
 // (the token's latency is the kernel's cost).  Workgroup 0 writes x (bf16) and
 // its pair-ordered f16 copy with 16-byte stores.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void route_logits_decode_kernel(RouteArgs a) {
+__global__ __launch_bounds__(1024) void route_logits_decode_kernel(const uint16_t* w_router, const float* residual,
+                                                                   int d, RouteArgs a) {
   __shared__ double red[16];
   __shared__ double part[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int d = a.d, e = blockIdx.x;
+  const int e = blockIdx.x;
   const int j = tid * 8;
   const bool has = j < d;
   // loads at clamped columns, zeroed when the thread owns none (no branch
-  // before the loads: the kernel arguments they need arrive together)
+  // before the loads; the arguments they need come preloaded in registers)
   const int jc = has ? j : 0;
-  uint4 wv = gload16(a.w_router + (size_t)e * d + jc);
-  float4 r0 = *reinterpret_cast<const float4*>(a.residual + jc);
-  float4 r1 = *reinterpret_cast<const float4*>(a.residual + jc + 4);
+  uint4 wv = gload16(w_router + (size_t)e * d + jc);
+  float4 r0 = *reinterpret_cast<const float4*>(residual + jc);
+  float4 r1 = *reinterpret_cast<const float4*>(residual + jc + 4);
   if (!has) {
     wv = make_uint4(0, 0, 0, 0);
     r0 = r1 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -255,7 +256,8 @@ hipError_t launch_route_logits(const RouteArgs& a, hipStream_t s, int* groups) {
     hipLaunchKernelGGL(route_logits_mfma_kernel, dim3((a.n_tok + 15) / 16, *groups), dim3(64 * ((a.E + 15) / 16)),
                        0, s, a);
   } else if (a.n_tok == 1 && a.d % 256 == 0 && a.d <= 8192) {
-    hipLaunchKernelGGL(route_logits_decode_kernel, dim3(a.E), dim3(64 * ((a.d + 511) / 512)), 0, s, a);
+    hipLaunchKernelGGL(route_logits_decode_kernel, dim3(a.E), dim3(64 * ((a.d + 511) / 512)), 0, s, a.w_router,
+                       a.residual, a.d, a);
   } else {
     return hipErrorInvalidValue;  // (the dims checks admit no other shape)
   }
