@@ -7,7 +7,11 @@ A step is one decode token through all 94 layers: exact routing (RMSNorm,
 float64 gate matvec, top-8, norm_topk_prob) and the fused SMOE-Q4 expert FFN
 added into the residual, each step starting from a fresh N(0,1) bf16 hidden
 state.  The token's 282 kernels are captured once into a HIP graph and
-replayed; the step's input copy runs eagerly inside the timed region.
+replayed; the step's input copy runs eagerly inside the timed region.  The
+line also carries ``prefill``: the prefill workload (a 512-token prompt in
+chunks of 64, Zipf(1.1)-biased routing) on the same stack (same experts and
+routers), with its own roofline (union bytes over grouped-GEMM time), MFMA
+utilisation and oracle baseline.
 
 Other workloads (one JSON line each): ``--workload prefill`` -- a 512-token
 prompt in chunks of 64 through the same 94 layers, layer-major, Zipf-biased
@@ -36,6 +40,7 @@ import synth  # noqa: E402
 from synth.device import DeviceStack  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_FLOPS = 2.5e15  # MI355X dense fp16 / bf16 matrix peak
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 # sources of the decode gate/up kernel: a stored traffic figure counts only
 # while they are unchanged since its counters were read
@@ -191,7 +196,8 @@ def cpu_baseline(stack, wl, budget_s=15.0):
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     per_token = spent / n * wl.n_layers
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": os.cpu_count(), "blas_threads": threads,
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"1 decode token through the first {n} of {wl.n_layers} layers, float64 numpy oracle, "
                       f"{spent:.1f} s of oracle time; tokens/s extrapolated to all {wl.n_layers} layers"}
 
@@ -268,7 +274,9 @@ def bench_decode(args):
     log(f"plain reads: 4 GiB stream {refs['stream_4gib_gbps']:.0f} GB/s; one launch of the same "
         f"{per_launch} B {refs['one_launch_same_bytes_us']:.2f} us = {refs['one_launch_same_bytes_gbps']:.0f} GB/s")
 
-    bytes_per_token = wl.n_layers * (dims.top_k * off["bytes"] + dims.n_experts * dims.d_model * 2)
+    layer_bytes = dims.top_k * off["bytes"] + dims.n_experts * dims.d_model * 2
+    bytes_per_token = wl.n_layers * layer_bytes
+    layer_us = ms / K * 1000.0 / wl.n_layers
     out = {
         "metric": f"MoE decode tokens/s + achieved HBM GB/s on {qname} expert bytes ({SHAPE_LABEL[args.shape]})",
         "value": tok_s,
@@ -287,6 +295,11 @@ def bench_decode(args):
                    "batch": 1,
                    "vault_bytes": stack.vault.numel(), "parallelism": "single GPU"},
         f"gbps_{args.quant}_expert_and_router_bytes": tok_s * bytes_per_token / 1e9,
+        "per_layer": {"bytes": layer_bytes, "us": layer_us, "gbps": layer_bytes / layer_us / 1e3,
+                      "frac": layer_bytes / layer_us / 1e3 / HBM_PEAK_GBPS,
+                      "timing": "graph replays: token time / layers; a layer's three kernels and the next "
+                                "layer's run back to back, so this is one layer's first-kernel start to "
+                                "last-kernel end plus one launch gap"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": stored_traffic(dims.bits, args.shape),
                      "kernel": "decode_gate_up_kernel", "bytes_per_launch": per_launch,
@@ -299,6 +312,17 @@ def bench_decode(args):
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(stack, wl, args.cpu_budget)
+    pwl = PREFILL_WORKLOADS.get(dims.bits)
+    if args.shape == "235b" and not args.no_prefill and pwl is not None and vars(pwl.dims) == vars(dims) \
+            and pwl.seed == wl.seed and pwl.n_layers == wl.n_layers:
+        # the prefill workload has the same experts and routers: only its Zipf
+        # logit bias is new
+        log("prefill on the same stack ...")
+        del H, ws, g
+        bias = torch.from_numpy(np.stack([synth.zipf_bias(pwl.seed, dims, L, pwl.zipf_s)
+                                          for L in range(pwl.n_layers)])).cuda()
+        out["prefill"] = measure_prefill(stack, pwl, pwl.n_layers, bias, args.prefill_steps, 1, chained=False,
+                                         cpu_budget=None if args.no_cpu_baseline else args.prefill_cpu_budget)
     print(json.dumps(out), flush=True)
 
 
@@ -334,43 +358,89 @@ def time_replays(g, warmup, steps, before=None):
     return start.elapsed_time(end) / steps
 
 
-def bench_prefill(args):
-    """Layer-major prefill of a 512-token prompt in chunks of 64: for each chunk
-    and layer, route the chunk (Zipf-biased logits), build the expert union,
-    run the grouped expert FFN and combine into the residual.
+PREFILL_WORKLOADS = {4: synth.CONFIGS[3], 2: synth.Q2_WORKLOADS[3]}
 
-    Two readings of the per-layer input are timed.  ``value``: every layer's
-    MoE input is the prompt's own N(0,1) hidden state (the layers' routers and
-    Zipf permutations are independent, so each layer sees realistic unions).
-    ``chained``: layer L+1 reads layer L's output residual; with the synthetic
-    weights (mean -scale/2 per element) the residual drifts to one common
-    direction within ~10 layers and every token then routes alike, so the
-    unions collapse."""
-    wl = synth.CONFIGS[3] if args.quant == "q4" else synth.Q2_WORKLOADS[3]
+
+def prefill_cpu_baseline(stack, wl, bias_np, prompt_np, budget_s=10.0):
+    """The float64 oracle on the host cores for the prefill workload: the first
+    tokens of the prompt's first chunk through layer 0 (oracle.moe_layer per
+    token, as oracle.prefill_chunk runs a chunk), as many as fit in
+    ``budget_s`` of oracle time (drawing the experts is not timed); per
+    chunk-layer seconds and prompt tokens/s are extrapolated from the
+    per-token time."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    dims = wl.dims
+    cache = {}
+
+    class Experts(dict):
+        def __missing__(self, e):
+            cache[e] = synth.expert_logical(wl.seed, dims, 0, e)
+            return cache[e]
+
+    experts = Experts()
+    spent, n = 0.0, 0
+    for t in range(wl.prefill_chunk):
+        r = prompt_np[t].astype(np.float64)
+        x, _ = oracle.rmsnorm_bf16(r, dims.rms_eps)
+        idx, _ = oracle.select_topk(oracle.router_logits(stack.router_bits[0], x, bias_np[0]), dims.top_k,
+                                    dims.norm_topk_prob)
+        for e in idx:  # draw the token's experts outside the timed region
+            experts[int(e)]
+        t0 = time.perf_counter()
+        oracle.moe_layer(r, stack.router_bits[0], experts, dims, bias_np[0])
+        spent += time.perf_counter() - t0
+        n += 1
+        if spent >= budget_s:
+            break
+    per_token_layer = spent / n
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": 1.0 / (per_token_layer * wl.n_layers), "unit": "prompt tokens/s", "cores": os.cpu_count(),
+            "blas_threads": threads, "kind": "oracle", "cpu": cpu_model(),
+            "s_per_chunk_layer": per_token_layer * wl.prefill_chunk,
+            "sample": f"the first {n} tokens of chunk 0 through layer 0 (float64 numpy oracle.moe_layer, "
+                      f"{spent:.1f} s of oracle time); per chunk-layer = per token x {wl.prefill_chunk}, "
+                      f"prompt tokens/s = 1 / (per token x {wl.n_layers} layers)"}
+
+
+def measure_prefill(stack, wl, NL, bias, steps, warmup, chained=True, instrument_chunks=2, cpu_budget=None):
+    """Layer-major prefill of the workload's prompt in chunks through NL layers
+    of ``stack`` (router logits biased by ``bias`` [NL][E]): for each chunk and
+    layer, route the chunk, build the expert union, run the grouped expert FFN
+    and combine into the residual.
+
+    Two readings of the per-layer input are timed.  ``fresh`` (the reported
+    one): every layer's MoE input is the prompt's own N(0,1) hidden state (the
+    layers' routers and Zipf permutations are independent, so each layer sees
+    realistic unions).  ``chained``: layer L+1 reads layer L's output residual;
+    with the synthetic weights (mean -scale/2 per element) the residual drifts
+    to one common direction within ~10 layers and every token then routes
+    alike, so the unions collapse.
+
+    Kernel timing: the first ``instrument_chunks`` chunks through all NL layers
+    are run eagerly with start/stop events around the two grouped GEMMs (the
+    queue pre-filled by a spin kernel); the roofline is union bytes over GEMM
+    time."""
     dims = wl.dims
     T, C = wl.steps, wl.prefill_chunk
     n_chunks = T // C
-    NL = wl.n_layers if args.layers is None else max(1, min(args.layers, wl.n_layers))
-    torch.cuda.set_device(0)
-    stack = DeviceStack(wl.seed, dims, NL, zipf_s=wl.zipf_s)
-    torch.cuda.synchronize()
-    log(f"stack ready: vault {stack.vault.numel() / 1e9:.2f} GB")
-    prompt = torch.from_numpy(np.stack([synth.hidden_bf16(wl.seed, 20_000 + t, dims.d_model)
-                                        for t in range(T)])).cuda()
+    prompt_np = np.stack([synth.hidden_bf16(wl.seed, 20_000 + t, dims.d_model) for t in range(T)])
+    prompt = torch.from_numpy(prompt_np).cuda()
     resid = torch.empty_like(prompt)
     mu = min(dims.n_experts, C * dims.top_k)
     x = torch.empty((C, dims.d_model), dtype=torch.int16, device="cuda")
     idx = torch.empty((C, dims.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((C, dims.top_k), dtype=torch.float32, device="cuda")
-    ucount = {m: torch.zeros((n_chunks, NL), dtype=torch.int32, device="cuda") for m in ("fresh", "chained")}
+    ucount = {m: torch.zeros((n_chunks, NL), dtype=torch.int32, device="cuda") for m in ("fresh", "chained", "ev")}
     uids = torch.empty(mu, dtype=torch.int32, device="cuda")
     offs = torch.empty(mu + 1, dtype=torch.int32, device="cuda")
     perm = torch.empty(C * dims.top_k, dtype=torch.int32, device="cuda")
     ws = smoe.workspace(dims, C)
 
-    def layer(L, c, r, uc):
-        smoe.route(dims, r, x, stack.router_layer(L), stack.bias_layer(L), idx, w, ws)
-        smoe.moe_prefill_chunk(dims, x, idx, w, stack.table(L), r, uids, uc[c, L:L + 1], offs, perm, ws)
+    def layer(L, c, r, uc, events=None):
+        smoe.route(dims, r, x, stack.router_layer(L), bias[L], idx, w, ws)
+        smoe.moe_prefill_chunk(dims, x, idx, w, stack.table(L), r, uids, uc[c, L:L + 1], offs, perm, ws,
+                               events=events)
 
     def prompt_fresh():
         for c in range(n_chunks):
@@ -387,35 +457,96 @@ def bench_prefill(args):
                 layer(L, c, r, ucount["chained"])
 
     off = synth.blob_sections(dims)
+    gate_up_bytes = (off["down_codes"] - off["gate_codes"]) + (off["down_params"] - off["gate_params"])
+    down_bytes = off["bytes"] - gate_up_bytes
     flops_per_prompt = 6.0 * dims.d_model * dims.d_ff * dims.top_k * NL * T
     res = {}
-    for mode, fn in (("fresh", prompt_fresh), ("chained", prompt_chained)):
+    for mode, fn in (("fresh", prompt_fresh), ("chained", prompt_chained)) if chained else (("fresh", prompt_fresh),):
         g = graph_of(fn)
-        ms = time_replays(g, args.warmup, args.steps)
+        ms = time_replays(g, warmup, steps)
         u = ucount[mode].cpu().numpy()
         ub = int(u.sum()) * off["bytes"]
         res[mode] = {"ms": ms, "tok_s": T / (ms / 1e3), "mean_union": float(u.mean()),
                      "union_bytes": ub, "union_gbps": ub / (ms / 1e3) / 1e9,
-                     "mfma_utilisation": flops_per_prompt / (ms / 1e3) / 2.5e15}
+                     "mfma_utilisation": flops_per_prompt / (ms / 1e3) / MFMA_F16_PEAK_FLOPS}
         log(f"prefill[{mode}]: {ms:.2f} ms/prompt, {res[mode]['tok_s']:.0f} tokens/s, "
             f"mean |union| {u.mean():.1f}, {res[mode]['union_gbps']:.0f} GB/s on union bytes")
         del g
+
+    # per-kernel GEMM timing, fed-prompt reading, first chunks
+    nc = max(1, min(instrument_chunks, n_chunks))
+    ev = HipEvents(4 * nc * NL)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for c in range(nc):
+        r = resid[c * C:(c + 1) * C]
+        for L in range(NL):
+            r.copy_(prompt[c * C:(c + 1) * C])
+            layer(L, c, r, ucount["ev"], events=ev.ev[4 * (c * NL + L):4 * (c * NL + L) + 4])
+    torch.cuda.synchronize()
+    u = ucount["ev"][:nc].cpu().numpy().reshape(-1)
+    gu = np.array([ev.elapsed_ms(4 * i, 4 * i + 1) for i in range(nc * NL)])
+    dn = np.array([ev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(nc * NL)])
+    ev.close()
+    gu_gbps = float((u * gate_up_bytes).sum() / (gu.sum() / 1e3) / 1e9)
+    dn_gbps = float((u * down_bytes).sum() / (dn.sum() / 1e3) / 1e9)
+    gemm_gbps = float((u * off["bytes"]).sum() / ((gu + dn).sum() / 1e3) / 1e9)
+    gemm_flops = 6.0 * dims.d_model * dims.d_ff * dims.top_k * C * len(u)
+    mfma_gemm = gemm_flops / ((gu + dn).sum() / 1e3) / MFMA_F16_PEAK_FLOPS
+    log(f"prefill GEMMs: gate/up {gu.mean() * 1e3:.1f} us ({gu_gbps:.0f} GB/s), down {dn.mean() * 1e3:.1f} us "
+        f"({dn_gbps:.0f} GB/s) over {len(u)} chunk-layers, mean |union| {u.mean():.1f}")
     f = res["fresh"]
     out = {
-        "metric": "layer-major prefill prompt tokens/s + GB/s on union expert bytes (235B-shape, 512-token "
-                  "prompt, chunks of 64" + (")" if dims.bits == 4 else ", SMOE-Q2)"),
-        "value": f["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": f["ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": f["tok_s"], "unit": "prompt tokens/s", "ms_per_prompt": f["ms"],
+        "config": {"workload": wl.name, "layers": NL, "prompt_tokens": T, "chunk": C},
         "dtype": f"q{dims.bits}-affine codes as fp16 MFMA inputs, fp32 accumulation with the affine step folded "
                  "per chunk; float64 router",
         "data": "synthetic (seeded SplitMix64 codes/scales, N(0,0.02) router, Zipf(1.1) logit bias, N(0,1) bf16 "
                 "prompt hidden states fed to every layer)",
-        "config": {"workload": wl.name, "layers": NL, "prompt_tokens": T, "chunk": C,
-                   "parallelism": "single GPU"},
         "mean_union": f["mean_union"], "union_bytes_per_prompt": f["union_bytes"], "union_gbps": f["union_gbps"],
         "union_hbm_frac": f["union_gbps"] / HBM_PEAK_GBPS, "mfma_utilisation": f["mfma_utilisation"],
-        "chained": {k: res["chained"][k] for k in ("tok_s", "ms", "mean_union", "union_gbps", "mfma_utilisation")},
+        "roofline": {"bound": "hbm", "achieved": gu_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gu_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "prefill grouped gate/up GEMM", "bytes_per_launch": float(u.mean() * gate_up_bytes),
+                     "avg_launch_us": float(gu.mean() * 1e3), "launches_timed": int(len(u)),
+                     "timing": "hipExtLaunchKernel start/stop events, eager chunks with the queue pre-filled",
+                     "down_gemm": {"avg_launch_us": float(dn.mean() * 1e3), "achieved": dn_gbps,
+                                   "frac": dn_gbps / HBM_PEAK_GBPS},
+                     "both_gemms": {"achieved": gemm_gbps, "frac": gemm_gbps / HBM_PEAK_GBPS,
+                                    "mfma_utilisation": mfma_gemm}},
     }
+    if chained:
+        out["chained"] = {k: res["chained"][k] for k in ("tok_s", "ms", "mean_union", "union_gbps",
+                                                         "mfma_utilisation")}
+    if cpu_budget:
+        log("cpu baseline (oracle, prefill) ...")
+        out["cpu_baseline"] = prefill_cpu_baseline(stack, wl, bias.cpu().numpy(), prompt_np, cpu_budget)
+    return out
+
+
+def bench_prefill(args):
+    """The prefill workload alone: a 512-token prompt in chunks of 64 through
+    the 94 layers (see measure_prefill)."""
+    wl = PREFILL_WORKLOADS[4 if args.quant == "q4" else 2]
+    dims = wl.dims
+    NL = wl.n_layers if args.layers is None else max(1, min(args.layers, wl.n_layers))
+    torch.cuda.set_device(0)
+    stack = DeviceStack(wl.seed, dims, NL, zipf_s=wl.zipf_s)
+    torch.cuda.synchronize()
+    log(f"stack ready: vault {stack.vault.numel() / 1e9:.2f} GB")
+    p = measure_prefill(stack, wl, NL, stack.bias, args.steps, args.warmup,
+                        cpu_budget=None if args.no_cpu_baseline else args.cpu_budget)
+    out = {
+        "metric": "layer-major prefill prompt tokens/s + GB/s on union expert bytes (235B-shape, 512-token "
+                  "prompt, chunks of 64" + (")" if dims.bits == 4 else ", SMOE-Q2)"),
+        "value": p.pop("value"), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": p.pop("ms_per_prompt"), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+    }
+    p.pop("unit")
+    cfg = p.pop("config")
+    cfg["parallelism"] = "single GPU"
+    out.update(dtype=p.pop("dtype"), data=p.pop("data"), config=cfg)
+    out.update(p)
     print(json.dumps(out), flush=True)
 
 
@@ -754,6 +885,12 @@ def main():
                          "Qwen3-30B-A3B-shaped one (48 layers, d_model 2048, 256 steps by default)")
     ap.add_argument("--prewarm", action="store_true",
                     help="ring workload: after the warm-up tokens, load the most claimed experts (idle time)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode workload: skip the prefill sub-object (the 512-token prompt on the same stack)")
+    ap.add_argument("--prefill-steps", type=int, default=3, help="decode workload: timed prompts of the prefill "
+                                                                 "sub-object")
+    ap.add_argument("--prefill-cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time for the prefill sub-object's CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "

@@ -234,12 +234,15 @@ int smoe_decode_layers_static(const smoe_dims* dims, int32_t n_layers, float* re
  * atomics.  An entry whose expert is outside [0, E) or whose table entry is
  * NULL (e.g. a ring table that holds only an acquired union) takes no part:
  * it is left out of the union and contributes nothing.  A token that lists
- * an expert more than once gets one row per entry (each weight applies). */
+ * an expert more than once gets one row per entry (each weight applies).
+ *   events       host array [4] of hipEvent_t, or NULL: when given, 0 and 1
+ *                are recorded at the start and end of the grouped gate/up
+ *                GEMM and 2 and 3 around the down GEMM (kernel timing) */
 int smoe_moe_prefill_chunk(const smoe_dims* dims, int32_t n_tok, const uint16_t* x,
                            const int32_t* topk_idx, const float* topk_w,
                            const void* const* expert_table, float* residual, int32_t* union_ids,
                            int32_t* union_count, int32_t* offsets, int32_t* perm, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           size_t workspace_bytes, void* const* events, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Expert ring ("The Ring Is an LRU Cache"): HBM slots caching (layer, expert)

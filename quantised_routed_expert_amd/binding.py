@@ -80,7 +80,7 @@ def lib():
             "smoe_moe_decode_slots": (I, [D, VP, VP, P(VP), VP, VP, S, VP]),
             "smoe_decode_layers": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, P(VP), VP, S, VP]),
             "smoe_decode_layers_static": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, VP]),
-            "smoe_moe_prefill_chunk": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, VP]),
+            "smoe_moe_prefill_chunk": (I, [D, ctypes.c_int32, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, S, P(VP), VP]),
             "smoe_ring_create": (I, [P(SmoeRingDesc), P(VP)]),
             "smoe_ring_acquire": (I, [VP, ctypes.c_int32, P(ctypes.c_int32), ctypes.c_int32, P(VP), VP]),
             "smoe_ring_release": (I, [VP]),
@@ -196,11 +196,16 @@ def decode_layers_static(dims, n_layers, residual, w_router, bias, expert_tables
 
 
 def moe_prefill_chunk(dims, x, topk_idx, topk_w, expert_table, residual, union_ids, union_count, offsets,
-                      perm, ws, stream=None):
+                      perm, ws, events=None, stream=None):
+    """events: optional 4 raw hipEvent_t handles (ints) around the two GEMMs."""
     n_tok = x.shape[0]
+    ev = None
+    if events is not None:
+        assert len(events) == 4
+        ev = (ctypes.c_void_p * 4)(*[int(e) for e in events])
     _check(lib().smoe_moe_prefill_chunk(ctypes.byref(dims_struct(dims)), int(n_tok), _ptr(x), _ptr(topk_idx),
                                         _ptr(topk_w), _ptr(expert_table), _ptr(residual), _ptr(union_ids),
-                                        _ptr(union_count), _ptr(offsets), _ptr(perm), _ptr(ws), ws.numel(),
+                                        _ptr(union_count), _ptr(offsets), _ptr(perm), _ptr(ws), ws.numel(), ev,
                                         _stream(stream)))
 
 

@@ -358,7 +358,7 @@ int smoe_decode_layers_static(const smoe_dims* d, int32_t n_layers, float* resid
 int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x, const int32_t* topk_idx,
                            const float* topk_w, const void* const* expert_table, float* residual,
                            int32_t* union_ids, int32_t* union_count, int32_t* offsets, int32_t* perm, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           size_t ws_bytes, void* const* events, void* stream) {
   g_err[0] = 0;
   if (int e = check_dims(d)) return e;
   if (n_tok < 1 || n_tok > kMaxPrefillTokens)
@@ -395,7 +395,7 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
   a.chunk = d->chunk;
   a.bits = quant_bits(d);
   a.lay = blob_layout(d->d_model, d->d_ff, d->chunk, a.bits);
-  hipError_t he = launch_prefill(a, (hipStream_t)stream);
+  hipError_t he = launch_prefill(a, (hipStream_t)stream, reinterpret_cast<const hipEvent_t*>(events));
   if (he != hipSuccess) return hip_fail(he, "prefill launch");
   return SMOE_OK;
 }

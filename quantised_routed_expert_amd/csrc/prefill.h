@@ -33,7 +33,8 @@ struct PrefillArgs {
   BlobLayout lay;
 };
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// ev: null, or 4 events recorded around the gate/up GEMM (0, 1) and the down GEMM (2, 3)
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, const hipEvent_t* ev = nullptr);
 
 // Upper bound on the number of 16-entry slices of a chunk's union experts.
 inline int prefill_max_slices(int T, int k, int E) { return (T * k + 15) / 16 + (E < T * k ? E : T * k); }

@@ -23,6 +23,8 @@
 //               order (no atomics).
 // The pages' own prefill FFN kernels keep a thread-per-row layout (Optimizations,
 // "The Dense Ceiling"); here the dense contraction runs on the matrix cores.
+#include <hip/hip_ext.h>
+
 #include "prefill.h"
 
 namespace smoe {
@@ -623,16 +625,21 @@ __device__ __forceinline__ half8_t codes8(uint32_t w) {
 // elements divided by 16, and the sum of each row's fp16 values over each
 // chunk of 64 (xsum[chunk of the block][row]).  Thread (r = tid / 16, c =
 // tid % 16) moves KT / 16 consecutive values of row r; load() and store() are
-// separate so that the loads run a block ahead.
+// separate so that the loads run a block ahead.  H rows come with one scale
+// per 64-value tile: the block's tiles are put on one common scale per row
+// (the largest tile scale F of the block, a power of two; a tile's values are
+// multiplied by its scale / F <= 1, exactly unless they fall below the fp16
+// normal range, where they are at most 2^-24 of the block's largest), and F
+// goes to fblk[row], by which the caller multiplies the block's result.
 template <bool FROM_BF16, int KT>
 struct FoldStage {
   static constexpr int V = KT / 128;  // 16-byte pieces (8 values) per thread
   uint4 v[V];
-  float fs[V];                        // H rows: the tile scale of each piece's chunk
+  float fs[V];                        // H rows: the tile scale of each piece
 
   // thread (r, k) takes pieces 16 j + k of row r: the 16 threads of a row
-  // read 256 contiguous bytes per load instruction.  For H rows the first
-  // thread of each chunk also loads the chunk's tile scale (hs, tiles).
+  // read 256 contiguous bytes per load instruction.  For H rows each thread
+  // also loads the tile scales of its pieces (hs, tiles).
   __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb,
                                        const float* hs = nullptr, int tiles = 0) {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
@@ -642,14 +649,22 @@ struct FoldStage {
       if (r < n_rows)
         v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + 8 * (16 * j + k));
       fs[j] = 1.0f;
-      if (!FROM_BF16 && r < n_rows && (k & 7) == 0) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 2 * j + (k >> 3)];
+      if (!FROM_BF16 && r < n_rows) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 2 * j + (k >> 3)];
     }
   }
 
-  // fsc (H rows only): [chunk of the block][row] tile scales
-  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16], float (*fsc)[16] = nullptr) const {
+  // fblk (H rows only): [row] the block's common scale
+  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16], float* fblk = nullptr) const {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
     const uint32_t k16 = 0x2C002C00u;  // (1/16, 1/16) in fp16
+    float fb = 1.0f;
+    if (!FROM_BF16) {
+      float m = fs[0];
+#pragma unroll
+      for (int j = 1; j < V; ++j) m = fmaxf(m, fs[j]);
+      fb = row_max16(m);
+      if (k == 0) fblk[r] = fb;
+    }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       uint4 o;
@@ -668,25 +683,25 @@ struct FoldStage {
         o.y = f16_bits(f[1] * 0.0625f) | (f16_bits(f[5] * 0.0625f) << 16);
         o.z = f16_bits(f[2]) | (f16_bits(f[6]) << 16);
         o.w = f16_bits(f[3] * 0.0625f) | (f16_bits(f[7] * 0.0625f) << 16);
-      } else {  // fp16 already in pair order (H): divide dwords 1 and 3 by 16
+      } else {  // fp16 in pair order (H): onto the common scale, dwords 1 and 3 divided by 16
+        const _Float16 rh = (_Float16)(fs[j] / fb);  // a power of two <= 1 (0 below fp16's range)
+        const h2_t ratio = {rh, rh};
         const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        h2_t hv[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const h2_t hv = as_h2(w4[p]);
-          part += (float)hv[0] + (float)hv[1];
+          hv[p] = as_h2(w4[p]) * ratio;
+          part += (float)hv[p][0] + (float)hv[p][1];
         }
-        o.x = v[j].x;
-        o.y = __builtin_bit_cast(uint32_t, as_h2(v[j].y) * as_h2(k16));
-        o.z = v[j].z;
-        o.w = __builtin_bit_cast(uint32_t, as_h2(v[j].w) * as_h2(k16));
+        o.x = __builtin_bit_cast(uint32_t, hv[0]);
+        o.y = __builtin_bit_cast(uint32_t, hv[1] * as_h2(k16));
+        o.z = __builtin_bit_cast(uint32_t, hv[2]);
+        o.w = __builtin_bit_cast(uint32_t, hv[3] * as_h2(k16));
       }
       *reinterpret_cast<uint4*>(&xs[r][8 * (16 * j + k)]) = o;
       // a chunk is 8 pieces: threads 8h .. 8h + 7 of the row (adjacent lanes)
       part = group_sum<8>(part);
-      if ((k & 7) == 0) {
-        xsum[2 * j + (k >> 3)][r] = part;
-        if (!FROM_BF16) fsc[2 * j + (k >> 3)][r] = fs[j];
-      }
+      if ((k & 7) == 0) xsum[2 * j + (k >> 3)][r] = part;
     }
   }
 };
@@ -738,11 +753,11 @@ __device__ __forceinline__ void relayout256(W& w, uint8_t* stage, int lane) {
 // column (feature) and its four rows 4 (lane / 16) + i; chunks in order.  All
 // of the block's MFMA chains are issued before the first result is folded, so
 // the VALU epilogue of one chunk overlaps the MFMAs of the next.
-// With SCALED, the A rows are H tiles stored at a power-of-two scale and the
-// chunk's term is multiplied by its tile scale fsc[chunk][row].
+// With SCALED, the A rows are H rows on one power-of-two scale per row for
+// the block, and the block's sum is multiplied by that scale fblk[row].
 template <int KT, bool SCALED = false>
 __device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _Float16 (*xs)[KT + 8],
-                                            float (*xsum)[16], int lane, float (*fsc)[16] = nullptr) {
+                                            float (*xsum)[16], int lane, const float* fblk = nullptr) {
   constexpr int NC = FoldW<KT>::NPW;
   const int g = lane >> 4, ml = lane & 15, r4 = 4 * (lane >> 4);
   const float4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -760,6 +775,8 @@ __device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _
       P[cl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, codes8(u[2 * h + 1]), P[cl], 0, 0, 0);
     }
   }
+  float4_t blk = zero;
+  float4_t& sum = SCALED ? blk : acc;  // the block's sum, scaled once at the end
 #pragma unroll
   for (int cl = 0; cl < NC; ++cl) {
     const uint4 pw = w.p[cl >> 2];
@@ -767,23 +784,22 @@ __device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _
     const float S = __uint_as_float(prm << 16) * 16777216.0f;  // scale * 2^24
     const float M = __uint_as_float(prm & 0xFFFF0000u);
     const float4 X = *reinterpret_cast<const float4*>(&xsum[cl][r4]);
-    if constexpr (SCALED) {
-      const float4 Fs = *reinterpret_cast<const float4*>(&fsc[cl][r4]);
-      acc[0] = fmaf(Fs.x, fmaf(S, P[cl][0], M * X.x), acc[0]);
-      acc[1] = fmaf(Fs.y, fmaf(S, P[cl][1], M * X.y), acc[1]);
-      acc[2] = fmaf(Fs.z, fmaf(S, P[cl][2], M * X.z), acc[2]);
-      acc[3] = fmaf(Fs.w, fmaf(S, P[cl][3], M * X.w), acc[3]);
-    } else {
-      acc[0] = fmaf(S, P[cl][0], fmaf(M, X.x, acc[0]));
-      acc[1] = fmaf(S, P[cl][1], fmaf(M, X.y, acc[1]));
-      acc[2] = fmaf(S, P[cl][2], fmaf(M, X.z, acc[2]));
-      acc[3] = fmaf(S, P[cl][3], fmaf(M, X.w, acc[3]));
-    }
+    sum[0] = fmaf(S, P[cl][0], fmaf(M, X.x, sum[0]));
+    sum[1] = fmaf(S, P[cl][1], fmaf(M, X.y, sum[1]));
+    sum[2] = fmaf(S, P[cl][2], fmaf(M, X.z, sum[2]));
+    sum[3] = fmaf(S, P[cl][3], fmaf(M, X.w, sum[3]));
+  }
+  if constexpr (SCALED) {
+    const float4 F = *reinterpret_cast<const float4*>(&fblk[r4]);
+    acc[0] = fmaf(F.x, blk[0], acc[0]);
+    acc[1] = fmaf(F.y, blk[1], acc[1]);
+    acc[2] = fmaf(F.z, blk[2], acc[2]);
+    acc[3] = fmaf(F.w, blk[3], acc[3]);
   }
 }
 
 template <int KT>
-__global__ __launch_bounds__(256) void prefill_gate_up_fold_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void prefill_gate_up_fold_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];  // padded rows: conflict-free A reads
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ int rows[16];
@@ -845,7 +861,7 @@ template <int KT>
 __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
-  __shared__ __attribute__((aligned(16))) float fsc[2][KT / 64][16];  // H tile scales
+  __shared__ __attribute__((aligned(16))) float fblk[2][16];  // the blocks' common H scales
   __shared__ int rows[16];
   __shared__ __attribute__((aligned(16))) uint8_t wst[4][KT == 256 ? 16 * kLineStageRow : 16];
   const int n_slices = *a.n_slices;
@@ -879,7 +895,7 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
   __syncthreads();
   hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0, a.Hs, tiles);
-  hr.store(xs[0], xsum[0], fsc[0]);
+  hr.store(xs[0], xsum[0], fblk[0]);
   wlay(w0);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
@@ -887,9 +903,9 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
       hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT, a.Hs, tiles);
       wload(w1, (i + 1) * KT);
     }
-    fold_kblock<KT, true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fsc[i & 1]);
+    fold_kblock<KT, true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fblk[i & 1]);
     if (i + 1 < nk) {
-      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fsc[(i + 1) & 1]);
+      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fblk[(i + 1) & 1]);
       wlay(w1);
     }
     w0 = w1;
@@ -931,7 +947,7 @@ __device__ __forceinline__ half8_t codes8_q2(uint32_t w) {
 template <bool FROM_BF16>
 struct FoldStageQ2 {
   uint4 v[4];
-  float fs[2];  // H rows: the tile scale of each group pair's chunk
+  float fs[2];  // H rows: the tile scale of each group pair's chunk (see FoldStage: one common scale per row)
 
   __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb,
                                        const float* hs = nullptr, int tiles = 0) {
@@ -946,13 +962,18 @@ struct FoldStageQ2 {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       fs[j] = 1.0f;
-      if (!FROM_BF16 && r < n_rows && (k & 3) == 0) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 4 * j + (k >> 2)];
+      if (!FROM_BF16 && r < n_rows) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 4 * j + (k >> 2)];
     }
   }
 
-  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16], float (*fsc)[16] = nullptr) const {
+  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16], float* fblk = nullptr) const {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
     const uint32_t k4 = 0x34003400u;  // (1/4, 1/4) in fp16
+    float fb = 1.0f;
+    if (!FROM_BF16) {
+      fb = row_max16(fmaxf(fs[0], fs[1]));
+      if (k == 0) fblk[r] = fb;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint4 o0, o1;
@@ -976,28 +997,25 @@ struct FoldStageQ2 {
         o1.y = f16_bits(f[5] * 0.25f) | (f16_bits(f[13] * 0.25f) << 16);
         o1.z = f16_bits(f[6]) | (f16_bits(f[14]) << 16);
         o1.w = f16_bits(f[7] * 0.25f) | (f16_bits(f[15] * 0.25f) << 16);
-      } else {  // fp16 already in pair order (H): divide the odd dwords by 4
+      } else {  // fp16 in pair order (H): onto the common scale, the odd dwords divided by 4
+        const _Float16 rh = (_Float16)(fs[j] / fb);  // a power of two <= 1 (0 below fp16's range)
+        const h2_t ratio = {rh, rh};
         const uint32_t w8[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
                                 v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+        uint32_t q[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-          const h2_t hv = as_h2(w8[p]);
+          const h2_t hv = as_h2(w8[p]) * ratio;
           part += (float)hv[0] + (float)hv[1];
+          q[p] = __builtin_bit_cast(uint32_t, (p & 1) ? hv * as_h2(k4) : hv);
         }
-        o0 = v[2 * j];
-        o1 = v[2 * j + 1];
-        o0.y = __builtin_bit_cast(uint32_t, as_h2(o0.y) * as_h2(k4));
-        o0.w = __builtin_bit_cast(uint32_t, as_h2(o0.w) * as_h2(k4));
-        o1.y = __builtin_bit_cast(uint32_t, as_h2(o1.y) * as_h2(k4));
-        o1.w = __builtin_bit_cast(uint32_t, as_h2(o1.w) * as_h2(k4));
+        o0 = make_uint4(q[0], q[1], q[2], q[3]);
+        o1 = make_uint4(q[4], q[5], q[6], q[7]);
       }
       *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k)]) = o0;
       *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k) + 8]) = o1;
       part = group_sum<4>(part);
-      if ((k & 3) == 0) {
-        xsum[4 * j + (k >> 2)][r] = part;
-        if (!FROM_BF16) fsc[4 * j + (k >> 2)][r] = fs[j];
-      }
+      if ((k & 3) == 0) xsum[4 * j + (k >> 2)][r] = part;
     }
   }
 };
@@ -1025,9 +1043,11 @@ __device__ __forceinline__ void load_lines_q2(FoldWQ2& w, const uint8_t* codes_r
 // folds.
 template <bool SCALED = false>
 __device__ __forceinline__ void fold_kblock_q2(float4_t& acc, const FoldWQ2& w, _Float16 (*xs)[512 + 8],
-                                               float (*xsum)[16], int lane, float (*fsc)[16] = nullptr) {
+                                               float (*xsum)[16], int lane, const float* fblk = nullptr) {
   const int g = lane >> 4, ml = lane & 15, r4 = 4 * (lane >> 4);
   const float4_t zero = {0.f, 0.f, 0.f, 0.f};
+  float4_t blk = zero;
+  float4_t& sum = SCALED ? blk : acc;  // the block's sum, scaled once at the end
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     uint32_t u[4] = {w.c[q].x, w.c[q].y, w.c[q].z, w.c[q].w};
@@ -1047,19 +1067,18 @@ __device__ __forceinline__ void fold_kblock_q2(float4_t& acc, const FoldWQ2& w, 
       const float S = __uint_as_float(pw[j] << 16) * 16777216.0f;  // scale * 2^24
       const float M = __uint_as_float(pw[j] & 0xFFFF0000u);
       const float4 X = *reinterpret_cast<const float4*>(&xsum[4 * q + j][r4]);
-      if constexpr (SCALED) {
-        const float4 Fs = *reinterpret_cast<const float4*>(&fsc[4 * q + j][r4]);
-        acc[0] = fmaf(Fs.x, fmaf(S, P[j][0], M * X.x), acc[0]);
-        acc[1] = fmaf(Fs.y, fmaf(S, P[j][1], M * X.y), acc[1]);
-        acc[2] = fmaf(Fs.z, fmaf(S, P[j][2], M * X.z), acc[2]);
-        acc[3] = fmaf(Fs.w, fmaf(S, P[j][3], M * X.w), acc[3]);
-      } else {
-        acc[0] = fmaf(S, P[j][0], fmaf(M, X.x, acc[0]));
-        acc[1] = fmaf(S, P[j][1], fmaf(M, X.y, acc[1]));
-        acc[2] = fmaf(S, P[j][2], fmaf(M, X.z, acc[2]));
-        acc[3] = fmaf(S, P[j][3], fmaf(M, X.w, acc[3]));
-      }
+      sum[0] = fmaf(S, P[j][0], fmaf(M, X.x, sum[0]));
+      sum[1] = fmaf(S, P[j][1], fmaf(M, X.y, sum[1]));
+      sum[2] = fmaf(S, P[j][2], fmaf(M, X.z, sum[2]));
+      sum[3] = fmaf(S, P[j][3], fmaf(M, X.w, sum[3]));
     }
+  }
+  if constexpr (SCALED) {
+    const float4 F = *reinterpret_cast<const float4*>(&fblk[r4]);
+    acc[0] = fmaf(F.x, blk[0], acc[0]);
+    acc[1] = fmaf(F.y, blk[1], acc[1]);
+    acc[2] = fmaf(F.z, blk[2], acc[2]);
+    acc[3] = fmaf(F.w, blk[3], acc[3]);
   }
 }
 
@@ -1122,7 +1141,7 @@ __global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a
   constexpr int KT = 512;
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
-  __shared__ __attribute__((aligned(16))) float fsc[2][KT / 64][16];  // H tile scales
+  __shared__ __attribute__((aligned(16))) float fblk[2][16];  // the blocks' common H scales
   __shared__ int rows[16];
   __shared__ __attribute__((aligned(16))) uint8_t wst[4][16 * kLineStageRow];
   const int n_slices = *a.n_slices;
@@ -1145,7 +1164,7 @@ __global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a
   if (tid < n_rows) rows[tid] = o + tid;  // H rows of this slice
   __syncthreads();
   hr.load(a.H, (size_t)a.f, rows, n_rows, 0, a.Hs, tiles);
-  hr.store(xs[0], xsum[0], fsc[0]);
+  hr.store(xs[0], xsum[0], fblk[0]);
   relayout256(w0, dst, lane);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
@@ -1153,9 +1172,9 @@ __global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a
       hr.load(a.H, (size_t)a.f, rows, n_rows, (i + 1) * KT, a.Hs, tiles);
       load_lines_q2(w1, dc0, row_bytes, dp, (i + 1) * KT, lane);
     }
-    fold_kblock_q2<true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fsc[i & 1]);
+    fold_kblock_q2<true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fblk[i & 1]);
     if (i + 1 < nk) {
-      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fsc[(i + 1) & 1]);
+      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fblk[(i + 1) & 1]);
       relayout256(w1, dst, lane);
     }
     w0 = w1;
@@ -1191,35 +1210,43 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 #define SMOE_PF_DN_KT 512  // K block of the down GEMM
 #endif
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  const int max_union = a.E < a.T * a.k ? a.E : a.T * a.k;
+// Launch on s, bracketed by start/stop events when ev0 is not null.
+#define SMOE_PF_LAUNCH(K, GRID, BLOCK, S, EV0, EV1, ...)                                      \
+  do {                                                                                     \
+    if (EV0) hipExtLaunchKernelGGL(K, GRID, BLOCK, 0, S, EV0, EV1, 0, __VA_ARGS__);           \
+    else hipLaunchKernelGGL(K, GRID, BLOCK, 0, S, __VA_ARGS__);                              \
+  } while (0)
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, const hipEvent_t* ev) {
+  // events 0/1 bracket the gate/up GEMM, 2/3 the down GEMM
+  const hipEvent_t g0 = ev ? ev[0] : nullptr, g1 = ev ? ev[1] : nullptr;
+  const hipEvent_t d0 = ev ? ev[2] : nullptr, d1 = ev ? ev[3] : nullptr;
   hipLaunchKernelGGL(prefill_union_kernel, dim3(1), dim3(1024), 0, s, a);
   const int ms = prefill_max_slices(a.T, a.k, a.E);
-  (void)max_union;
   const dim3 gu(a.f / 64, ms), dn(a.d / 64, ms);
   // K blocks of 256 codes for gate/up (two matrices in registers), 512 for
   // down, when K allows (runs of 128 / 256 bytes per row); else 128
   constexpr int GKT = SMOE_PF_GU_KT, DKT = SMOE_PF_DN_KT;
   if (a.bits == 2) {  // SMOE-Q2 (chunk 64, d_model a multiple of 512): folded per chunk in K
     // blocks of 512; a d_ff that is not a multiple of 512 takes the fp16-dequant down GEMM
-    hipLaunchKernelGGL(prefill_gate_up_fold_q2_kernel, gu, dim3(256), 0, s, a);
-    if (a.f % 512 == 0) hipLaunchKernelGGL(prefill_down_fold_q2_kernel, dn, dim3(256), 0, s, a);
-    else if (a.f % 256 == 0) hipLaunchKernelGGL((prefill_down_kernel<64, 256, 2>), dn, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_down_kernel<64, 128, 2>), dn, dim3(256), 0, s, a);
+    SMOE_PF_LAUNCH(prefill_gate_up_fold_q2_kernel, gu, dim3(256), s, g0, g1, a);
+    if (a.f % 512 == 0) SMOE_PF_LAUNCH(prefill_down_fold_q2_kernel, dn, dim3(256), s, d0, d1, a);
+    else if (a.f % 256 == 0) SMOE_PF_LAUNCH((prefill_down_kernel<64, 256, 2>), dn, dim3(256), s, d0, d1, a);
+    else SMOE_PF_LAUNCH((prefill_down_kernel<64, 128, 2>), dn, dim3(256), s, d0, d1, a);
   } else if (a.chunk == 64 && a.d % 256 == 0 && a.f % 256 == 0) {  // affine folded per chunk
-    hipLaunchKernelGGL((prefill_gate_up_fold_kernel<256>), gu, dim3(256), 0, s, a);
+    SMOE_PF_LAUNCH((prefill_gate_up_fold_kernel<256>), gu, dim3(256), s, g0, g1, a);
     // K blocks of 256 for the down GEMM too (512 measured slower)
-    hipLaunchKernelGGL((prefill_down_fold_kernel<256>), dn, dim3(256), 0, s, a);
+    SMOE_PF_LAUNCH((prefill_down_fold_kernel<256>), dn, dim3(256), s, d0, d1, a);
   } else if (a.chunk == 64) {
-    if (a.d % GKT == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<64, GKT>), gu, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_gate_up_kernel<64, 128>), gu, dim3(256), 0, s, a);
-    if (a.f % DKT == 0) hipLaunchKernelGGL((prefill_down_kernel<64, DKT>), dn, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_down_kernel<64, 128>), dn, dim3(256), 0, s, a);
+    if (a.d % GKT == 0) SMOE_PF_LAUNCH((prefill_gate_up_kernel<64, GKT>), gu, dim3(256), s, g0, g1, a);
+    else SMOE_PF_LAUNCH((prefill_gate_up_kernel<64, 128>), gu, dim3(256), s, g0, g1, a);
+    if (a.f % DKT == 0) SMOE_PF_LAUNCH((prefill_down_kernel<64, DKT>), dn, dim3(256), s, d0, d1, a);
+    else SMOE_PF_LAUNCH((prefill_down_kernel<64, 128>), dn, dim3(256), s, d0, d1, a);
   } else {
-    if (a.d % GKT == 0) hipLaunchKernelGGL((prefill_gate_up_kernel<32, GKT>), gu, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_gate_up_kernel<32, 128>), gu, dim3(256), 0, s, a);
-    if (a.f % DKT == 0) hipLaunchKernelGGL((prefill_down_kernel<32, DKT>), dn, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_down_kernel<32, 128>), dn, dim3(256), 0, s, a);
+    if (a.d % GKT == 0) SMOE_PF_LAUNCH((prefill_gate_up_kernel<32, GKT>), gu, dim3(256), s, g0, g1, a);
+    else SMOE_PF_LAUNCH((prefill_gate_up_kernel<32, 128>), gu, dim3(256), s, g0, g1, a);
+    if (a.f % DKT == 0) SMOE_PF_LAUNCH((prefill_down_kernel<32, DKT>), dn, dim3(256), s, d0, d1, a);
+    else SMOE_PF_LAUNCH((prefill_down_kernel<32, 128>), dn, dim3(256), s, d0, d1, a);
   }
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((a.d + 255) / 256, a.T), dim3(256), 0, s, a);
   return hipGetLastError();
