@@ -744,14 +744,29 @@ def bench_ring_prefill(args):
     perm = torch.empty(C * k, dtype=torch.int32, device="cuda")
     table = torch.empty(E, dtype=torch.int64, device="cuda")
     unions = []
+    # per chunk-layer timing of the last timed prompt (chunk order): routing
+    # (compute stream), the host side of the routed acquisition, and the span
+    # of that acquisition's fills on the copy stream
+    timing = {"on": False, "ev": [], "host_s": []}
 
     def chunk_layer(c, L):
         r = resid[c * C:(c + 1) * C]
         r.copy_(prompt[c * C:(c + 1) * C])
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timing["on"] else None
+        if ev:
+            ev[0].record()
         smoe.route(dims, r, x, router[L], bias[L], idx, w, ws)
+        if ev:
+            ev[1].record()
+            ev[2].record(copy_stream)
+        t0 = time.perf_counter()
         # the library reads the routing back, forms the union in first-touch
         # order and acquires it (fills in that order), then writes the table
         unions.append(len(ring.acquire_routed(L, idx, table)))
+        if ev:
+            timing["host_s"].append(time.perf_counter() - t0)
+            ev[3].record(copy_stream)
+            timing["ev"].append(ev)
         smoe.moe_prefill_chunk(dims, x, idx, w, table, r, uids, ucount, offs, perm, ws)
 
     def prompt_run(tag, order):
@@ -778,7 +793,9 @@ def bench_ring_prefill(args):
         n_u0 = len(unions)
         t1 = time.time()
         for i in range(K):
+            timing["on"] = order == "chunk" and i == K - 1
             prompt_run(f"{order}-order timed prompt {i + 1}", order)
+        timing["on"] = False
         torch.cuda.synchronize()
         dt = time.time() - t1
         s1 = ring.stats()
@@ -792,6 +809,24 @@ def bench_ring_prefill(args):
             f"{res[order]['hit_rate']:.3f}, H2D {res[order]['h2d_gbps']:.1f} GB/s")
     ring.release()
     ring.destroy()
+    # first-touch firing: how much a fill could start earlier if it fired as
+    # soon as its first token was routed, against how long the fills take
+    route_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in timing["ev"]])
+    fill_us = np.array([e[2].elapsed_time(e[3]) * 1e3 for e in timing["ev"]])
+    host_us = np.array(timing["host_s"]) * 1e6
+    per_cl_us = res["chunk"]["ms"] * 1e3 / (n_chunks * NL)
+    with_fills = fill_us > 1.0
+    f1 = {"chunk_layers": int(len(route_us)), "route_us_mean": float(route_us.mean()),
+          "acquire_host_us_mean": float(host_us.mean()),
+          "fill_span_us_mean_when_missing": float(fill_us[with_fills].mean()) if with_fills.any() else 0.0,
+          "chunk_layers_with_fills": int(with_fills.sum()), "chunk_layer_us_mean": per_cl_us,
+          "max_gain_frac_of_prompt": float(route_us.sum() / (per_cl_us * len(route_us))),
+          "note": "all tokens of a chunk are routed by one batch of kernels, so firing a fill at its first "
+                  "token's routing could start it at most the routing time earlier; max_gain_frac_of_prompt "
+                  "is that bound over the prompt time"}
+    log(f"first-touch firing bound: routing {f1['route_us_mean']:.1f} us per chunk-layer, fills "
+        f"{f1['fill_span_us_mean_when_missing']:.0f} us when missing, at most "
+        f"{100 * f1['max_gain_frac_of_prompt']:.2f}% of the prompt time")
     f = res["chunk"]
     out = {
         "metric": "ring-backed layer-major prefill prompt tokens/s (235B-shape, 512-token prompt, chunks of 64, "
@@ -808,6 +843,7 @@ def bench_ring_prefill(args):
         "vault_layers_page_locked": n_pinned,
         "host_link": dict(link, h2d_frac_of_pinned=f["h2d_frac_of_pinned"]),
         "layer_outer": res["layer"],
+        "first_touch_firing": f1,
     }
     del views
     for v in vault:
