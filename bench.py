@@ -11,7 +11,9 @@ replayed; the step's input copy runs eagerly inside the timed region.  The
 line also carries ``prefill``: the prefill workload (a 512-token prompt in
 chunks of 64, Zipf(1.1)-biased routing) on the same stack (same experts and
 routers), with its own roofline (union bytes over grouped-GEMM time), MFMA
-utilisation and oracle baseline.
+utilisation and oracle baseline.  Prefill keeps four chunks in flight on four
+streams, each one layer behind the previous and waiting for it layer by layer
+(``--chunks-in-flight``; the one-chunk time is reported beside it).
 
 Other workloads (one JSON line each): ``--workload prefill`` -- a 512-token
 prompt in chunks of 64 through the same 94 layers, layer-major, Zipf-biased
@@ -322,6 +324,7 @@ def bench_decode(args):
         bias = torch.from_numpy(np.stack([synth.zipf_bias(pwl.seed, dims, L, pwl.zipf_s)
                                           for L in range(pwl.n_layers)])).cuda()
         out["prefill"] = measure_prefill(stack, pwl, pwl.n_layers, bias, args.prefill_steps, 1, chained=False,
+                                         lanes=args.chunks_in_flight,
                                          cpu_budget=None if args.no_cpu_baseline else args.prefill_cpu_budget)
     print(json.dumps(out), flush=True)
 
@@ -403,7 +406,8 @@ def prefill_cpu_baseline(stack, wl, bias_np, prompt_np, budget_s=10.0):
                       f"prompt tokens/s = 1 / (per token x {wl.n_layers} layers)"}
 
 
-def measure_prefill(stack, wl, NL, bias, steps, warmup, chained=True, instrument_chunks=2, cpu_budget=None):
+def measure_prefill(stack, wl, NL, bias, steps, warmup, chained=True, instrument_chunks=2, cpu_budget=None,
+                    lanes=1, graph=True):
     """Layer-major prefill of the workload's prompt in chunks through NL layers
     of ``stack`` (router logits biased by ``bias`` [NL][E]): for each chunk and
     layer, route the chunk, build the expert union, run the grouped expert FFN
@@ -417,6 +421,13 @@ def measure_prefill(stack, wl, NL, bias, steps, warmup, chained=True, instrument
     to one common direction within ~10 layers and every token then routes
     alike, so the unions collapse.
 
+    ``lanes`` > 1 keeps that many chunks in flight on as many streams: chunk c
+    runs on stream c % lanes, one layer behind chunk c - 1, and its layer L
+    waits for chunk c - 1's layer L (the order a causal model needs: a
+    chunk's layer reads the earlier chunks' output of that layer).  One
+    chunk's latency-bound routing and union kernels then overlap another's
+    grouped GEMMs.  Each stream has its own routing buffers and workspace.
+
     Kernel timing: the first ``instrument_chunks`` chunks through all NL layers
     are run eagerly with start/stop events around the two grouped GEMMs (the
     queue pre-filled by a spin kernel); the roofline is union bytes over GEMM
@@ -428,42 +439,89 @@ def measure_prefill(stack, wl, NL, bias, steps, warmup, chained=True, instrument
     prompt = torch.from_numpy(prompt_np).cuda()
     resid = torch.empty_like(prompt)
     mu = min(dims.n_experts, C * dims.top_k)
-    x = torch.empty((C, dims.d_model), dtype=torch.int16, device="cuda")
-    idx = torch.empty((C, dims.top_k), dtype=torch.int32, device="cuda")
-    w = torch.empty((C, dims.top_k), dtype=torch.float32, device="cuda")
-    ucount = {m: torch.zeros((n_chunks, NL), dtype=torch.int32, device="cuda") for m in ("fresh", "chained", "ev")}
-    uids = torch.empty(mu, dtype=torch.int32, device="cuda")
-    offs = torch.empty(mu + 1, dtype=torch.int32, device="cuda")
-    perm = torch.empty(C * dims.top_k, dtype=torch.int32, device="cuda")
-    ws = smoe.workspace(dims, C)
+    ucount = {m: torch.zeros((n_chunks, NL), dtype=torch.int32, device="cuda")
+              for m in ("fresh", "chained", "fresh_one_lane", "ev")}
+
+    def lane_buffers():
+        return {"x": torch.empty((C, dims.d_model), dtype=torch.int16, device="cuda"),
+                "idx": torch.empty((C, dims.top_k), dtype=torch.int32, device="cuda"),
+                "w": torch.empty((C, dims.top_k), dtype=torch.float32, device="cuda"),
+                "uids": torch.empty(mu, dtype=torch.int32, device="cuda"),
+                "offs": torch.empty(mu + 1, dtype=torch.int32, device="cuda"),
+                "perm": torch.empty(C * dims.top_k, dtype=torch.int32, device="cuda"),
+                "ws": smoe.workspace(dims, C)}
+
+    lanes = max(1, min(int(lanes), n_chunks))
+    bufs = [lane_buffers() for _ in range(lanes)]
+    streams = [None] + [torch.cuda.Stream() for _ in range(lanes - 1)]  # default priority
 
     def layer(L, c, r, uc, events=None):
-        smoe.route(dims, r, x, stack.router_layer(L), bias[L], idx, w, ws)
-        smoe.moe_prefill_chunk(dims, x, idx, w, stack.table(L), r, uids, uc[c, L:L + 1], offs, perm, ws,
-                               events=events)
+        b = bufs[c % lanes]
+        smoe.route(dims, r, b["x"], stack.router_layer(L), bias[L], b["idx"], b["w"], b["ws"])
+        smoe.moe_prefill_chunk(dims, b["x"], b["idx"], b["w"], stack.table(L), r, b["uids"], uc[c, L:L + 1],
+                               b["offs"], b["perm"], b["ws"], events=events)
+
+    done = [[torch.cuda.Event() for _ in range(NL)] for _ in range(lanes)] if lanes > 1 else None
+
+    def run_prompt(fresh, uc, nl):
+        # groups of nl chunks; within a group chunk c0 + j is j layers behind
+        # chunk c0 and waits for chunk c0 + j - 1 to finish each layer
+        main = torch.cuda.current_stream()
+        for st in streams[1:nl]:
+            st.wait_stream(main)
+        for c0 in range(0, n_chunks, nl):
+            nc = min(nl, n_chunks - c0)
+            for step in range(NL + nc - 1):
+                for j in range(nc):
+                    L, c = step - j, c0 + j
+                    if not 0 <= L < NL:
+                        continue
+                    st = streams[j] or main
+                    with torch.cuda.stream(st):
+                        if j > 0:
+                            st.wait_event(done[j - 1][L])
+                        r = resid[c * C:(c + 1) * C]
+                        if fresh:
+                            r.copy_(prompt[c * C:(c + 1) * C])
+                        layer(L, c, r, uc)
+                        if done is not None and j + 1 < nc:
+                            done[j][L].record(st)
+            for st in streams[1:nl]:  # the next group starts after this one
+                main.wait_stream(st)
 
     def prompt_fresh():
-        for c in range(n_chunks):
-            r = resid[c * C:(c + 1) * C]
-            for L in range(NL):
-                r.copy_(prompt[c * C:(c + 1) * C])
-                layer(L, c, r, ucount["fresh"])
+        run_prompt(True, ucount["fresh"], lanes)
 
     def prompt_chained():
         resid.copy_(prompt)
-        for c in range(n_chunks):
-            r = resid[c * C:(c + 1) * C]
-            for L in range(NL):
-                layer(L, c, r, ucount["chained"])
+        run_prompt(False, ucount["chained"], lanes)
+
+    def prompt_fresh_one_lane():
+        run_prompt(True, ucount["fresh_one_lane"], 1)
 
     off = synth.blob_sections(dims)
     gate_up_bytes = (off["down_codes"] - off["gate_codes"]) + (off["down_params"] - off["gate_params"])
     down_bytes = off["bytes"] - gate_up_bytes
     flops_per_prompt = 6.0 * dims.d_model * dims.d_ff * dims.top_k * NL * T
     res = {}
-    for mode, fn in (("fresh", prompt_fresh), ("chained", prompt_chained)) if chained else (("fresh", prompt_fresh),):
-        g = graph_of(fn)
-        ms = time_replays(g, warmup, steps)
+    readings = [("fresh", prompt_fresh)] + ([("chained", prompt_chained)] if chained else []) + \
+        ([("fresh_one_lane", prompt_fresh_one_lane)] if lanes > 1 else [])
+    for mode, fn in readings:
+        if graph:
+            g = graph_of(fn)
+            ms = time_replays(g, warmup, steps)
+        else:  # eager launches (the streams of the lanes run as the host issues them)
+            g = None
+            for _ in range(max(1, warmup)):
+                fn()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / steps
         u = ucount[mode].cpu().numpy()
         ub = int(u.sum()) * off["bytes"]
         res[mode] = {"ms": ms, "tok_s": T / (ms / 1e3), "mean_union": float(u.mean()),
@@ -515,9 +573,13 @@ def measure_prefill(stack, wl, NL, bias, steps, warmup, chained=True, instrument
                      "both_gemms": {"achieved": gemm_gbps, "frac": gemm_gbps / HBM_PEAK_GBPS,
                                     "mfma_utilisation": mfma_gemm}},
     }
+    out["config"]["chunks_in_flight"] = lanes
     if chained:
         out["chained"] = {k: res["chained"][k] for k in ("tok_s", "ms", "mean_union", "union_gbps",
                                                          "mfma_utilisation")}
+    if lanes > 1:
+        out["one_chunk_in_flight"] = {k: res["fresh_one_lane"][k] for k in ("tok_s", "ms", "union_gbps",
+                                                                            "mfma_utilisation")}
     if cpu_budget:
         log("cpu baseline (oracle, prefill) ...")
         out["cpu_baseline"] = prefill_cpu_baseline(stack, wl, bias.cpu().numpy(), prompt_np, cpu_budget)
@@ -534,7 +596,7 @@ def bench_prefill(args):
     stack = DeviceStack(wl.seed, dims, NL, zipf_s=wl.zipf_s)
     torch.cuda.synchronize()
     log(f"stack ready: vault {stack.vault.numel() / 1e9:.2f} GB")
-    p = measure_prefill(stack, wl, NL, stack.bias, args.steps, args.warmup,
+    p = measure_prefill(stack, wl, NL, stack.bias, args.steps, args.warmup, lanes=args.chunks_in_flight,
                         cpu_budget=None if args.no_cpu_baseline else args.cpu_budget)
     out = {
         "metric": "layer-major prefill prompt tokens/s + GB/s on union expert bytes (235B-shape, 512-token "
@@ -925,6 +987,8 @@ def main():
                     help="decode workload: skip the prefill sub-object (the 512-token prompt on the same stack)")
     ap.add_argument("--prefill-steps", type=int, default=3, help="decode workload: timed prompts of the prefill "
                                                                  "sub-object")
+    ap.add_argument("--chunks-in-flight", type=int, default=4,
+                    help="prefill: chunks kept in flight on as many streams (a causal pipeline, one layer apart)")
     ap.add_argument("--prefill-cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the prefill sub-object's CPU baseline")
     args = ap.parse_args()
