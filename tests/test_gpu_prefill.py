@@ -218,3 +218,64 @@ def test_prefill_repeated_expert_in_a_token():
     refs = oracle_mix(res, idx, w, LazyExperts(1337, dims, 0), dims)
     for t in range(T):
         check_moe_output(got["r_out"][t].astype(np.float64) - res[t], refs[t], f"repeat t{t}")
+
+
+def test_prefill_chunks_on_concurrent_streams_match_one_stream():
+    """Three 64-token chunks through three chained layers of the 235B shape,
+    once one chunk after another on one stream, once as a causal pipeline on
+    three streams (chunk c one layer behind chunk c - 1 and waiting for its
+    layer, each stream with its own buffers and workspace: the schedule the
+    benchmark runs).  The library keeps no state between calls, so the
+    residuals must be bitwise equal."""
+    dims = SHAPES["q235b"]
+    NL, C, n_chunks = 3, 64, 3
+    stack = DeviceStack(synth.SEED, dims, NL, zipf_s=1.1)
+    say(f"concurrent prefill streams: {n_chunks} chunks x {NL} layers, dims {vars(dims)}")
+    prompt = torch.from_numpy(np.stack([synth.hidden_bf16(synth.SEED, 30_000 + t, dims.d_model)
+                                        for t in range(C * n_chunks)])).cuda()
+    mu = min(dims.n_experts, C * dims.top_k)
+
+    def buffers():
+        return dict(x=torch.empty((C, dims.d_model), dtype=torch.int16, device="cuda"),
+                    idx=torch.empty((C, dims.top_k), dtype=torch.int32, device="cuda"),
+                    w=torch.empty((C, dims.top_k), dtype=torch.float32, device="cuda"),
+                    uids=torch.empty(mu, dtype=torch.int32, device="cuda"),
+                    uc=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                    offs=torch.empty(mu + 1, dtype=torch.int32, device="cuda"),
+                    perm=torch.empty(C * dims.top_k, dtype=torch.int32, device="cuda"),
+                    ws=smoe.workspace(dims, C))
+
+    def chunk_layer(b, r, L):
+        smoe.route(dims, r, b["x"], stack.router_layer(L), stack.bias_layer(L), b["idx"], b["w"], b["ws"])
+        smoe.moe_prefill_chunk(dims, b["x"], b["idx"], b["w"], stack.table(L), r, b["uids"], b["uc"], b["offs"],
+                               b["perm"], b["ws"])
+
+    seq = prompt.clone()
+    b0 = buffers()
+    for c in range(n_chunks):
+        for L in range(NL):
+            chunk_layer(b0, seq[c * C:(c + 1) * C], L)
+    torch.cuda.synchronize()
+
+    par = prompt.clone()
+    bufs = [buffers() for _ in range(n_chunks)]
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(n_chunks - 1)]
+    done = [[torch.cuda.Event() for _ in range(NL)] for _ in range(n_chunks)]
+    for st in streams[1:]:
+        st.wait_stream(main)
+    for step in range(NL + n_chunks - 1):
+        for c in range(n_chunks):
+            L = step - c
+            if not 0 <= L < NL:
+                continue
+            with torch.cuda.stream(streams[c]):
+                if c > 0:
+                    streams[c].wait_event(done[c - 1][L])
+                chunk_layer(bufs[c], par[c * C:(c + 1) * C], L)
+                done[c][L].record(streams[c])
+    for st in streams[1:]:
+        main.wait_stream(st)
+    torch.cuda.synchronize()
+    assert torch.equal(seq, par)
+    assert torch.isfinite(seq).all()
