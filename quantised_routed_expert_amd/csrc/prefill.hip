@@ -834,8 +834,6 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_fold_kernel(PrefillArg
   __syncthreads();
   xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
   xr.store(xs[0], xsum[0]);
-  relayout256(g0, gst, lane);
-  relayout256(u0, ust, lane);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {  // rows first, then weights, of block i + 1
@@ -843,13 +841,13 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_fold_kernel(PrefillArg
       load_lines256(g1, gc0, row_bytes, gp, (i + 1) * KT, lane);
       load_lines256(u1, uc0, row_bytes, up, (i + 1) * KT, lane);
     }
+    // block i's weights were loaded one iteration ago: re-laid only now, so
+    // that their loads have a whole iteration to land
+    relayout256(g0, gst, lane);
+    relayout256(u0, ust, lane);
     fold_kblock<KT>(ag, g0, xs[i & 1], xsum[i & 1], lane);
     fold_kblock<KT>(au, u0, xs[i & 1], xsum[i & 1], lane);
-    if (i + 1 < nk) {
-      xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
-      relayout256(g1, gst, lane);
-      relayout256(u1, ust, lane);
-    }
+    if (i + 1 < nk) xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
     g0 = g1;
     u0 = u1;
     __syncthreads();
@@ -896,18 +894,15 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   __syncthreads();
   hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0, a.Hs, tiles);
   hr.store(xs[0], xsum[0], fblk[0]);
-  wlay(w0);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
       hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT, a.Hs, tiles);
       wload(w1, (i + 1) * KT);
     }
+    wlay(w0);  // block i, loaded one iteration ago
     fold_kblock<KT, true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fblk[i & 1]);
-    if (i + 1 < nk) {
-      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fblk[(i + 1) & 1]);
-      wlay(w1);
-    }
+    if (i + 1 < nk) hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fblk[(i + 1) & 1]);
     w0 = w1;
     __syncthreads();
   }
@@ -1114,8 +1109,6 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_fold_q2_kernel(Prefill
   __syncthreads();
   xr.load(a.x, (size_t)a.d, rows, n_rows, 0);
   xr.store(xs[0], xsum[0]);
-  relayout256(g0, gst, lane);
-  relayout256(u0, ust, lane);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
@@ -1123,13 +1116,11 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_fold_q2_kernel(Prefill
       load_lines_q2(g1, gc0, row_bytes, gp, (i + 1) * KT, lane);
       load_lines_q2(u1, uc0, row_bytes, up, (i + 1) * KT, lane);
     }
+    relayout256(g0, gst, lane);  // block i, loaded one iteration ago
+    relayout256(u0, ust, lane);
     fold_kblock_q2(ag, g0, xs[i & 1], xsum[i & 1], lane);
     fold_kblock_q2(au, u0, xs[i & 1], xsum[i & 1], lane);
-    if (i + 1 < nk) {
-      xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
-      relayout256(g1, gst, lane);
-      relayout256(u1, ust, lane);
-    }
+    if (i + 1 < nk) xr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1]);
     g0 = g1;
     u0 = u1;
     __syncthreads();
@@ -1165,18 +1156,15 @@ __global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a
   __syncthreads();
   hr.load(a.H, (size_t)a.f, rows, n_rows, 0, a.Hs, tiles);
   hr.store(xs[0], xsum[0], fblk[0]);
-  relayout256(w0, dst, lane);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
       hr.load(a.H, (size_t)a.f, rows, n_rows, (i + 1) * KT, a.Hs, tiles);
       load_lines_q2(w1, dc0, row_bytes, dp, (i + 1) * KT, lane);
     }
+    relayout256(w0, dst, lane);  // block i, loaded one iteration ago
     fold_kblock_q2<true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fblk[i & 1]);
-    if (i + 1 < nk) {
-      hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fblk[(i + 1) & 1]);
-      relayout256(w1, dst, lane);
-    }
+    if (i + 1 < nk) hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fblk[(i + 1) & 1]);
     w0 = w1;
     __syncthreads();
   }
