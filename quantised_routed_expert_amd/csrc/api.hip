@@ -56,7 +56,7 @@ int check_dims(const smoe_dims* d) {
 
 // Workspace carve-up (offsets from the workspace base, 256-byte aligned).
 struct Workspace {
-  size_t logits, plog, idx, w, ptr, x, px, h, ph, phs, py, pinv, slices, recs, end;
+  size_t logits, plog, idx, w, ptr, x, px, h, ph, phs, py, pxa, pxas, pinv, slices, recs, end;
 };
 
 Workspace ws_layout(const smoe_dims* d, int max_tokens) {
@@ -75,6 +75,8 @@ Workspace ws_layout(const smoe_dims* d, int max_tokens) {
   w.ph = o;     o = align_up(o + T * k * F * 2, 256);
   w.phs = o;    o = align_up(o + T * k * (F / 64) * 4, 256);
   w.py = o;     o = align_up(o + T * k * D * 4, 256);
+  w.pxa = o;    o = align_up(o + T * D * 2, 256);
+  w.pxas = o;   o = align_up(o + T * (D / 64) * 4, 256);
   w.pinv = o;   o = align_up(o + T * k * 4, 256);
   w.slices = o; o = align_up(o + ((T * k + 15) / 16 + (E < T * k ? E : T * k) + 1) * 4, 256);
   w.recs = o;   o = align_up(o + ((T * k + 15) / 16 + (E < T * k ? E : T * k)) * 16, 256);
@@ -387,6 +389,8 @@ int smoe_moe_prefill_chunk(const smoe_dims* d, int32_t n_tok, const uint16_t* x,
   a.H = reinterpret_cast<_Float16*>(base + L.ph);
   a.Hs = reinterpret_cast<float*>(base + L.phs);
   a.Y = reinterpret_cast<float*>(base + L.py);
+  a.xa = reinterpret_cast<_Float16*>(base + L.pxa);
+  a.xas = reinterpret_cast<float*>(base + L.pxas);
   a.T = n_tok;
   a.d = d->d_model;
   a.f = d->d_ff;

@@ -28,6 +28,9 @@ struct PrefillArgs {
                               // row's 64-feature tile scaled by a power of two
   float* Hs;                  // [T*k][f / 64] inverse scale of each tile: H = fp16 * Hs
   float* Y;                   // [T*k][d] per-entry expert outputs
+  _Float16* xa;               // [T][d] the chunk's x as the folded gate/up GEMM's A operand: fp16
+                              // in pair order (groups of 8: e_p, e_{p+4}), odd dwords divided by 16
+  float* xas;                 // [T][d / 64] sum of each chunk of 64 x values (before the division)
   int T, d, f, E, k, chunk;
   int bits;                   // code width: 4 (SMOE-Q4) or 2 (SMOE-Q2)
   BlobLayout lay;

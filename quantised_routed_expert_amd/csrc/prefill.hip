@@ -621,87 +621,129 @@ __device__ __forceinline__ half8_t codes8(uint32_t w) {
   return __builtin_bit_cast(half8_t, r);
 }
 
-// A slice's 16 token rows for one K block as fp16 in pair order, the odd
-// elements divided by 16, and the sum of each row's fp16 values over each
-// chunk of 64 (xsum[chunk of the block][row]).  Thread (r = tid / 16, c =
-// tid % 16) moves KT / 16 consecutive values of row r; load() and store() are
-// separate so that the loads run a block ahead.  H rows come with one scale
-// per 64-value tile: the block's tiles are put on one common scale per row
-// (the largest tile scale F of the block, a power of two; a tile's values are
-// multiplied by its scale / F <= 1, exactly unless they fall below the fp16
-// normal range, where they are at most 2^-24 of the block's largest), and F
-// goes to fblk[row], by which the caller multiplies the block's result.
-template <bool FROM_BF16, int KT>
+// A slice's 16 H rows (the down GEMM's A operand) for one K block, as fp16
+// in pair order with the odd elements divided by 16, and the sum of each
+// row's fp16 values over each chunk of 64 (xsum[chunk of the block][row]).
+// Thread (r = tid / 16, k = tid % 16) moves pieces 16 j + k of row r (the
+// 16 threads of a row read 256 contiguous bytes per load instruction);
+// load() and store() are separate so that the loads run a block ahead.  H
+// comes with one scale per 64-value tile: the block's tiles are put on one
+// common scale per row (the largest tile scale F of the block, a power of
+// two; a tile's values are multiplied by its scale / F <= 1, exactly unless
+// they fall below the fp16 normal range, where they are at most 2^-24 of the
+// block's largest), and F goes to fblk[row], by which the caller multiplies
+// the block's result.
+template <int KT>
 struct FoldStage {
   static constexpr int V = KT / 128;  // 16-byte pieces (8 values) per thread
   uint4 v[V];
-  float fs[V];                        // H rows: the tile scale of each piece
+  float fs[V];                        // the tile scale of each piece
 
-  // thread (r, k) takes pieces 16 j + k of row r: the 16 threads of a row
-  // read 256 contiguous bytes per load instruction.  For H rows each thread
-  // also loads the tile scales of its pieces (hs, tiles).
-  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb,
-                                       const float* hs = nullptr, int tiles = 0) {
+  __device__ __forceinline__ void load(const _Float16* src, size_t row_elems, const int* rows, int n_rows, int kb,
+                                       const float* hs, int tiles) {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       v[j] = make_uint4(0, 0, 0, 0);
-      if (r < n_rows)
-        v[j] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb + 8 * (16 * j + k));
       fs[j] = 1.0f;
-      if (!FROM_BF16 && r < n_rows) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 2 * j + (k >> 3)];
+      if (r < n_rows) {
+        v[j] = gload16(src + (size_t)rows[r] * row_elems + kb + 8 * (16 * j + k));
+        fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 2 * j + (k >> 3)];
+      }
     }
   }
 
-  // fblk (H rows only): [row] the block's common scale
-  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16], float* fblk = nullptr) const {
+  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16], float* fblk) const {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
     const uint32_t k16 = 0x2C002C00u;  // (1/16, 1/16) in fp16
-    float fb = 1.0f;
-    if (!FROM_BF16) {
-      float m = fs[0];
+    float m = fs[0];
 #pragma unroll
-      for (int j = 1; j < V; ++j) m = fmaxf(m, fs[j]);
-      fb = row_max16(m);
-      if (k == 0) fblk[r] = fb;
-    }
+    for (int j = 1; j < V; ++j) m = fmaxf(m, fs[j]);
+    const float fb = row_max16(m);
+    if (k == 0) fblk[r] = fb;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      uint4 o;
+      const _Float16 rh = (_Float16)(fs[j] / fb);  // a power of two <= 1 (0 below fp16's range)
+      const h2_t ratio = {rh, rh};
+      const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      h2_t hv[4];
       float part = 0.f;
-      if (FROM_BF16) {  // bf16 in natural order -> fp16 pairs (e_p, e_{p+4})
-        const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        float f[8];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          f[2 * p] = (float)(_Float16)bf16_to_f32(w4[p] & 0xFFFF);
-          f[2 * p + 1] = (float)(_Float16)bf16_to_f32(w4[p] >> 16);
-        }
-#pragma unroll
-        for (int p = 0; p < 8; ++p) part += f[p];
-        o.x = f16_bits(f[0]) | (f16_bits(f[4]) << 16);
-        o.y = f16_bits(f[1] * 0.0625f) | (f16_bits(f[5] * 0.0625f) << 16);
-        o.z = f16_bits(f[2]) | (f16_bits(f[6]) << 16);
-        o.w = f16_bits(f[3] * 0.0625f) | (f16_bits(f[7] * 0.0625f) << 16);
-      } else {  // fp16 in pair order (H): onto the common scale, dwords 1 and 3 divided by 16
-        const _Float16 rh = (_Float16)(fs[j] / fb);  // a power of two <= 1 (0 below fp16's range)
-        const h2_t ratio = {rh, rh};
-        const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        h2_t hv[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          hv[p] = as_h2(w4[p]) * ratio;
-          part += (float)hv[p][0] + (float)hv[p][1];
-        }
-        o.x = __builtin_bit_cast(uint32_t, hv[0]);
-        o.y = __builtin_bit_cast(uint32_t, hv[1] * as_h2(k16));
-        o.z = __builtin_bit_cast(uint32_t, hv[2]);
-        o.w = __builtin_bit_cast(uint32_t, hv[3] * as_h2(k16));
+      for (int p = 0; p < 4; ++p) {
+        hv[p] = as_h2(w4[p]) * ratio;
+        part += (float)hv[p][0] + (float)hv[p][1];
       }
+      uint4 o;
+      o.x = __builtin_bit_cast(uint32_t, hv[0]);
+      o.y = __builtin_bit_cast(uint32_t, hv[1] * as_h2(k16));
+      o.z = __builtin_bit_cast(uint32_t, hv[2]);
+      o.w = __builtin_bit_cast(uint32_t, hv[3] * as_h2(k16));
       *reinterpret_cast<uint4*>(&xs[r][8 * (16 * j + k)]) = o;
       // a chunk is 8 pieces: threads 8h .. 8h + 7 of the row (adjacent lanes)
       part = group_sum<8>(part);
       if ((k & 7) == 0) xsum[2 * j + (k >> 3)][r] = part;
+    }
+  }
+};
+
+// The chunk's x in the folded gate/up GEMM's A layout, once per call
+// (rather than once per slice and feature block): x_a[t][j] as fp16 in pair
+// order (dword p of each group of 8 holds e_p, e_{p+4}), the odd dwords
+// divided by 16, and x_as[t][c] the sum of chunk c's 64 fp16 values, in the
+// order the H stage sums its rows.  grid = (ceil(d / 2048), T), 256 threads;
+// thread i owns the 8 values 8 i .. 8 i + 7 of its 2048 (threads past d read
+// the row's first piece and store nothing; d is a multiple of 256, so they
+// make up whole chunks).
+__global__ __launch_bounds__(256) void prefill_stage_x_kernel(PrefillArgs a) {
+  const int t = blockIdx.y, piece = blockIdx.x * 256 + threadIdx.x;
+  const bool in = 8 * piece < a.d;
+  const uint4 v = gload16(a.x + (size_t)t * a.d + (in ? 8 * piece : 0));
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    f[2 * p] = (float)(_Float16)bf16_to_f32(w4[p] & 0xFFFF);
+    f[2 * p + 1] = (float)(_Float16)bf16_to_f32(w4[p] >> 16);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) part += f[p];
+  uint4 o;
+  o.x = f16_bits(f[0]) | (f16_bits(f[4]) << 16);
+  o.y = f16_bits(f[1] * 0.0625f) | (f16_bits(f[5] * 0.0625f) << 16);
+  o.z = f16_bits(f[2]) | (f16_bits(f[6]) << 16);
+  o.w = f16_bits(f[3] * 0.0625f) | (f16_bits(f[7] * 0.0625f) << 16);
+  if (in) *reinterpret_cast<uint4*>(a.xa + (size_t)t * a.d + 8 * piece) = o;
+  part = group_sum<8>(part);  // a chunk is 8 pieces: 8 adjacent lanes
+  if (in && (piece & 7) == 0) a.xas[(size_t)t * (a.d / 64) + piece / 8] = part;
+}
+
+// The token rows of a slice for one K block, copied from x_a / x_as (already
+// in the A layout) into the workgroup's stage: thread (r, k) moves pieces
+// 16 j + k of row r, and the first thread of each chunk its chunk sum.
+template <int KT>
+struct XCopyStage {
+  static constexpr int V = KT / 128;
+  uint4 v[V];
+  float sum[V];
+  __device__ __forceinline__ void load(const PrefillArgs& a, const int* rows, int n_rows, int kb) {
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      v[j] = make_uint4(0, 0, 0, 0);
+      sum[j] = 0.f;
+      if (r < n_rows) {
+        v[j] = gload16(a.xa + (size_t)rows[r] * a.d + kb + 8 * (16 * j + k));
+        if ((k & 7) == 0) sum[j] = a.xas[(size_t)rows[r] * (a.d / 64) + kb / 64 + 2 * j + (k >> 3)];
+      }
+    }
+  }
+  __device__ __forceinline__ void store(_Float16 (*xs)[KT + 8], float (*xsum)[16]) const {
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      *reinterpret_cast<uint4*>(&xs[r][8 * (16 * j + k)]) = v[j];
+      if ((k & 7) == 0) xsum[2 * j + (k >> 3)][r] = sum[j];
     }
   }
 };
@@ -821,7 +863,7 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_fold_kernel(PrefillArg
   const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
   const int nk = a.d / KT;
-  FoldStage<true, KT> xr;
+  XCopyStage<KT> xr;  // the token rows, staged once per call by prefill_stage_x_kernel
   FoldW<KT> g0, u0, g1, u1;
   const size_t nw0 = (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;  // the wave's first row
   const uint8_t* gc0 = blob + nw0;
@@ -832,12 +874,12 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_fold_kernel(PrefillArg
   load_lines256(u0, uc0, row_bytes, up, 0, lane);
   if (tid < si.n_rows) rows[tid] = a.perm[si.o + tid] / a.k;  // token of each entry
   __syncthreads();
-  xr.load(a.x, (size_t)a.d, rows, si.n_rows, 0);
+  xr.load(a, rows, si.n_rows, 0);
   xr.store(xs[0], xsum[0]);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {  // rows first, then weights, of block i + 1
-      xr.load(a.x, (size_t)a.d, rows, si.n_rows, (i + 1) * KT);
+      xr.load(a, rows, si.n_rows, (i + 1) * KT);
       load_lines256(g1, gc0, row_bytes, gp, (i + 1) * KT, lane);
       load_lines256(u1, uc0, row_bytes, up, (i + 1) * KT, lane);
     }
@@ -876,7 +918,7 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   const uint8_t* dp = blob + a.lay.down_params + (size_t)n0 * prow;
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   const int nk = a.f / KT;
-  FoldStage<false, KT> hr;
+  FoldStage<KT> hr;
   FoldW<KT> w0, w1;
   // KT == 256: line-wise weight loads re-laid through the wave's LDS stage
   const uint8_t* dc0 = blob + a.lay.down_codes + (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;
@@ -934,81 +976,54 @@ __device__ __forceinline__ half8_t codes8_q2(uint32_t w) {
   return __builtin_bit_cast(half8_t, r);
 }
 
-// A slice's 16 token rows for one K block of 512 as fp16 in the 16-group pair
-// order, the odd elements divided by 4, and each row's sum over each chunk of
-// 64 (xsum[chunk of the block][row]).  Thread (r = tid / 16, k = tid % 16)
-// takes the groups 16 j + k (two adjacent 16-byte pieces each) of row r; a
-// chunk's four groups sit in four adjacent lanes.
-template <bool FROM_BF16>
+// A slice's 16 H rows (the down GEMM's A operand) for one K block of 512 as
+// fp16 in the 16-group pair order, the odd elements divided by 4, and each
+// row's sum over each chunk of 64 (xsum[chunk of the block][row]).  Thread
+// (r = tid / 16, k = tid % 16) takes the groups 16 j + k (two adjacent
+// 16-byte pieces each) of row r; a chunk's four groups sit in four adjacent
+// lanes.  The block's tiles are put on one common scale per row, as for the
+// SMOE-Q4 H stage, and that scale goes to fblk[row].
 struct FoldStageQ2 {
   uint4 v[4];
-  float fs[2];  // H rows: the tile scale of each group pair's chunk (see FoldStage: one common scale per row)
+  float fs[2];  // the tile scale of each group pair's chunk
 
-  __device__ __forceinline__ void load(const void* src, size_t row_elems, const int* rows, int n_rows, int kb,
-                                       const float* hs = nullptr, int tiles = 0) {
+  __device__ __forceinline__ void load(const _Float16* src, size_t row_elems, const int* rows, int n_rows, int kb,
+                                       const float* hs, int tiles) {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[i] = make_uint4(0, 0, 0, 0);
-      if (r < n_rows)
-        v[i] = gload16(reinterpret_cast<const uint16_t*>(src) + (size_t)rows[r] * row_elems + kb +
-                       16 * (16 * (i >> 1) + k) + 8 * (i & 1));
+      if (r < n_rows) v[i] = gload16(src + (size_t)rows[r] * row_elems + kb + 16 * (16 * (i >> 1) + k) + 8 * (i & 1));
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       fs[j] = 1.0f;
-      if (!FROM_BF16 && r < n_rows) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 4 * j + (k >> 2)];
+      if (r < n_rows) fs[j] = hs[(size_t)rows[r] * tiles + kb / 64 + 4 * j + (k >> 2)];
     }
   }
 
-  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16], float* fblk = nullptr) const {
+  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16], float* fblk) const {
     const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
     const uint32_t k4 = 0x34003400u;  // (1/4, 1/4) in fp16
-    float fb = 1.0f;
-    if (!FROM_BF16) {
-      fb = row_max16(fmaxf(fs[0], fs[1]));
-      if (k == 0) fblk[r] = fb;
-    }
+    const float fb = row_max16(fmaxf(fs[0], fs[1]));
+    if (k == 0) fblk[r] = fb;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      uint4 o0, o1;
+      // onto the common scale, the odd dwords divided by 4
+      const _Float16 rh = (_Float16)(fs[j] / fb);  // a power of two <= 1 (0 below fp16's range)
+      const h2_t ratio = {rh, rh};
+      const uint32_t w8[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
+                              v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
+      uint32_t q[8];
       float part = 0.f;
-      if (FROM_BF16) {  // bf16 in natural order -> fp16 pairs (e_p, e_{p+8})
-        const uint32_t w8[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
-                                v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
-        float f[16];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          f[2 * p] = (float)(_Float16)bf16_to_f32(w8[p] & 0xFFFF);
-          f[2 * p + 1] = (float)(_Float16)bf16_to_f32(w8[p] >> 16);
-        }
-#pragma unroll
-        for (int p = 0; p < 16; ++p) part += f[p];
-        o0.x = f16_bits(f[0]) | (f16_bits(f[8]) << 16);
-        o0.y = f16_bits(f[1] * 0.25f) | (f16_bits(f[9] * 0.25f) << 16);
-        o0.z = f16_bits(f[2]) | (f16_bits(f[10]) << 16);
-        o0.w = f16_bits(f[3] * 0.25f) | (f16_bits(f[11] * 0.25f) << 16);
-        o1.x = f16_bits(f[4]) | (f16_bits(f[12]) << 16);
-        o1.y = f16_bits(f[5] * 0.25f) | (f16_bits(f[13] * 0.25f) << 16);
-        o1.z = f16_bits(f[6]) | (f16_bits(f[14]) << 16);
-        o1.w = f16_bits(f[7] * 0.25f) | (f16_bits(f[15] * 0.25f) << 16);
-      } else {  // fp16 in pair order (H): onto the common scale, the odd dwords divided by 4
-        const _Float16 rh = (_Float16)(fs[j] / fb);  // a power of two <= 1 (0 below fp16's range)
-        const h2_t ratio = {rh, rh};
-        const uint32_t w8[8] = {v[2 * j].x, v[2 * j].y, v[2 * j].z, v[2 * j].w,
-                                v[2 * j + 1].x, v[2 * j + 1].y, v[2 * j + 1].z, v[2 * j + 1].w};
-        uint32_t q[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const h2_t hv = as_h2(w8[p]) * ratio;
-          part += (float)hv[0] + (float)hv[1];
-          q[p] = __builtin_bit_cast(uint32_t, (p & 1) ? hv * as_h2(k4) : hv);
-        }
-        o0 = make_uint4(q[0], q[1], q[2], q[3]);
-        o1 = make_uint4(q[4], q[5], q[6], q[7]);
+      for (int p = 0; p < 8; ++p) {
+        const h2_t hv = as_h2(w8[p]) * ratio;
+        part += (float)hv[0] + (float)hv[1];
+        q[p] = __builtin_bit_cast(uint32_t, (p & 1) ? hv * as_h2(k4) : hv);
       }
-      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k)]) = o0;
-      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k) + 8]) = o1;
+      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k)]) = make_uint4(q[0], q[1], q[2], q[3]);
+      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k) + 8]) = make_uint4(q[4], q[5], q[6], q[7]);
       part = group_sum<4>(part);
       if ((k & 3) == 0) xsum[4 * j + (k >> 2)][r] = part;
     }
@@ -1018,6 +1033,72 @@ struct FoldStageQ2 {
 // One K block (512 codes) of one weight row per lane after the relayout:
 // pieces (= chunks) 4 q + g, and the (scale, min) words of the block's eight
 // chunks.
+// SMOE-Q2's A layout of the chunk's x, once per call: groups of 16 in pair
+// order (dword p holds e_p, e_{p+8}), the odd dwords divided by 4, and the
+// chunk sums, in the order the H stage forms them.  grid = (ceil(d / 4096), T), 256
+// threads; thread i owns the 16 values 16 i .. 16 i + 15 of its 4096 (d is a
+// multiple of 512 for SMOE-Q2, so the threads past d make up whole chunks).
+__global__ __launch_bounds__(256) void prefill_stage_x_q2_kernel(PrefillArgs a) {
+  const int t = blockIdx.y, piece = blockIdx.x * 256 + threadIdx.x;
+  const bool in = 16 * piece < a.d;
+  const uint16_t* src = a.x + (size_t)t * a.d + (in ? 16 * piece : 0);
+  const uint4 v0 = gload16(src), v1 = gload16(src + 8);
+  const uint32_t w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float f[16];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    f[2 * p] = (float)(_Float16)bf16_to_f32(w8[p] & 0xFFFF);
+    f[2 * p + 1] = (float)(_Float16)bf16_to_f32(w8[p] >> 16);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) part += f[p];
+  uint4 o0, o1;
+  o0.x = f16_bits(f[0]) | (f16_bits(f[8]) << 16);
+  o0.y = f16_bits(f[1] * 0.25f) | (f16_bits(f[9] * 0.25f) << 16);
+  o0.z = f16_bits(f[2]) | (f16_bits(f[10]) << 16);
+  o0.w = f16_bits(f[3] * 0.25f) | (f16_bits(f[11] * 0.25f) << 16);
+  o1.x = f16_bits(f[4]) | (f16_bits(f[12]) << 16);
+  o1.y = f16_bits(f[5] * 0.25f) | (f16_bits(f[13] * 0.25f) << 16);
+  o1.z = f16_bits(f[6]) | (f16_bits(f[14]) << 16);
+  o1.w = f16_bits(f[7] * 0.25f) | (f16_bits(f[15] * 0.25f) << 16);
+  if (in) {
+    _Float16* dst = a.xa + (size_t)t * a.d + 16 * piece;
+    *reinterpret_cast<uint4*>(dst) = o0;
+    *reinterpret_cast<uint4*>(dst + 8) = o1;
+  }
+  part = group_sum<4>(part);  // a chunk is 4 groups of 16: 4 adjacent lanes
+  if (in && (piece & 3) == 0) a.xas[(size_t)t * (a.d / 64) + piece / 4] = part;
+}
+
+// The slice's token rows for one K block of 512, copied from x_a / x_as.
+struct XCopyStageQ2 {
+  uint4 v[4];
+  float sum[2];
+  __device__ __forceinline__ void load(const PrefillArgs& a, const int* rows, int n_rows, int kb) {
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (r < n_rows) v[i] = gload16(a.xa + (size_t)rows[r] * a.d + kb + 16 * (16 * (i >> 1) + k) + 8 * (i & 1));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sum[j] = 0.f;
+      if (r < n_rows && (k & 3) == 0) sum[j] = a.xas[(size_t)rows[r] * (a.d / 64) + kb / 64 + 4 * j + (k >> 2)];
+    }
+  }
+  __device__ __forceinline__ void store(_Float16 (*xs)[512 + 8], float (*xsum)[16]) const {
+    const int tid = threadIdx.x, r = tid >> 4, k = tid & 15;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k)]) = v[2 * j];
+      *reinterpret_cast<uint4*>(&xs[r][16 * (16 * j + k) + 8]) = v[2 * j + 1];
+      if ((k & 3) == 0) xsum[4 * j + (k >> 2)][r] = sum[j];
+    }
+  }
+};
+
 struct FoldWQ2 {
   uint4 c[2];
   uint4 p[2];
@@ -1096,7 +1177,7 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_fold_q2_kernel(Prefill
   const uint8_t* up = blob + a.lay.up_params + (size_t)n0 * prow;
   float4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
   const int nk = a.d / KT;
-  FoldStageQ2<true> xr;
+  XCopyStageQ2 xr;  // the token rows, staged once per call by prefill_stage_x_q2_kernel
   FoldWQ2 g0, u0, g1, u1;
   const size_t nw0 = (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;  // the wave's first row
   const uint8_t* gc0 = blob + nw0;  // gate codes start the blob
@@ -1107,12 +1188,12 @@ __global__ __launch_bounds__(256, 2) void prefill_gate_up_fold_q2_kernel(Prefill
   load_lines_q2(u0, uc0, row_bytes, up, 0, lane);
   if (tid < n_rows) rows[tid] = a.perm[o + tid] / a.k;  // token of each entry
   __syncthreads();
-  xr.load(a.x, (size_t)a.d, rows, n_rows, 0);
+  xr.load(a, rows, n_rows, 0);
   xr.store(xs[0], xsum[0]);
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
-      xr.load(a.x, (size_t)a.d, rows, n_rows, (i + 1) * KT);
+      xr.load(a, rows, n_rows, (i + 1) * KT);
       load_lines_q2(g1, gc0, row_bytes, gp, (i + 1) * KT, lane);
       load_lines_q2(u1, uc0, row_bytes, up, (i + 1) * KT, lane);
     }
@@ -1148,7 +1229,7 @@ __global__ __launch_bounds__(256) void prefill_down_fold_q2_kernel(PrefillArgs a
   uint8_t* dst = wst[wave];
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   const int nk = a.f / KT;
-  FoldStageQ2<false> hr;
+  FoldStageQ2 hr;
   FoldWQ2 w0, w1;
   const int tiles = a.f / 64;
   load_lines_q2(w0, dc0, row_bytes, dp, 0, lane);
@@ -1217,11 +1298,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, const hipEvent_t*
   constexpr int GKT = SMOE_PF_GU_KT, DKT = SMOE_PF_DN_KT;
   if (a.bits == 2) {  // SMOE-Q2 (chunk 64, d_model a multiple of 512): folded per chunk in K
     // blocks of 512; a d_ff that is not a multiple of 512 takes the fp16-dequant down GEMM
+    hipLaunchKernelGGL(prefill_stage_x_q2_kernel, dim3((a.d + 4095) / 4096, a.T), dim3(256), 0, s, a);
     SMOE_PF_LAUNCH(prefill_gate_up_fold_q2_kernel, gu, dim3(256), s, g0, g1, a);
     if (a.f % 512 == 0) SMOE_PF_LAUNCH(prefill_down_fold_q2_kernel, dn, dim3(256), s, d0, d1, a);
     else if (a.f % 256 == 0) SMOE_PF_LAUNCH((prefill_down_kernel<64, 256, 2>), dn, dim3(256), s, d0, d1, a);
     else SMOE_PF_LAUNCH((prefill_down_kernel<64, 128, 2>), dn, dim3(256), s, d0, d1, a);
   } else if (a.chunk == 64 && a.d % 256 == 0 && a.f % 256 == 0) {  // affine folded per chunk
+    hipLaunchKernelGGL(prefill_stage_x_kernel, dim3((a.d + 2047) / 2048, a.T), dim3(256), 0, s, a);
     SMOE_PF_LAUNCH((prefill_gate_up_fold_kernel<256>), gu, dim3(256), s, g0, g1, a);
     // K blocks of 256 for the down GEMM too (512 measured slower)
     SMOE_PF_LAUNCH((prefill_down_fold_kernel<256>), dn, dim3(256), s, d0, d1, a);
