@@ -897,13 +897,21 @@ __global__ __launch_bounds__(256, 3) void prefill_gate_up_fold_kernel(PrefillArg
   store_h_tile(a, ag, au, si.o, si.n_rows, pair_index<4>(n0), red);
 }
 
+// Y = H x D^T for one slice, folded per chunk like the gate/up GEMM.  A
+// workgroup computes two 64-column tiles of the slice's 16 rows (each wave 16
+// columns of each), so the H rows it stages in LDS per K block serve 128
+// output columns: half the H gathers, conversions, barriers and workgroup
+// prologues of one tile per workgroup.  Grid (d_model / 128, max slices);
+// occupancy 3 is held by a launch bound (one tile: 102 registers, occupancy
+// 4, and slower).
 template <int KT>
-__global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void prefill_down_fold_kernel(PrefillArgs a) {
+  constexpr int NT = 2;  // 64-column tiles per workgroup
   __shared__ _Float16 xs[2][16][KT + 8];
   __shared__ __attribute__((aligned(16))) float xsum[2][KT / 64][16];
   __shared__ __attribute__((aligned(16))) float fblk[2][16];  // the blocks' common H scales
   __shared__ int rows[16];
-  __shared__ __attribute__((aligned(16))) uint8_t wst[4][KT == 256 ? 16 * kLineStageRow : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t wst[4][NT][16 * kLineStageRow];
   const int n_slices = *a.n_slices;
   const PrefillArgs::SliceRec rec = a.recs[blockIdx.y];
   if ((int)blockIdx.y >= n_slices || !rec.blob) return;
@@ -911,27 +919,27 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   si.o = rec.o;
   si.n_rows = rec.n_rows;
   const uint8_t* blob = reinterpret_cast<const uint8_t*>(rec.blob);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
-  const int n0 = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row_bytes = (size_t)a.f / 2, prow = (size_t)(a.f / 64) * 4;
-  const uint8_t* dc = blob + a.lay.down_codes + (size_t)n0 * row_bytes;
-  const uint8_t* dp = blob + a.lay.down_params + (size_t)n0 * prow;
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int n0[NT];
+  const uint8_t* dp[NT];
+  const uint8_t* dc0[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int c0 = blockIdx.x * 64 * NT + t * 64 + wave * 16;
+    n0[t] = c0 + (lane & 15);
+    dp[t] = blob + a.lay.down_params + (size_t)n0[t] * prow;
+    dc0[t] = blob + a.lay.down_codes + (size_t)c0 * row_bytes;
+  }
+  float4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
   const int nk = a.f / KT;
   FoldStage<KT> hr;
-  FoldW<KT> w0, w1;
-  // KT == 256: line-wise weight loads re-laid through the wave's LDS stage
-  const uint8_t* dc0 = blob + a.lay.down_codes + (size_t)(blockIdx.x * 64 + wave * 16) * row_bytes;
-  uint8_t* dst = wst[wave];
-  auto wload = [&](FoldW<KT>& w, int kb) {
-    if constexpr (KT == 256) load_lines256(w, dc0, row_bytes, dp, kb, lane);
-    else w.load(dc, dp, kb, g);
-  };
-  auto wlay = [&](FoldW<KT>& w) {
-    if constexpr (KT == 256) relayout256(w, dst, lane);
-  };
+  FoldW<KT> w0[NT], w1[NT];
   const int tiles = a.f / 64;
-  wload(w0, 0);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) load_lines256(w0[t], dc0[t], row_bytes, dp[t], 0, lane);
   if (tid < si.n_rows) rows[tid] = si.o + tid;  // H rows of this slice
   __syncthreads();
   hr.load(a.H, (size_t)a.f, rows, si.n_rows, 0, a.Hs, tiles);
@@ -940,19 +948,25 @@ __global__ __launch_bounds__(256) void prefill_down_fold_kernel(PrefillArgs a) {
   for (int i = 0; i < nk; ++i) {
     if (i + 1 < nk) {
       hr.load(a.H, (size_t)a.f, rows, si.n_rows, (i + 1) * KT, a.Hs, tiles);
-      wload(w1, (i + 1) * KT);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) load_lines256(w1[t], dc0[t], row_bytes, dp[t], (i + 1) * KT, lane);
     }
-    wlay(w0);  // block i, loaded one iteration ago
-    fold_kblock<KT, true>(acc, w0, xs[i & 1], xsum[i & 1], lane, fblk[i & 1]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) relayout256(w0[t], wst[wave][t], lane);  // block i, loaded one iteration ago
+#pragma unroll
+    for (int t = 0; t < NT; ++t) fold_kblock<KT, true>(acc[t], w0[t], xs[i & 1], xsum[i & 1], lane, fblk[i & 1]);
     if (i + 1 < nk) hr.store(xs[(i + 1) & 1], xsum[(i + 1) & 1], fblk[(i + 1) & 1]);
-    w0 = w1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w0[t] = w1[t];
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * (lane >> 4) + i;
-    if (row < si.n_rows) a.Y[(size_t)(si.o + row) * a.d + n0] = acc[i];
-  }
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (lane >> 4) + i;
+      if (row < si.n_rows) a.Y[(size_t)(si.o + row) * a.d + n0[t]] = acc[t][i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1307,7 +1321,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s, const hipEvent_t*
     hipLaunchKernelGGL(prefill_stage_x_kernel, dim3((a.d + 2047) / 2048, a.T), dim3(256), 0, s, a);
     SMOE_PF_LAUNCH((prefill_gate_up_fold_kernel<256>), gu, dim3(256), s, g0, g1, a);
     // K blocks of 256 for the down GEMM too (512 measured slower)
-    SMOE_PF_LAUNCH((prefill_down_fold_kernel<256>), dn, dim3(256), s, d0, d1, a);
+    SMOE_PF_LAUNCH((prefill_down_fold_kernel<256>), dim3(a.d / 128, ms), dim3(256), s, d0, d1, a);
   } else if (a.chunk == 64) {
     if (a.d % GKT == 0) SMOE_PF_LAUNCH((prefill_gate_up_kernel<64, GKT>), gu, dim3(256), s, g0, g1, a);
     else SMOE_PF_LAUNCH((prefill_gate_up_kernel<64, 128>), gu, dim3(256), s, g0, g1, a);
