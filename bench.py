@@ -597,6 +597,7 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     log(f"stack ready: vault {stack.vault.numel() / 1e9:.2f} GB")
     p = measure_prefill(stack, wl, NL, stack.bias, args.steps, args.warmup, lanes=args.chunks_in_flight,
+                        graph=not args.prefill_eager,
                         cpu_budget=None if args.no_cpu_baseline else args.cpu_budget)
     out = {
         "metric": "layer-major prefill prompt tokens/s + GB/s on union expert bytes (235B-shape, 512-token "
@@ -991,6 +992,9 @@ def main():
                     help="prefill: chunks kept in flight on as many streams (a causal pipeline, one layer apart)")
     ap.add_argument("--prefill-cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the prefill sub-object's CPU baseline")
+    ap.add_argument("--prefill-eager", action="store_true",
+                    help="prefill workload: time the readings as eager launches, not graph replays (for counter "
+                         "runs, under which replaying the prompt's graphs is slow)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the routed-expert layer is built and measured on a single "
