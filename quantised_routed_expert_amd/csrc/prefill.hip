@@ -13,12 +13,15 @@
 //               epilogue -> H [T*k][d_ff] fp16.  Chunk 64 (d_model, d_ff
 //               multiples of 256): the raw codes enter MFMA and the affine
 //               step is folded per chunk (the *_fold kernels; for SMOE-Q2
-//               blobs the *_fold_q2 kernels); otherwise the codes are
-//               dequantised to fp16 in registers (exact when min = -8 * scale,
-//               or -2 * scale for SMOE-Q2, whose down GEMM takes this form
-//               when d_ff is not a multiple of 512).
+//               blobs the *_fold_q2 kernels), after a small kernel has put
+//               the chunk's x rows in the fold's A layout once per call
+//               (prefill_stage_x*); otherwise the codes are dequantised to
+//               fp16 in registers (exact when min = -8 * scale, or -2 * scale
+//               for SMOE-Q2, whose down GEMM takes this form when d_ff is not
+//               a multiple of 512).
 //   3. down:    grouped GEMM H x D^T per union expert -> Y [T*k][d_model] fp32,
-//               in the same two forms.
+//               in the same two forms (the SMOE-Q4 fold with two 64-column
+//               tiles per workgroup).
 //   4. combine: residual[t] += sum_r w[t][r] * Y[position of (t, r)], in rank
 //               order (no atomics).
 // The pages' own prefill FFN kernels keep a thread-per-row layout (Optimizations,
