@@ -795,9 +795,12 @@ __device__ __forceinline__ void relayout256(W& w, uint8_t* stage, int lane) {
 }
 
 // acc += sum over the block's chunks of s_c P_c + m_c X_c for this lane's
-// column (feature) and its four rows 4 (lane / 16) + i; chunks in order.  All
-// of the block's MFMA chains are issued before the first result is folded, so
-// the VALU epilogue of one chunk overlaps the MFMAs of the next.
+// column (feature) and its four rows 4 (lane / 16) + i.  All of the block's
+// MFMA chains are issued before the first result is folded, so the VALU
+// epilogue of one chunk overlaps the MFMAs of the next.  The m_c X_c terms of
+// four chunks are one fp32 MFMA (v_mfma_f32_16x16x4f32: X[rows][chunks] times
+// m[chunks][columns], accumulated onto the sum), which leaves the VALU one
+// FMA per element and chunk, s_c P_c.
 // With SCALED, the A rows are H rows on one power-of-two scale per row for
 // the block, and the block's sum is multiplied by that scale fblk[row].
 template <int KT, bool SCALED = false>
@@ -822,17 +825,23 @@ __device__ __forceinline__ void fold_kblock(float4_t& acc, const FoldW<KT>& w, _
   }
   float4_t blk = zero;
   float4_t& sum = SCALED ? blk : acc;  // the block's sum, scaled once at the end
+  // the min terms of four chunks at a time as one fp32 MFMA: lane (g, ml)
+  // gives X[chunk g][row ml] and m[chunk g][its column]
+#pragma unroll
+  for (int c4 = 0; c4 < NC / 4; ++c4) {
+    const uint4 pw = w.p[c4];
+    const uint32_t pm = g == 0 ? pw.x : g == 1 ? pw.y : g == 2 ? pw.z : pw.w;
+    sum = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[4 * c4 + g][ml], __uint_as_float(pm & 0xFFFF0000u), sum, 0, 0, 0);
+  }
 #pragma unroll
   for (int cl = 0; cl < NC; ++cl) {
     const uint4 pw = w.p[cl >> 2];
     const uint32_t prm = (cl & 3) == 0 ? pw.x : (cl & 3) == 1 ? pw.y : (cl & 3) == 2 ? pw.z : pw.w;
     const float S = __uint_as_float(prm << 16) * 16777216.0f;  // scale * 2^24
-    const float M = __uint_as_float(prm & 0xFFFF0000u);
-    const float4 X = *reinterpret_cast<const float4*>(&xsum[cl][r4]);
-    sum[0] = fmaf(S, P[cl][0], fmaf(M, X.x, sum[0]));
-    sum[1] = fmaf(S, P[cl][1], fmaf(M, X.y, sum[1]));
-    sum[2] = fmaf(S, P[cl][2], fmaf(M, X.z, sum[2]));
-    sum[3] = fmaf(S, P[cl][3], fmaf(M, X.w, sum[3]));
+    sum[0] = fmaf(S, P[cl][0], sum[0]);
+    sum[1] = fmaf(S, P[cl][1], sum[1]);
+    sum[2] = fmaf(S, P[cl][2], sum[2]);
+    sum[3] = fmaf(S, P[cl][3], sum[3]);
   }
   if constexpr (SCALED) {
     const float4 F = *reinterpret_cast<const float4*>(&fblk[r4]);
