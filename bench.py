@@ -20,7 +20,7 @@ prompt in chunks of 64 through the same 94 layers, layer-major, Zipf-biased
 routing; ``--workload ring`` -- decode with the experts in a 1536-slot HBM ring
 refilled from a vault in pinned host memory (Markov hidden states).
 
-Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: the layer is built and measured on
 one GPU.
 """
 import argparse
